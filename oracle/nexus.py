@@ -1,0 +1,231 @@
+"""The Nexus Sampling eviction step, written out in fp64 numpy (test infrastructure).
+
+Every function follows [Nexus] = "Forget Without Compromise: Nexus Sampling for
+Streaming KV-Cache Eviction Under Fixed Budgets" (academ.us article page) and
+says which passage.  No blocking, fusion or reordering beyond the definitions:
+one BLAS matmul for the logits, then elementwise numpy.
+
+Readings of passages the pages leave open (each also listed in the design doc):
+  granularity  tokens, i.e. block size b = 1, so BlockSum_b and rownorm of
+               section 2.1 Eq. (1) are identities on softmax rows.
+  GQA          "head-averaged representations" (section 2.1): for KV head h the
+               softmax rows of its G query heads h*G .. h*G+G-1 are averaged,
+               per window row, in probability space.
+  walk rows    Eq. (4) feeds one fresh window row per step: the H most recent
+               rows W-H .. W-1, oldest first; H = 0 gives c~ = 0.
+  ramp         Eq. (5) r_j = j/(N-1) with 0-based j (0 oldest, 1 newest);
+               r = 0 when N = 1.
+  n            Eq. (6) with n = 1; its ordering equals the A-Res key ln(u)/w.
+  ties         equal keys: the larger (newer) index wins.
+  w <= 0       key -inf (kept only when needed to fill B); non-finite w is an
+               error.
+  forced       the first n_sink and last n_recent positions get key +inf
+               (section 2.3, forced slots).
+  order        kept indices are returned ascending (cache order).
+
+Pins (tests/test_oracle_nexus.py): the hand-computed tiny cache in
+tests/golden/, closed forms (Q = 0 gives a = 1/N; identical rows; H = 1),
+the walk's rank-1 decomposition (appendix 8.6), softmax against scipy,
+permutation equivariance, and selection laws against exact enumeration
+(oracle/enumerate.py) and the uniform-reservoir special case.
+"""
+
+import numpy as np
+
+from . import philox
+
+LAMBDA_DEFAULT = 0.5     # [Nexus] section 5.1: mixing weight
+EPS_TIE_DEFAULT = 1e-6   # [Nexus] section 5.1: tie-break magnitude
+
+
+# ----------------------------------------------------------------- inputs ----
+
+def bf16_bits_to_f64(bits):
+    """Exact fp64 value of raw bfloat16 bit patterns (uint16 array)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def as_f64(x, dtype):
+    """Inputs as exact fp64: dtype 'bf16' means raw uint16 bit patterns."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ------------------------------------------------------------ Nexus score ----
+
+def window_rows(q_grp, k):
+    """Per-row distributions a^(q) of the window, averaged over the GQA group.
+
+    [Nexus] section 2.1, Eq. (1): softmax(Q K^T / sqrt(D)) over the cached keys,
+    one row per window query; at b = 1 BlockSum and rownorm change nothing.
+    q_grp: [G, W, D] fp64 (the G query heads sharing one KV head); k: [N, D].
+    Returns P: [W, N], P[w] = (1/G) * sum_i softmax_j(q_{i,w} . k_j / sqrt(D)).
+    """
+    q_grp = np.asarray(q_grp, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = k.shape[-1]
+    logits = np.matmul(q_grp, k.T) / np.sqrt(d)               # [G, W, N]
+    shifted = logits - logits.max(axis=-1, keepdims=True)
+    e = np.exp(shifted)
+    p = e / e.sum(axis=-1, keepdims=True)
+    return p.mean(axis=0)
+
+
+def direct_score(P):
+    """[Nexus] section 2.2, Eq. (3): a = (1/W) sum_q a^(q), the uniform row average."""
+    return np.asarray(P, dtype=np.float64).mean(axis=0)
+
+
+def nexus_walk(P, walk_iters):
+    """[Nexus] section 2.2, Eq. (4): the alignment-weighted walk, normalised.
+
+    C starts at 0; each step takes the next window row a^(q) (rows W-H .. W-1,
+    oldest first), sets gamma = 1 + <a^(q), C> using C before the update, then
+    C <- C + gamma * a^(q).  Returns c~ = C / ||C||_1 (zeros when H = 0).
+    """
+    P = np.asarray(P, dtype=np.float64)
+    W, N = P.shape
+    if not 0 <= walk_iters <= W:
+        raise ValueError("walk_iters must lie in [0, W]")
+    C = np.zeros(N)
+    for t in range(W - walk_iters, W):
+        row = P[t]
+        gamma = 1.0 + float(np.dot(row, C))
+        C = C + gamma * row
+    if walk_iters == 0:
+        return np.zeros(N)
+    return C / np.abs(C).sum()
+
+
+def nexus_score(a, c, lam=LAMBDA_DEFAULT):
+    """[Nexus] section 2.2, Eq. (2): s = a + lambda * c~."""
+    return np.asarray(a, dtype=np.float64) + lam * np.asarray(c, dtype=np.float64)
+
+
+def recency_weights(s, eps=EPS_TIE_DEFAULT):
+    """[Nexus] section 2.2, Eq. (5): w_j = s_j + eps * r_j with r_j = j/(N-1)."""
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[-1]
+    r = np.arange(n, dtype=np.float64) / (n - 1) if n > 1 else np.zeros(n)
+    return s + eps * r
+
+
+def head_weights(q_grp, k, walk_iters, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT):
+    """All scoring stages for one KV head; returns a dict of the intermediates."""
+    P = window_rows(q_grp, k)
+    a = direct_score(P)
+    c = nexus_walk(P, walk_iters)
+    s = nexus_score(a, c, lam)
+    w = recency_weights(s, eps)
+    return {"P": P, "a": a, "c": c, "s": s, "w": w}
+
+
+# ------------------------------------------------------- reservoir select ----
+
+def reservoir_keys(w, u, n_sink=0, n_recent=0):
+    """A-Res keys for one KV head; [Nexus] section 2.3, Eq. (6) with n = 1.
+
+    Ranking by u^(1/w) equals ranking by ln(u)/w (ln is increasing), computed
+    here in fp64.  w <= 0 gives -inf.  The forced sink / recency positions
+    (section 2.3) get +inf so that they always survive.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite Nexus weight")
+    n = w.shape[-1]
+    pos = w > 0
+    keys = np.full(n, -np.inf)
+    keys[pos] = np.log(u[pos]) / w[pos]
+    if n_sink:
+        keys[:n_sink] = np.inf
+    if n_recent:
+        keys[n - n_recent:] = np.inf
+    return keys
+
+
+def select_top(keys, budget):
+    """Keep the `budget` largest keys; [Nexus] section 2.3 (keep the top K).
+
+    Equal keys: the larger index wins.  budget >= N keeps everything.
+    Returns the kept indices in ascending (cache) order.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    n = keys.shape[-1]
+    if budget >= n:
+        return np.arange(n, dtype=np.int64)
+    order = np.lexsort((np.arange(n), keys))   # ascending by key, then index
+    return np.sort(order[n - budget:])
+
+
+def unit_uniforms(n_tokens, unit_id, layer, step, seed):
+    """The token uniforms of one KV head for one eviction event."""
+    j = np.arange(n_tokens, dtype=np.uint64)
+    return philox.uniforms(j, unit_id, layer, step, seed)
+
+
+# ------------------------------------------------------------ whole step ----
+
+def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
+               step=0, seq_id=0, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT,
+               n_sink=0, n_recent=0, heads=None):
+    """One eviction event for one (sequence, layer): every KV head.
+
+    [Nexus] section 2.1 (streaming view): keep `budget` of the N resident
+    positions per KV head and continue with the kept K and V rows.
+    q: [H_q, W, D]; k, v: [H_kv, N, D] (raw bf16 bits when dtype == 'bf16').
+    Query head g reads KV head g // G.  `heads` restricts the work to a
+    subset of KV heads (results for the others are left out).
+    Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    h_q, W, d = q.shape
+    h_kv, n, _ = k.shape
+    if h_q % h_kv:
+        raise ValueError("H_q must be a multiple of H_kv")
+    if budget < 1 or n < 1:
+        raise ValueError("budget and n_tokens must be >= 1")
+    if n_sink + n_recent > budget:
+        raise ValueError("forced slots exceed the budget")
+    g = h_q // h_kv
+    heads = range(h_kv) if heads is None else heads
+    out = {"w": {}, "keys": {}, "keep": {}, "out_k": {}, "out_v": {}}
+    for h in heads:
+        q_grp = as_f64(q[h * g:(h + 1) * g], dtype)
+        kh = as_f64(k[h], dtype)
+        sc = head_weights(q_grp, kh, walk_iters, lam, eps)
+        u = unit_uniforms(n, seq_id * h_kv + h, layer, step, seed)
+        keys = reservoir_keys(sc["w"], u, n_sink, n_recent)
+        keep = select_top(keys, budget)
+        out["w"][h] = sc["w"]
+        out["keys"][h] = keys
+        out["keep"][h] = keep
+        out["out_k"][h] = k[h][keep]
+        out["out_v"][h] = v[h][keep]
+    return out
+
+
+def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
+                        n_sink=0, n_recent=0):
+    """Reservoir selection on given weights w: [H_kv, N] (any precision).
+
+    The oracle run on someone else's scores: same Philox stream, fp64 keys,
+    full sort.  Returns (keys [H_kv, N], list of ascending keep arrays).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    h_kv, n = w.shape
+    keys = np.empty((h_kv, n))
+    keeps = []
+    for h in range(h_kv):
+        u = unit_uniforms(n, seq_id * h_kv + h, layer, step, seed)
+        keys[h] = reservoir_keys(w[h], u, n_sink, n_recent)
+        keeps.append(select_top(keys[h], budget))
+    return keys, keeps
