@@ -1,0 +1,175 @@
+"""Benchmark of the Nexus Sampling eviction step on one MI355X.
+
+One step = one eviction event over every layer of the headline workload: a
+Llama-3-8B-shaped model (32 layers, 32 query heads sharing 8 KV heads, head_dim
+128, bf16) whose cache holds N = 32768 tokens per KV head, evicted to B = 6554
+with a window of W = 32 queries and walk depth H = 3.  All five stages run in
+one nx_evict_batch call: scoring (two MFMA sweeps), walk and keys, radix
+select, compaction.  Inputs are synthetic and resident in HBM before timing.
+
+Prints one JSON line: KV tokens scored and sampled per second (256 head units
+x 32768 tokens per step), step latency, the dominant kernel's roofline
+fraction measured with HIP events inside the timed loop, and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import streaming_weighted_sampling_amd as nx  # noqa: E402
+from workloads import WORKLOADS, fill_layer_, bf16_bits  # noqa: E402
+
+METRIC = "KV tokens scored+sampled/sec and eviction-step latency at N=32K, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def build_batch(wl, device):
+    L, H, N, D, B = wl.n_layers, wl.h_kv, wl.n_tokens, wl.head_dim, wl.budget
+    q = torch.empty(L, wl.h_q, wl.window, D, dtype=torch.bfloat16, device=device)
+    k = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
+    v = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
+    q32 = torch.empty(wl.h_q, wl.window, D, device=device)
+    k32 = torch.empty(H, N, D, device=device)
+    v32 = torch.empty(H, N, D, device=device)
+    for layer in range(L):
+        fill_layer_(wl, q32, k32, v32, layer=layer)
+        q[layer].copy_(q32)
+        k[layer].copy_(k32)
+        v[layer].copy_(v32)
+    del q32, k32, v32
+    keep = torch.empty(L, H, B, dtype=torch.int32, device=device)
+    out_k = torch.empty(L, H, B, D, dtype=torch.bfloat16, device=device)
+    out_v = torch.empty_like(out_k)
+    items = [dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=out_k[l], out_v=out_v[l],
+                  kv_head_stride=N * D, out_head_stride=B * D, n_tokens=N, budget=B, layer=l)
+             for l in range(L)]
+    units = nx.make_units(items, device=device)
+    return dict(q=q, k=k, v=v, keep=keep, out_k=out_k, out_v=out_v, units=units)
+
+
+def cpu_baseline(wl, data, budget_s):
+    """The fp64 oracle on whole KV heads of layer 0, until ~budget_s seconds pass."""
+    from oracle import nexus
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    q = bf16_bits(data["q"][0])
+    heads_done, t0 = 0, time.perf_counter()
+    while heads_done < wl.h_kv:
+        h = heads_done
+        k = bf16_bits(data["k"][0, h:h + 1])
+        v = bf16_bits(data["v"][0, h:h + 1])
+        qg = q[h * wl.group:(h + 1) * wl.group]
+        nexus.evict_step(qg, k, v, wl.budget, wl.walk_iters, 0, dtype="bf16", layer=0)
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": heads_done * wl.n_tokens / dt, "unit": "KV tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads_done} KV head(s) of layer 0 ({heads_done * wl.n_tokens} tokens, "
+                      f"full step per head, {dt:.1f} s, BLAS threads {threads}, "
+                      f"{os.cpu_count()} host CPUs visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the eviction path has no multi-GPU mode "
+              "(head units are independent; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl = WORKLOADS["llama3_8b_stream32"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    data = build_batch(wl, dev)
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16)
+    ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        nx.nx_evict_batch(cfg, data["units"], wl.n_layers, wl.n_tokens, wl.walk_iters, 0,
+                          workspace=ws, step=i, max_out_rows=wl.budget)
+
+    for i in range(args.warmup):
+        step(i)
+    nx.nx_read_device_status(cfg, ws)
+    torch.cuda.synchronize()
+
+    nx.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nx.profile_enable(False)
+    stages = nx.profile_read()
+    nx.nx_read_device_status(cfg, ws)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    units = wl.n_layers * wl.h_kv
+    tokens = units * wl.n_tokens
+    value = tokens / (ms_per_step * 1e-3)
+
+    # Algorithmic work per launch (one launch per stage per step covers every layer).
+    d, e = wl.head_dim, 2
+    k_bytes = tokens * d * e                                  # one read of the resident K
+    compact_bytes = units * wl.budget * (4 * d * e + 4)       # K,V read+write of kept rows + index
+    qk_flops = tokens * 2 * wl.group * wl.window * d          # one QK^T sweep
+    per_launch = {name: (ms / max(cnt, 1), cnt) for name, (ms, cnt) in stages.items() if cnt}
+    dominant = max(per_launch, key=lambda s: per_launch[s][0])
+    dom_ms = per_launch[dominant][0]
+    if dominant == "score_stats":
+        achieved, peak, unit, bound = k_bytes / (dom_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    elif dominant == "kv_compact":
+        achieved, peak, unit, bound = compact_bytes / (dom_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:   # score_probs: the second sweep recomputes the logits on MFMA
+        achieved, peak, unit, bound = qk_flops / (dom_ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_stream32 eviction event at N=32768 (32 layers x 8 KV "
+                               "heads, GQA 32:8, head_dim 128, W=32, H=3, B=6554)",
+                   "layers": wl.n_layers, "kv_heads": wl.h_kv, "n_tokens": wl.n_tokens,
+                   "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters},
+        "step_latency_ms": round(ms_per_step, 4),
+        "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},
+        "stage_gbs": {
+            "score_stats_k_read": round(k_bytes / (per_launch["score_stats"][0] * 1e-3) / 1e9, 1),
+            "kv_compact": round(compact_bytes / (per_launch["kv_compact"][0] * 1e-3) / 1e9, 1),
+            "step_algorithmic": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
+        },
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

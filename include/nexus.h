@@ -1,0 +1,210 @@
+/*
+ * nexus.h -- C ABI of the Nexus Sampling eviction step for AMD Instinct MI355X (gfx950).
+ *
+ * The method ([Nexus]): "Forget Without Compromise: Nexus Sampling for Streaming
+ * KV-Cache Eviction Under Fixed Budgets" (academ.us article page).  One eviction
+ * event keeps B of the N resident positions of every KV head and continues with
+ * the kept K and V rows (section 2.1, streaming view).  The kept set is drawn by
+ * weighted reservoir sampling (section 2.3, Eq. 6) on the Nexus weight
+ * w = a + lambda * c~ + eps * r (section 2.2, Eqs. 2-5), where a is the direct
+ * attention of a window of W recent queries (section 2.1, Eq. 1; section 2.2,
+ * Eq. 3) and c~ the normalised alignment-weighted walk over the same rows
+ * (section 2.2, Eq. 4).
+ *
+ * Granularity is one token (block size b = 1), the reservoir uses one uniform
+ * per token (n = 1) and the A-Res key ln(u)/w in fp64.  The uniform comes from
+ * Philox4x32-10 (Salmon et al., SC'11) with counter
+ * (token, seq_id * n_kv_heads + kv_head, layer, step) and key (seed lo, seed hi):
+ * u = ((((x0 << 32) | x1) >> 11) + 1) * 2^-53 in (0, 1].
+ * Equal keys: the larger (newer) token index wins.  Kept indices are ascending.
+ *
+ * Conventions for every entry point:
+ *  - Buffers are device memory owned by the caller (for example torch tensors).
+ *    The library allocates nothing and keeps no per-call state outside the
+ *    caller's workspace.
+ *  - Work is enqueued on desc->stream (a hipStream_t; NULL = legacy default
+ *    stream) and the call returns at once.  Calls that share a workspace must
+ *    be ordered on one stream.
+ *  - Host-side argument errors return a negative nx_status before anything is
+ *    enqueued.  Errors only the device can see (a non-finite weight, an invalid
+ *    batch item) are recorded in a status word inside the workspace and
+ *    reported by nx_read_device_status().
+ *  - Layouts are row-major.  Q window: [n_q_heads, window, head_dim], row 0 the
+ *    oldest query; query head g reads KV head g / (n_q_heads / n_kv_heads).
+ *    K and V caches: [n_kv_heads][kv_head_stride elements], each head holding
+ *    [n_tokens, head_dim] rows.  Outputs: keep indices [n_kv_heads, budget]
+ *    (int32), out_k / out_v [n_kv_heads][out_head_stride elements] holding
+ *    [kept, head_dim] rows, kept = min(budget, n_tokens).
+ *  - Element types: NX_BF16 (bfloat16) or NX_F32, shared by Q, K, V and the
+ *    outputs; head_dim 64 or 128.
+ */
+#ifndef NEXUS_H
+#define NEXUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nx_status;
+enum {
+  NX_OK = 0,
+  NX_EINVAL = -1,        /* bad argument (null pointer, size, budget, walk depth) */
+  NX_EALIAS = -2,        /* an output overlaps an input */
+  NX_EWORKSPACE = -3,    /* workspace missing or smaller than nx_evict_workspace_bytes() */
+  NX_EUNSUPPORTED = -4,  /* dtype / head_dim / group size outside the built kernels */
+  NX_ENONFINITE = -5,    /* device: a Nexus weight was NaN or infinite */
+  NX_EHIP = -6           /* a HIP runtime call failed */
+};
+
+enum { NX_BF16 = 0, NX_F32 = 1 };
+
+/* Problem shape and parameters shared by the calls of one eviction event. */
+typedef struct nx_desc {
+  int32_t n_q_heads;        /* H_q, a multiple of n_kv_heads */
+  int32_t n_kv_heads;       /* H_kv */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t window;           /* W >= 1: recent queries scored against the cache (section 2.1) */
+  int32_t dtype;            /* NX_BF16 or NX_F32 */
+  float lambda;             /* mixing weight of Eq. 2 (0.5 in section 5.1) */
+  float eps_tie;            /* recency tie-break of Eq. 5 (1e-6 in section 5.1) */
+  int32_t n_sink;           /* leading positions always kept (section 2.3, forced slots) */
+  int32_t n_recent;         /* trailing positions always kept (section 2.3, forced slots) */
+  uint32_t layer;           /* Philox counter word 2 */
+  uint32_t step;            /* Philox counter word 3 (eviction event number) */
+  uint32_t seq_id;          /* sequence number for Philox counter word 1 (single-item calls) */
+  int32_t max_out_rows;     /* batch calls: expected max of kept + n_append over the items;
+                               sizes the compaction grid only (any value is correct, a
+                               close bound is fastest); 0 means max_tokens */
+  int64_t kv_head_stride;   /* elements between KV heads in k/v; 0 means n_tokens * head_dim */
+  int64_t out_head_stride;  /* elements between KV heads in out_k/out_v; 0 means budget * head_dim */
+  void* workspace;          /* device scratch, >= nx_evict_workspace_bytes(); zero-filled once
+                               before first use and not modified by the caller afterwards */
+  size_t workspace_bytes;
+  void* stream;             /* hipStream_t */
+} nx_desc;
+
+/*
+ * One (sequence, layer) item of a batched eviction event.  An array of these
+ * lives in DEVICE memory for nx_evict_batch.  Field meanings match
+ * nx_evict_step; app_k / app_v (nullable) are n_append new K / V rows per KV
+ * head ([n_kv_heads][n_append * head_dim], contiguous) written right after the
+ * kept rows, so that a streaming cache is compacted and extended in one pass
+ * (the append-then-evict loop of section 2.1).  out_head_stride must then
+ * hold kept + n_append rows.
+ */
+typedef struct nx_unit {
+  const void* q;
+  const void* k;
+  const void* v;
+  int32_t* keep;
+  void* out_k;
+  void* out_v;
+  const void* app_k;
+  const void* app_v;
+  int64_t kv_head_stride;   /* elements; must be >= n_tokens * head_dim */
+  int64_t out_head_stride;  /* elements; must be >= (kept + n_append) * head_dim */
+  int32_t n_tokens;
+  int32_t budget;
+  int32_t n_append;
+  uint32_t layer;
+  uint32_t seq_id;
+  uint32_t reserved;
+} nx_unit;
+
+/*
+ * Workspace bytes for calls with up to `max_units` items (1 for single-item
+ * calls) of up to `max_tokens` tokens each and walk depth `walk_iters`.
+ * Returns 0 if desc is invalid.  Pure host function.
+ */
+size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t max_units,
+                                int32_t walk_iters);
+
+/*
+ * One eviction event for one (sequence, layer): score every resident token of
+ * every KV head against the query window (section 2.1 Eq. 1, section 2.2
+ * Eqs. 2-5), draw exactly min(budget, n_tokens) tokens per KV head by the A-Res
+ * reservoir (section 2.3 Eq. 6, n = 1), and gather their K and V rows
+ * (section 2.1: inference continues with the kept rows).
+ *   q_window     [n_q_heads, window, head_dim]
+ *   k_cache      [n_kv_heads][kv_head_stride]; v_cache likewise
+ *   n_tokens     N >= 1 resident tokens per head
+ *   budget       B >= 1 kept tokens per head (B >= N keeps all)
+ *   walk_iters   H in [0, min(window, 8)]: the H most recent window rows, oldest
+ *                first, feed the walk; H = 0 gives plain direct attention
+ *   seed         64-bit Philox key
+ *   out_keep_idx [n_kv_heads, budget] int32, ascending; entries past `kept` untouched
+ *   out_k, out_v [n_kv_heads][out_head_stride], must not overlap k_cache / v_cache
+ * Errors: NX_EINVAL, NX_EALIAS, NX_EWORKSPACE, NX_EUNSUPPORTED, NX_EHIP.
+ */
+nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,
+                        const void* v_cache, int32_t n_tokens, int32_t budget,
+                        int32_t walk_iters, uint64_t seed, int32_t* out_keep_idx,
+                        void* out_k, void* out_v);
+
+/*
+ * The same event for `n_units` (sequence, layer) items in one launch per stage
+ * (all layers of a model, or ragged sequences).  units_dev points to n_units
+ * nx_unit records in device memory; desc supplies the shared shape, lambda,
+ * eps_tie, forced slots, step and workspace (its seq_id, layer and strides are
+ * ignored: each item carries its own).  max_tokens bounds every item's
+ * n_tokens.  Items are checked on the device; a bad item is skipped and
+ * reported as NX_EINVAL by nx_read_device_status().
+ */
+nx_status nx_evict_batch(const nx_desc* desc, const nx_unit* units_dev, int32_t n_units,
+                         int32_t max_tokens, int32_t walk_iters, uint64_t seed);
+
+/*
+ * Scoring stage only: the Nexus weights w (section 2.2 Eq. 5) of every resident
+ * token, out_w [n_kv_heads, n_tokens] fp32.
+ */
+nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void* k_cache,
+                           int32_t n_tokens, int32_t walk_iters, float* out_w);
+
+/*
+ * Reservoir stage only (section 2.3 Eq. 6, n = 1) on given weights
+ * w [n_kv_heads, n_tokens] fp32: Philox uniforms, fp64 keys ln(u)/w (w <= 0 gives
+ * -inf, forced slots +inf), and the top-budget selection.
+ *   out_keep_idx [n_kv_heads, budget] int32 ascending
+ *   out_keys     nullable; [n_kv_heads, n_tokens] fp64 keys
+ */
+nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tokens,
+                              int32_t budget, uint64_t seed, int32_t* out_keep_idx,
+                              double* out_keys);
+
+/*
+ * Compaction stage only (section 2.1: continue with K_S, V_S): bit copies
+ * out_k[h, r] = k[h, keep_idx[h, r]] and likewise for V, r < min(budget, n_tokens).
+ * keep_idx entries must lie in [0, n_tokens).
+ */
+nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_cache,
+                        const int32_t* keep_idx, int32_t n_tokens, int32_t budget,
+                        void* out_k, void* out_v);
+
+/*
+ * Waits for desc->stream, reads and clears the workspace status word.
+ * Returns NX_OK, NX_ENONFINITE, NX_EINVAL (a bad batch item) or NX_EHIP.
+ */
+nx_status nx_read_device_status(const nx_desc* desc);
+
+/* Human-readable name of a status code.  Pure host function. */
+const char* nx_status_str(nx_status status);
+
+/*
+ * Per-stage timing with HIP events recorded on desc->stream around every
+ * kernel launch of later calls (process-wide; not thread-safe).
+ * nx_profile_enable(1) clears and starts, nx_profile_enable(0) stops.
+ * nx_profile_read waits for the recorded events and fills, per stage index,
+ * the summed milliseconds and the launch count; returns the number of stages.
+ */
+nx_status nx_profile_enable(int32_t enable);
+int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_stages);
+const char* nx_stage_name(int32_t stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NEXUS_H */

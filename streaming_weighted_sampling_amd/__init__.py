@@ -1,0 +1,16 @@
+"""Nexus Sampling eviction step for AMD Instinct MI355X (gfx950).
+
+The work runs in libnexus.so (HIP kernels behind the C ABI of include/nexus.h);
+this package is its build script and a thin torch-facing binding.  Importing
+the binding fails loudly when the library has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    NX_OK, NX_EINVAL, NX_EALIAS, NX_EWORKSPACE, NX_EUNSUPPORTED, NX_ENONFINITE, NX_EHIP,
+    NX_BF16, NX_F32, NxDesc, NxUnit, NexusError, LIB_PATH, load, status_str,
+)
+from .api import (  # noqa: F401
+    NexusConfig, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,
+    nx_reservoir_select, nx_kv_compact, make_units, nx_evict_batch, nx_read_device_status,
+    profile_enable, profile_read,
+)

@@ -1,0 +1,358 @@
+// Host side of the C ABI declared in include/nexus.h: argument validation,
+// workspace carving and the launch sequence on the caller's stream.
+//
+// [Nexus] = "Forget Without Compromise: Nexus Sampling for Streaming KV-Cache
+// Eviction Under Fixed Budgets" (academ.us article page).
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "nx_internal.hpp"
+
+using namespace nx;
+
+namespace {
+
+constexpr int32_t kMaxTokens = 1 << 24;
+constexpr int32_t kMaxRowsPad = 512;    // 4 waves x 4 M-tiles x 32 rows
+
+int32_t elem_size(int32_t dtype) { return dtype == NX_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+nx_status check_desc(const nx_desc* d) {
+  if (d == nullptr) return NX_EINVAL;
+  if (d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads)
+    return NX_EINVAL;
+  if (d->window < 1 || d->n_sink < 0 || d->n_recent < 0) return NX_EINVAL;
+  if (!std::isfinite(d->lambda) || !std::isfinite(d->eps_tie)) return NX_EINVAL;
+  if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return NX_EUNSUPPORTED;
+  return NX_OK;
+}
+
+nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, int32_t walk,
+                        Geometry* g) {
+  nx_status st = check_desc(d);
+  if (st != NX_OK) return st;
+  if (max_tokens < 1 || max_tokens > kMaxTokens || n_items < 1) return NX_EINVAL;
+  if (walk < 0 || walk > d->window) return NX_EINVAL;
+  const int32_t group = d->n_q_heads / d->n_kv_heads;
+  const int64_t rows = int64_t(group) * d->window;
+  const int64_t rows_pad = (rows + 31) / 32 * 32;
+  if (walk > kMaxWalk || int64_t(group) * walk > kMaxWalkRows || rows_pad > kMaxRowsPad)
+    return NX_EUNSUPPORTED;
+  const int64_t n_hu = int64_t(n_items) * d->n_kv_heads;
+  if (n_hu > 65535) return NX_EUNSUPPORTED;     // grid y dimension of the token stages
+  g->h_q = d->n_q_heads;
+  g->h_kv = d->n_kv_heads;
+  g->group = group;
+  g->head_dim = d->head_dim;
+  g->window = d->window;
+  g->walk = walk;
+  g->rows = int32_t(rows);
+  g->rows_pad = int32_t(rows_pad);
+  g->walk_rows = group * walk;
+  g->dtype = d->dtype;
+  g->n_hu = int32_t(n_hu);
+  g->max_tokens = max_tokens;
+  g->max_out_rows = max_tokens;
+  g->n_t1 = (max_tokens + kTokPerBlock - 1) / kTokPerBlock;
+  g->n_t2 = g->n_t1;
+  g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
+  return NX_OK;
+}
+
+nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
+  const WsLayout L = ws_layout(g);
+  if (d->workspace == nullptr || d->workspace_bytes < L.total) return NX_EWORKSPACE;
+  char* base = static_cast<char*>(d->workspace);
+  a->status = reinterpret_cast<uint32_t*>(base + L.status);
+  a->part1 = reinterpret_cast<float*>(base + L.part1);
+  a->beta = reinterpret_cast<float*>(base + L.beta);
+  a->a = reinterpret_cast<float*>(base + L.a);
+  a->p = reinterpret_cast<float*>(base + L.p);
+  a->gram = reinterpret_cast<float*>(base + L.gram);
+  a->keys = reinterpret_cast<uint64_t*>(base + L.keys);
+  a->selp = reinterpret_cast<uint64_t*>(base + L.selp);
+  return NX_OK;
+}
+
+Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.g = g;
+  a.lambda = d->lambda;
+  a.eps_tie = d->eps_tie;
+  a.c_log2 = float(1.4426950408889634 / std::sqrt(double(d->head_dim)));
+  a.n_sink = d->n_sink;
+  a.n_recent = d->n_recent;
+  a.step = d->step;
+  a.seed = seed;
+  return a;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, int64_t heads, int64_t stride_elems, int64_t last_elems, int32_t esz) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + uintptr_t(((heads - 1) * stride_elems + last_elems) * esz)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// ---- profiling (process-wide) ----
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int stage; hipEvent_t e0, e1; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler& prof() { static Profiler p; return p; }
+
+template <typename F>
+hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
+  Profiler& p = prof();
+  if (!p.on) return launch();
+  std::lock_guard<std::mutex> lock(p.mu);
+  hipEvent_t e0 = p.get(), e1 = p.get();
+  if (e0) (void)hipEventRecord(e0, s);
+  const hipError_t err = launch();
+  if (e1) (void)hipEventRecord(e1, s);
+  if (e0 && e1) p.recs.push_back({stage, e0, e1});
+  return err;
+}
+
+// Enqueue stages [first, last] in order.
+nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
+  hipError_t err = hipSuccess;
+  for (int st = first; st <= last && err == hipSuccess; ++st) {
+    switch (st) {
+      case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
+      case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
+      case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
+      case kStageReservoirKeys: err = run_stage(st, s, [&] { return launch_reservoir_keys(a, s); }); break;
+      case kStageTopbSelect: err = run_stage(st, s, [&] { return launch_topb_select(a, s); }); break;
+      case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(a, s); }); break;
+      default: break;
+    }
+  }
+  return err == hipSuccess ? NX_OK : NX_EHIP;
+}
+
+nx_unit single_unit(const nx_desc* d, const void* q, const void* k, const void* v, int32_t* keep,
+                    void* out_k, void* out_v, int32_t n, int32_t budget) {
+  nx_unit u;
+  std::memset(&u, 0, sizeof(u));
+  u.q = q;
+  u.k = k;
+  u.v = v;
+  u.keep = keep;
+  u.out_k = out_k;
+  u.out_v = out_v;
+  u.kv_head_stride = d->kv_head_stride ? d->kv_head_stride : int64_t(n) * d->head_dim;
+  u.out_head_stride = d->out_head_stride ? d->out_head_stride : int64_t(budget) * d->head_dim;
+  u.n_tokens = n;
+  u.budget = budget;
+  u.layer = d->layer;
+  u.seq_id = d->seq_id;
+  return u;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t max_units,
+                                int32_t walk_iters) {
+  Geometry g;
+  if (make_geometry(desc, max_tokens, max_units, walk_iters, &g) != NX_OK) return 0;
+  return ws_layout(g).total;
+}
+
+nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,
+                        const void* v_cache, int32_t n_tokens, int32_t budget, int32_t walk_iters,
+                        uint64_t seed, int32_t* out_keep_idx, void* out_k, void* out_v) {
+  Geometry g;
+  nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
+  if (st != NX_OK) return st;
+  if (!q_window || !k_cache || !v_cache || !out_keep_idx || !out_k || !out_v) return NX_EINVAL;
+  if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
+  const nx_unit u = single_unit(desc, q_window, k_cache, v_cache, out_keep_idx, out_k, out_v,
+                                n_tokens, budget);
+  const int64_t d = desc->head_dim, hk = desc->n_kv_heads;
+  const int32_t kept = budget < n_tokens ? budget : n_tokens;
+  if (u.kv_head_stride < n_tokens * d || u.out_head_stride < kept * d) return NX_EINVAL;
+  const int32_t esz = elem_size(desc->dtype);
+  const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);
+  const Range rv = span(v_cache, hk, u.kv_head_stride, n_tokens * d, esz);
+  const Range rq = span(q_window, 1, 0, int64_t(desc->n_q_heads) * desc->window * d, esz);
+  const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
+  const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
+  const Range rkeep = span(out_keep_idx, 1, 0, hk * budget, 4);
+  for (Range o : {rok, rov, rkeep})
+    for (Range i : {rk, rv, rq})
+      if (overlap(o, i)) return NX_EALIAS;
+  if (overlap(rok, rov) || overlap(rok, rkeep) || overlap(rov, rkeep)) return NX_EALIAS;
+  g.max_out_rows = kept;
+  Args a = base_args(desc, g, seed);
+  if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
+  a.single = u;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageKvCompact);
+}
+
+nx_status nx_evict_batch(const nx_desc* desc, const nx_unit* units_dev, int32_t n_units,
+                         int32_t max_tokens, int32_t walk_iters, uint64_t seed) {
+  Geometry g;
+  nx_status st = make_geometry(desc, max_tokens, n_units, walk_iters, &g);
+  if (st != NX_OK) return st;
+  if (units_dev == nullptr) return NX_EINVAL;
+  if (desc->max_out_rows < 0) return NX_EINVAL;
+  g.max_out_rows = desc->max_out_rows > 0 ? desc->max_out_rows : max_tokens;
+  Args a = base_args(desc, g, seed);
+  if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
+  a.units = units_dev;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageKvCompact);
+}
+
+nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void* k_cache,
+                           int32_t n_tokens, int32_t walk_iters, float* out_w) {
+  Geometry g;
+  nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
+  if (st != NX_OK) return st;
+  if (!q_window || !k_cache || !out_w) return NX_EINVAL;
+  nx_unit u = single_unit(desc, q_window, k_cache, nullptr, nullptr, nullptr, nullptr, n_tokens,
+                          n_tokens);
+  if (u.kv_head_stride < int64_t(n_tokens) * desc->head_dim) return NX_EINVAL;
+  if (desc->n_sink + desc->n_recent > n_tokens) return NX_EINVAL;
+  Args a = base_args(desc, g, 0);
+  if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
+  a.single = u;
+  a.w_out = out_w;
+  a.stop_after_weights = 1;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageReservoirKeys);
+}
+
+nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tokens,
+                              int32_t budget, uint64_t seed, int32_t* out_keep_idx,
+                              double* out_keys) {
+  Geometry g;
+  nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
+  if (st != NX_OK) return st;
+  if (!w || !out_keep_idx) return NX_EINVAL;
+  if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
+  // The scoring inputs are not used; q and k only need to be non-null.
+  nx_unit u = single_unit(desc, w, w, nullptr, out_keep_idx, nullptr, nullptr, n_tokens, budget);
+  u.kv_head_stride = int64_t(n_tokens) * desc->head_dim;
+  Args a = base_args(desc, g, seed);
+  if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
+  a.single = u;
+  a.w_in = w;
+  a.keys_out = out_keys;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageReservoirKeys, kStageTopbSelect);
+}
+
+nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_cache,
+                        const int32_t* keep_idx, int32_t n_tokens, int32_t budget, void* out_k,
+                        void* out_v) {
+  Geometry g;
+  nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
+  if (st != NX_OK) return st;
+  if (!k_cache || !v_cache || !keep_idx || !out_k || !out_v) return NX_EINVAL;
+  if (budget < 1) return NX_EINVAL;
+  const nx_unit u = single_unit(desc, k_cache, k_cache, v_cache, const_cast<int32_t*>(keep_idx),
+                                out_k, out_v, n_tokens, budget);
+  const int64_t d = desc->head_dim, hk = desc->n_kv_heads;
+  const int32_t kept = budget < n_tokens ? budget : n_tokens;
+  if (u.kv_head_stride < n_tokens * d || u.out_head_stride < kept * d) return NX_EINVAL;
+  const int32_t esz = elem_size(desc->dtype);
+  const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);
+  const Range rv = span(v_cache, hk, u.kv_head_stride, n_tokens * d, esz);
+  const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
+  const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
+  for (Range o : {rok, rov})
+    for (Range i : {rk, rv})
+      if (overlap(o, i)) return NX_EALIAS;
+  if (overlap(rok, rov)) return NX_EALIAS;
+  if (desc->workspace == nullptr || desc->workspace_bytes < 256) return NX_EWORKSPACE;
+  g.max_out_rows = kept;
+  Args a = base_args(desc, g, 0);
+  a.status = static_cast<uint32_t*>(desc->workspace);   // the status word is the only scratch used
+  a.single = u;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageKvCompact, kStageKvCompact);
+}
+
+nx_status nx_read_device_status(const nx_desc* desc) {
+  if (desc == nullptr || desc->workspace == nullptr || desc->workspace_bytes < 256) return NX_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(desc->stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return NX_EHIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, desc->workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return NX_EHIP;
+  if (word != 0) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(desc->workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+      return NX_EHIP;
+  }
+  if (word & kStatusNonFinite) return NX_ENONFINITE;
+  if (word & kStatusBadItem) return NX_EINVAL;
+  return NX_OK;
+}
+
+const char* nx_status_str(nx_status s) {
+  switch (s) {
+    case NX_OK: return "NX_OK";
+    case NX_EINVAL: return "NX_EINVAL: invalid argument";
+    case NX_EALIAS: return "NX_EALIAS: output overlaps an input";
+    case NX_EWORKSPACE: return "NX_EWORKSPACE: workspace missing or too small";
+    case NX_EUNSUPPORTED: return "NX_EUNSUPPORTED: shape or dtype outside the built kernels";
+    case NX_ENONFINITE: return "NX_ENONFINITE: non-finite Nexus weight";
+    case NX_EHIP: return "NX_EHIP: HIP runtime error";
+    default: return "unknown nx_status";
+  }
+}
+
+nx_status nx_profile_enable(int32_t enable) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  if (enable) {
+    for (auto& r : p.recs) { p.pool.push_back(r.e0); p.pool.push_back(r.e1); }
+    p.recs.clear();
+  }
+  p.on = enable != 0;
+  return NX_OK;
+}
+
+int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_stages) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lock(p.mu);
+  const int n = max_stages < kNumStages ? max_stages : kNumStages;
+  for (int i = 0; i < n; ++i) {
+    if (stage_ms) stage_ms[i] = 0.f;
+    if (stage_launches) stage_launches[i] = 0;
+  }
+  for (auto& r : p.recs) {
+    if (r.stage >= n) continue;
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) == hipSuccess && hipEventElapsedTime(&ms, r.e0, r.e1) == hipSuccess) {
+      if (stage_ms) stage_ms[r.stage] += ms;
+      if (stage_launches) stage_launches[r.stage] += 1;
+    }
+  }
+  return kNumStages;
+}
+
+const char* nx_stage_name(int32_t stage) {
+  static const char* names[kNumStages] = {"score_stats",    "score_combine", "score_probs",
+                                          "reservoir_keys", "topb_select",   "kv_compact"};
+  return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
+}
+
+}  // extern "C"

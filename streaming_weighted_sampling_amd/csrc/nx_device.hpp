@@ -1,0 +1,119 @@
+// Device helpers shared by the HIP kernels: head-unit resolution, the Philox
+// generator, key encoding and wavefront reductions.  gfx950 only (wave64).
+#pragma once
+
+#include "nx_internal.hpp"
+
+namespace nx {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+// One KV head of one (sequence, layer) item, resolved on the device.
+struct HeadUnit {
+  const char* q;       // first query row of the GQA group (query head h * G)
+  const char* k;       // this head's cache rows
+  const char* v;
+  int32_t* keep;       // this head's keep indices (budget entries)
+  char* out_k;
+  char* out_v;
+  const char* app_k;
+  const char* app_v;
+  int32_t n, budget, kept, n_append;
+  uint32_t layer, unit_id;
+  int32_t h;
+  bool valid;
+};
+
+__device__ inline nx_unit load_item(const Args& a, int item) {
+  if (a.units == nullptr) return a.single;
+  return a.units[item];
+}
+
+// Resolve head unit `hu` (= item * H_kv + kv_head); checks the item's fields.
+__device__ inline HeadUnit head_unit(const Args& a, int hu) {
+  const Geometry& g = a.g;
+  const int item = hu / g.h_kv;
+  const int h = hu - item * g.h_kv;
+  const nx_unit u = load_item(a, item);
+  const int64_t esz = g.dtype == NX_BF16 ? 2 : 4;
+  const int64_t d = g.head_dim;
+  HeadUnit r;
+  r.h = h;
+  r.n = u.n_tokens;
+  r.budget = u.budget;
+  r.kept = u.budget < u.n_tokens ? u.budget : u.n_tokens;
+  r.n_append = u.n_append;
+  r.layer = u.layer;
+  r.unit_id = u.seq_id * uint32_t(g.h_kv) + uint32_t(h);
+  r.q = static_cast<const char*>(u.q) + int64_t(h) * g.group * g.window * d * esz;
+  r.k = static_cast<const char*>(u.k) + int64_t(h) * u.kv_head_stride * esz;
+  r.v = u.v ? static_cast<const char*>(u.v) + int64_t(h) * u.kv_head_stride * esz : nullptr;
+  r.keep = u.keep ? u.keep + int64_t(h) * u.budget : nullptr;
+  r.out_k = u.out_k ? static_cast<char*>(u.out_k) + int64_t(h) * u.out_head_stride * esz : nullptr;
+  r.out_v = u.out_v ? static_cast<char*>(u.out_v) + int64_t(h) * u.out_head_stride * esz : nullptr;
+  r.app_k = u.app_k ? static_cast<const char*>(u.app_k) + int64_t(h) * u.n_append * d * esz : nullptr;
+  r.app_v = u.app_v ? static_cast<const char*>(u.app_v) + int64_t(h) * u.n_append * d * esz : nullptr;
+  bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && u.budget >= 1 &&
+            u.n_append >= 0 && a.n_sink + a.n_recent <= u.budget &&
+            u.kv_head_stride >= int64_t(u.n_tokens) * d && u.q != nullptr && u.k != nullptr;
+  if (u.out_k || u.out_v)
+    ok = ok && u.out_head_stride >= int64_t(r.kept + u.n_append) * d;
+  if (u.n_append > 0) ok = ok && u.app_k != nullptr && u.app_v != nullptr;
+  r.valid = ok;
+  return r;
+}
+
+__device__ inline void raise_status(const Args& a, uint32_t bits) {
+  atomicOr(a.status, bits);
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// Philox-4x32 S-box with multipliers 0xD2511F53 / 0xCD9E8D57, the round key
+// bumped by the Weyl constants 0x9E3779B9 / 0xBB67AE85 between rounds.
+__device__ inline uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = uint64_t(0xD2511F53u) * c.x;
+    const uint64_t p1 = uint64_t(0xCD9E8D57u) * c.z;
+    const uint32_t hi0 = uint32_t(p0 >> 32), lo0 = uint32_t(p0);
+    const uint32_t hi1 = uint32_t(p1 >> 32), lo1 = uint32_t(p1);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// 53-bit uniform in (0, 1] from the first two output words.
+__device__ inline double philox_uniform53(uint32_t x0, uint32_t x1) {
+  const uint64_t k53 = ((uint64_t(x0) << 32) | uint64_t(x1)) >> 11;
+  return double(k53 + 1) * 0x1p-53;
+}
+
+// Order-preserving encoding of an fp64 key as uint64 (larger key, larger code).
+// -0.0 is folded into +0.0 first.
+__device__ inline uint64_t key_code(double x) {
+  x = x + 0.0;
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ inline double key_decode(uint64_t c) {
+  const uint64_t b = (c >> 63) ? (c & 0x7FFFFFFFFFFFFFFFull) : ~c;
+  return __longlong_as_double(static_cast<long long>(b));
+}
+
+// Sums / max over the 32 lanes that share a lane-half (xor masks below 32).
+__device__ inline float half_sum(float x) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+__device__ inline float half_max(float x) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+}  // namespace nx

@@ -1,0 +1,110 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+//
+// One eviction event is five kernel stages per group of "head units" (one
+// head unit = one KV head of one (sequence, layer) item):
+//   score_stats    window logits Q K^T / sqrt(D) with bf16/fp32 MFMA, per-row
+//                  max and sum of exponentials over a token tile
+//   score_combine  merge the tile statistics of every window row
+//   score_probs    logits again, probabilities averaged over the GQA group:
+//                  direct score a, the H walk rows, and their Gram partials
+//   reservoir_keys walk coefficients, Nexus weight, Philox uniform, fp64 key
+//   topb_select    radix select of the budget largest keys, ascending indices
+//   kv_compact     gather of the kept K/V rows (+ optional appended rows)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/nexus.h"
+
+namespace nx {
+
+constexpr int kMaxWalk = 8;          // walk depth H supported by the kernels
+constexpr int kMaxWalkRows = 64;     // G * H window rows feeding the walk
+constexpr int kMaxRows = 1024;       // G * W rows per head unit
+constexpr int kTokPerBlock = 256;    // tokens per score workgroup
+constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
+constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
+
+enum Stage {
+  kStageScoreStats = 0,
+  kStageScoreCombine,
+  kStageScoreProbs,
+  kStageReservoirKeys,
+  kStageTopbSelect,
+  kStageKvCompact,
+  kNumStages
+};
+
+// Geometry of one call: everything the host derives from the descriptor.
+struct Geometry {
+  int32_t h_q, h_kv, group, head_dim, window, walk, rows, rows_pad, walk_rows;
+  int32_t dtype;
+  int32_t n_hu;          // head units = n_items * h_kv
+  int32_t max_tokens;
+  int32_t max_out_rows;  // compaction grid rows per head unit
+  int32_t n_t1, n_t2;    // score tiles per head unit (pass 1, pass 2)
+  int32_t n_kc;          // reservoir_keys chunks per head unit
+};
+
+// Workspace carving (byte offsets from the workspace base, 256-B aligned).
+struct WsLayout {
+  size_t status, part1, beta, a, p, gram, keys, selp, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const Geometry& g) {
+  WsLayout L{};
+  size_t off = 0;
+  const size_t hu = size_t(g.n_hu), nm = size_t(g.max_tokens);
+  L.status = off; off = align256(off + 256);
+  L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
+  L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
+  L.a = off;      off = align256(off + hu * nm * sizeof(float));
+  L.p = off;      off = align256(off + hu * size_t(g.walk > 0 ? g.walk : 1) * nm * sizeof(float));
+  L.gram = off;   off = align256(off + hu * g.n_t2 * kMaxWalk * kMaxWalk * sizeof(float));
+  L.keys = off;   off = align256(off + hu * nm * sizeof(uint64_t));
+  L.selp = off;   off = align256(off + hu * g.n_kc * 2 * sizeof(uint64_t));
+  L.total = off;
+  return L;
+}
+
+// Device status bits (OR-ed into the workspace status word).
+constexpr uint32_t kStatusNonFinite = 1u;
+constexpr uint32_t kStatusBadItem = 2u;
+
+// Kernel argument block, passed by value to every stage.
+struct Args {
+  const nx_unit* units;   // device array of items, or nullptr: use `single`
+  nx_unit single;
+  Geometry g;
+  float lambda, eps_tie, c_log2;   // c_log2 = log2(e) / sqrt(D)
+  int32_t n_sink, n_recent;
+  uint32_t step;
+  uint64_t seed;
+  // workspace
+  uint32_t* status;
+  float* part1;    // [n_hu][n_t1][rows_pad][2]: (max, sum) in log2 units
+  float* beta;     // [n_hu][rows_pad]
+  float* a;        // [n_hu][max_tokens]
+  float* p;        // [n_hu][walk][max_tokens]
+  float* gram;     // [n_hu][n_t2][kMaxWalk * kMaxWalk]
+  uint64_t* keys;  // [n_hu][max_tokens], order-preserving bits of the fp64 key
+  uint64_t* selp;  // [n_hu][n_kc][2]: OR and AND of the chunk's keys
+  // stage-only extras
+  const float* w_in;    // reservoir-only mode: weights [h_kv][n] (row stride n)
+  float* w_out;         // optional weight export [h_kv][n]
+  double* keys_out;     // optional key export [h_kv][n]
+  int32_t stop_after_weights;  // 1: reservoir_keys writes w_out and stops
+};
+
+hipError_t launch_score_stats(const Args& a, hipStream_t s);
+hipError_t launch_score_combine(const Args& a, hipStream_t s);
+hipError_t launch_score_probs(const Args& a, hipStream_t s);
+hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
+hipError_t launch_topb_select(const Args& a, hipStream_t s);
+hipError_t launch_kv_compact(const Args& a, hipStream_t s);
+
+}  // namespace nx

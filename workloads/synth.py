@@ -118,7 +118,8 @@ def _plant_head(k, qm, wl, hh_pos, br_pos, zipf_delta, g):
     m = qm.mean(dim=0)
     m_dir = m / m.norm()
     if rows < d:
-        pinv = torch.linalg.pinv(qm.double()).float()          # [D, rows]
+        # small [rows, D] pseudo-inverse, computed on the host in fp64
+        pinv = torch.linalg.pinv(qm.double().cpu()).float().to(qm.device)   # [D, rows]
         proj_q = pinv @ qm                                       # projector onto span(Q)
     else:
         pinv, proj_q = None, None
