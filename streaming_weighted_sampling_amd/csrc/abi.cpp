@@ -33,6 +33,7 @@ nx_status check_desc(const nx_desc* d) {
 
 nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, int32_t walk,
                         Geometry* g) {
+  *g = Geometry{};
   nx_status st = check_desc(d);
   if (st != NX_OK) return st;
   if (max_tokens < 1 || max_tokens > kMaxTokens || n_items < 1) return NX_EINVAL;
@@ -57,8 +58,15 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->n_hu = int32_t(n_hu);
   g->max_tokens = max_tokens;
   g->max_out_rows = max_tokens;
-  g->n_t1 = (max_tokens + kTokPerBlock - 1) / kTokPerBlock;
+  g->n_t1 = (max_tokens + kMinTokPerBlock - 1) / kMinTokPerBlock;
   g->n_t2 = g->n_t1;
+  // Tokens per score workgroup: the widest power of two in [256, 2048] that
+  // still gives >= 2048 workgroups per pass (8 per CU): fewer tile partials
+  // and less per-workgroup setup without starving the chip.
+  int32_t tpb = kMaxTokPerBlock;
+  while (tpb > kMinTokPerBlock && n_hu * ((int64_t(max_tokens) + tpb - 1) / tpb) < 2048) tpb /= 2;
+  g->tok_per_block = tpb;
+  g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
   return NX_OK;
 }
@@ -73,6 +81,7 @@ nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
   a->a = reinterpret_cast<float*>(base + L.a);
   a->p = reinterpret_cast<float*>(base + L.p);
   a->gram = reinterpret_cast<float*>(base + L.gram);
+  a->coef = reinterpret_cast<float*>(base + L.coef);
   a->keys = reinterpret_cast<uint64_t*>(base + L.keys);
   a->selp = reinterpret_cast<uint64_t*>(base + L.selp);
   return NX_OK;
@@ -138,6 +147,7 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
       case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
       case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
       case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
+      case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
       case kStageReservoirKeys: err = run_stage(st, s, [&] { return launch_reservoir_keys(a, s); }); break;
       case kStageTopbSelect: err = run_stage(st, s, [&] { return launch_topb_select(a, s); }); break;
       case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(a, s); }); break;
@@ -172,7 +182,7 @@ extern "C" {
 
 size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t max_units,
                                 int32_t walk_iters) {
-  Geometry g;
+  Geometry g{};
   if (make_geometry(desc, max_tokens, max_units, walk_iters, &g) != NX_OK) return 0;
   return ws_layout(g).total;
 }
@@ -180,7 +190,7 @@ size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t
 nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,
                         const void* v_cache, int32_t n_tokens, int32_t budget, int32_t walk_iters,
                         uint64_t seed, int32_t* out_keep_idx, void* out_k, void* out_v) {
-  Geometry g;
+  Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
   if (!q_window || !k_cache || !v_cache || !out_keep_idx || !out_k || !out_v) return NX_EINVAL;
@@ -210,7 +220,7 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
 
 nx_status nx_evict_batch(const nx_desc* desc, const nx_unit* units_dev, int32_t n_units,
                          int32_t max_tokens, int32_t walk_iters, uint64_t seed) {
-  Geometry g;
+  Geometry g{};
   nx_status st = make_geometry(desc, max_tokens, n_units, walk_iters, &g);
   if (st != NX_OK) return st;
   if (units_dev == nullptr) return NX_EINVAL;
@@ -224,7 +234,7 @@ nx_status nx_evict_batch(const nx_desc* desc, const nx_unit* units_dev, int32_t 
 
 nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void* k_cache,
                            int32_t n_tokens, int32_t walk_iters, float* out_w) {
-  Geometry g;
+  Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
   if (!q_window || !k_cache || !out_w) return NX_EINVAL;
@@ -243,7 +253,7 @@ nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void
 nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tokens,
                               int32_t budget, uint64_t seed, int32_t* out_keep_idx,
                               double* out_keys) {
-  Geometry g;
+  Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
   if (!w || !out_keep_idx) return NX_EINVAL;
@@ -262,7 +272,7 @@ nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tok
 nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_cache,
                         const int32_t* keep_idx, int32_t n_tokens, int32_t budget, void* out_k,
                         void* out_v) {
-  Geometry g;
+  Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
   if (!k_cache || !v_cache || !keep_idx || !out_k || !out_v) return NX_EINVAL;
@@ -350,8 +360,9 @@ int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_st
 }
 
 const char* nx_stage_name(int32_t stage) {
-  static const char* names[kNumStages] = {"score_stats",    "score_combine", "score_probs",
-                                          "reservoir_keys", "topb_select",   "kv_compact"};
+  static const char* names[kNumStages] = {"score_stats", "score_combine",  "score_probs",
+                                          "walk_coef",   "reservoir_keys", "topb_select",
+                                          "kv_compact"};
   return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
 }
 

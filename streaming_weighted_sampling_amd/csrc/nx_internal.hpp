@@ -1,13 +1,15 @@
 // Internal interface between the C ABI (abi.cpp) and the HIP kernels.
 //
-// One eviction event is five kernel stages per group of "head units" (one
-// head unit = one KV head of one (sequence, layer) item):
-//   score_stats    window logits Q K^T / sqrt(D) with bf16/fp32 MFMA, per-row
-//                  max and sum of exponentials over a token tile
+// One eviction event runs seven kernel stages over "head units" (one head
+// unit = one KV head of one (sequence, layer) item):
+//   score_stats    window logits Q K^T / sqrt(D) with bf16/fp32 MFMA; per tile
+//                  and window row the max and the sum of exponentials
 //   score_combine  merge the tile statistics of every window row
 //   score_probs    logits again, probabilities averaged over the GQA group:
 //                  direct score a, the H walk rows, and their Gram partials
-//   reservoir_keys walk coefficients, Nexus weight, Philox uniform, fp64 key
+//   walk_coef      reduce the Gram partials, run the walk recurrence, store
+//                  the per-row coefficients gamma_t / ||C||_1
+//   reservoir_keys Nexus weight, Philox uniform, fp64 key
 //   topb_select    radix select of the budget largest keys, ascending indices
 //   kv_compact     gather of the kept K/V rows (+ optional appended rows)
 #pragma once
@@ -23,7 +25,8 @@ namespace nx {
 constexpr int kMaxWalk = 8;          // walk depth H supported by the kernels
 constexpr int kMaxWalkRows = 64;     // G * H window rows feeding the walk
 constexpr int kMaxRows = 1024;       // G * W rows per head unit
-constexpr int kTokPerBlock = 256;    // tokens per score workgroup
+constexpr int kMinTokPerBlock = 256;   // smallest token range of a score workgroup
+constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two)
 constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
 
@@ -31,6 +34,7 @@ enum Stage {
   kStageScoreStats = 0,
   kStageScoreCombine,
   kStageScoreProbs,
+  kStageWalkCoef,
   kStageReservoirKeys,
   kStageTopbSelect,
   kStageKvCompact,
@@ -44,13 +48,15 @@ struct Geometry {
   int32_t n_hu;          // head units = n_items * h_kv
   int32_t max_tokens;
   int32_t max_out_rows;  // compaction grid rows per head unit
-  int32_t n_t1, n_t2;    // score tiles per head unit (pass 1, pass 2)
+  int32_t tok_per_block; // tokens per score workgroup for this call
+  int32_t n_tmax;        // score tiles per head unit at tok_per_block (for max_tokens)
+  int32_t n_t1, n_t2;    // workspace tile slots per head unit (sized for kMinTokPerBlock)
   int32_t n_kc;          // reservoir_keys chunks per head unit
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
-  size_t status, part1, beta, a, p, gram, keys, selp, total;
+  size_t status, part1, beta, a, p, gram, coef, keys, selp, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -65,6 +71,7 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.a = off;      off = align256(off + hu * nm * sizeof(float));
   L.p = off;      off = align256(off + hu * size_t(g.walk > 0 ? g.walk : 1) * nm * sizeof(float));
   L.gram = off;   off = align256(off + hu * g.n_t2 * kMaxWalk * kMaxWalk * sizeof(float));
+  L.coef = off;   off = align256(off + hu * kMaxWalk * sizeof(float));
   L.keys = off;   off = align256(off + hu * nm * sizeof(uint64_t));
   L.selp = off;   off = align256(off + hu * g.n_kc * 2 * sizeof(uint64_t));
   L.total = off;
@@ -91,6 +98,7 @@ struct Args {
   float* a;        // [n_hu][max_tokens]
   float* p;        // [n_hu][walk][max_tokens]
   float* gram;     // [n_hu][n_t2][kMaxWalk * kMaxWalk]
+  float* coef;     // [n_hu][kMaxWalk]: gamma_t / ||C||_1
   uint64_t* keys;  // [n_hu][max_tokens], order-preserving bits of the fp64 key
   uint64_t* selp;  // [n_hu][n_kc][2]: OR and AND of the chunk's keys
   // stage-only extras
@@ -103,6 +111,7 @@ struct Args {
 hipError_t launch_score_stats(const Args& a, hipStream_t s);
 hipError_t launch_score_combine(const Args& a, hipStream_t s);
 hipError_t launch_score_probs(const Args& a, hipStream_t s);
+hipError_t launch_walk_coef(const Args& a, hipStream_t s);
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
 hipError_t launch_topb_select(const Args& a, hipStream_t s);
 hipError_t launch_kv_compact(const Args& a, hipStream_t s);

@@ -3,11 +3,12 @@
 // [Nexus] = "Forget Without Compromise: Nexus Sampling for Streaming KV-Cache
 // Eviction Under Fixed Budgets" (academ.us article page).
 //
-// reservoir_keys  (many workgroups per head unit, 1024 tokens each)
+// walk_coef       (one wavefront per head unit)
 //   * walk coefficients of section 2.2 Eq. (4) from the Gram partials of the
 //     walk rows P_t: gamma_1 = 1, gamma_t = 1 + sum_{t'<t} gamma_t' <P_t, P_t'>,
-//     and c~_j = sum_t gamma_t P_t[j] / ||C||_1 with ||C||_1 = sum_t gamma_t |P_t|_1
+//     so that c~_j = sum_t gamma_t P_t[j] / ||C||_1, ||C||_1 = sum_t gamma_t |P_t|_1
 //     (the rank-1 form of the recurrence, appendix 8.6; no N-vector is carried)
+// reservoir_keys  (many workgroups per head unit, 1024 tokens each)
 //   * Nexus weight w_j = a_j + lambda c~_j + eps j/(N-1) (Eqs. 2 and 5)
 //   * Philox4x32-10 uniform u_j, counter (j, unit, layer, step), key = seed
 //   * A-Res key ln(u_j)/w_j in fp64 (section 2.3 Eq. 6 with n = 1), -inf for
@@ -29,32 +30,37 @@ constexpr int kKeysThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
-__global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args a) {
+// One wavefront per head unit: fixed-order reduction of the per-tile Gram
+// partials (lane-strided sums, then a butterfly), then the walk recurrence
+// of section 2.2 Eq. (4) in its rank-1 form: gamma_1 = 1,
+// gamma_t = 1 + sum_{t'<t} gamma_t' <P_t, P_t'>, ||C||_1 = sum_t gamma_t |P_t|_1.
+__global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
   const Geometry& g = a.g;
-  const int hu = blockIdx.y, chunk = blockIdx.x;
+  const int hu = blockIdx.x;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) return;
-  const int j0 = chunk * kKeysPerBlock;
-  if (j0 >= u.n) return;
-  __shared__ float s_coef[kMaxWalk];
-  __shared__ uint64_t s_or[kKeysThreads / 64], s_and[kKeysThreads / 64];
-
-  if (a.w_in == nullptr && threadIdx.x == 0) {
-    // Fixed-order reduction of the per-tile Gram partials.
-    float gm[kMaxWalk][kMaxWalk];
+  const int lane = threadIdx.x;
+  const int n_tiles = (u.n + g.tok_per_block - 1) / g.tok_per_block;
+  const float* gp = a.gram + size_t(hu) * g.n_t2 * (kMaxWalk * kMaxWalk);
+  float gm[kMaxWalk][kMaxWalk];
+#pragma unroll
+  for (int t = 0; t < kMaxWalk; ++t)
+#pragma unroll
+    for (int t2 = 0; t2 < kMaxWalk; ++t2) gm[t][t2] = 0.f;
+  for (int tl = lane; tl < n_tiles; tl += 64) {
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t)
 #pragma unroll
-      for (int t2 = 0; t2 < kMaxWalk; ++t2) gm[t][t2] = 0.f;
-    const int n_tiles = (u.n + kTokPerBlock - 1) / kTokPerBlock;
-    const float* gp = a.gram + size_t(hu) * g.n_t2 * (kMaxWalk * kMaxWalk);
-    for (int tl = 0; tl < n_tiles; ++tl) {
+      for (int t2 = 0; t2 <= t; ++t2)
+        if (t < g.walk) gm[t][t2] += gp[size_t(tl) * (kMaxWalk * kMaxWalk) + t * kMaxWalk + t2];
+  }
 #pragma unroll
-      for (int t = 0; t < kMaxWalk; ++t)
+  for (int t = 0; t < kMaxWalk; ++t)
 #pragma unroll
-        for (int t2 = 0; t2 <= t; ++t2)
-          if (t < g.walk) gm[t][t2] += gp[size_t(tl) * (kMaxWalk * kMaxWalk) + t * kMaxWalk + t2];
-    }
+    for (int t2 = 0; t2 <= t; ++t2)
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) gm[t][t2] += __shfl_xor(gm[t][t2], m, 64);
+  if (lane == 0) {
     float gam[kMaxWalk];
     float norm = 0.f;
 #pragma unroll
@@ -66,8 +72,23 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
       if (t < g.walk) norm = fmaf(x, gm[t][t], norm);
     }
 #pragma unroll
-    for (int t = 0; t < kMaxWalk; ++t) s_coef[t] = (t < g.walk) ? gam[t] / norm : 0.f;
+    for (int t = 0; t < kMaxWalk; ++t)
+      a.coef[size_t(hu) * kMaxWalk + t] = (t < g.walk) ? gam[t] / norm : 0.f;
   }
+}
+
+__global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.y, chunk = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int j0 = chunk * kKeysPerBlock;
+  if (j0 >= u.n) return;
+  __shared__ float s_coef[kMaxWalk];
+  __shared__ uint64_t s_or[kKeysThreads / 64], s_and[kKeysThreads / 64];
+
+  if (threadIdx.x < kMaxWalk)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
   __syncthreads();
 
   const float* a_in = a.a + size_t(hu) * g.max_tokens;
@@ -275,6 +296,11 @@ __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) 
 }
 
 }  // namespace
+
+hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(walk_coef_kernel, dim3(a.g.n_hu), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL(reservoir_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);

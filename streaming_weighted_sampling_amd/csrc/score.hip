@@ -140,10 +140,42 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
   return acc;
 }
 
-// One sweep of pass 1 over the block's tokens.  kExact = false keeps one
-// shift per row (the row max of the first 32 tokens) and adds 2^(y - shift);
+// Streams the block's K sub-tiles (32 tokens each) through a two-slot LDS
+// buffer.  Global loads run kPrefetch sub-tiles ahead in a register ring so
+// that several 8-KB tiles per workgroup are in flight while the MFMA and
+// exponential work of the current one proceeds.  body(st, lds) consumes
+// sub-tile st; one barrier per sub-tile.
+constexpr int kPrefetch = 4;
+
+template <typename T, int D, typename Body>
+__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* lds0, char* lds1,
+                                   Body&& body) {
+  using GE = Geo<T, D>;
+  uint4 ring[kPrefetch][GE::kLoads];
+#pragma unroll
+  for (int r = 0; r < kPrefetch; ++r)
+    if (r < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * r, u.n, ring[r]);
+  store_tile_lds<T, D>(lds0, ring[0]);
+  __syncthreads();
+  for (int st0 = 0; st0 < n_sub; st0 += kPrefetch) {
+#pragma unroll
+    for (int r = 0; r < kPrefetch; ++r) {
+      const int st = st0 + r;
+      if (st < n_sub) {
+        // ring[r] held sub-tile st, already copied to LDS: refill it.
+        if (st + kPrefetch < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * (st + kPrefetch), u.n, ring[r]);
+        body(st, (st & 1) ? lds1 : lds0);
+        if (st + 1 < n_sub) store_tile_lds<T, D>((st & 1) ? lds0 : lds1, ring[(r + 1) % kPrefetch]);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// Pass 1 over the block's tokens.  kExact = false keeps one shift per row (the
+// row max over the first 32 tokens) and adds 2^(y - shift) per logit;
 // kExact = true keeps a per-lane running max (two exponentials per logit) and
-// is only used when the cheap sweep overflowed.
+// only runs when the cheap sweep overflowed.
 template <typename T, int D, int MPW, bool kExact>
 __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int n_sub,
                                    const uint4 (&qf)[MPW][Geo<T, D>::kChunks],
@@ -152,16 +184,10 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const int n_mt = a.g.rows_pad / 32;
   const float c = a.c_log2;
-  uint4 pre[GE::kLoads];
-  load_tile_regs<T, D>(u.k, t0, u.n, pre);
-  store_tile_lds<T, D>(lds0, pre);
-  __syncthreads();
-  for (int st = 0; st < n_sub; ++st) {
-    char* cur = (st & 1) ? lds1 : lds0;
-    char* nxt = (st & 1) ? lds0 : lds1;
-    if (st + 1 < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * (st + 1), u.n, pre);
+  sweep_tiles<T, D>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
+    const bool full = t0 + 32 * st + 32 <= u.n;      // wave-uniform
     const bool valid = t0 + 32 * st + nn < u.n;
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
@@ -170,21 +196,19 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
         if constexpr (!kExact) {
           if (st == 0) {
 #pragma unroll
+            for (int v = 0; v < 16; ++v) my[i][v] = half_max(valid ? acc[v] * c : -INFINITY);
+          }
+          if (full) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) z[i][v] += __builtin_amdgcn_exp2f(fmaf(acc[v], c, -my[i][v]));
+          } else {
+#pragma unroll
             for (int v = 0; v < 16; ++v) {
-              my[i][v] = half_max(valid ? acc[v] * c : -INFINITY);
-              z[i][v] = 0.f;
+              const float e = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -my[i][v]));
+              z[i][v] += valid ? e : 0.f;
             }
           }
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -my[i][v]));
-            z[i][v] += valid ? e : 0.f;
-          }
         } else {
-          if (st == 0) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) { my[i][v] = -INFINITY; z[i][v] = 0.f; }
-          }
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const float y = acc[v] * c;
@@ -197,21 +221,20 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
         }
       }
     }
-    if (st + 1 < n_sub) store_tile_lds<T, D>(nxt, pre);
-    __syncthreads();
-  }
+  });
 }
 
+// Pass 1 on one (head unit, tile) item: writes the tile's (max, sum) pair
+// for every window row.
 template <typename T, int D, int MPW>
-__global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
+__device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
-  __shared__ __align__(16) char lds[2][GE::kTileBytes];
-  const int hu = blockIdx.y, tile = blockIdx.x;
-  const HeadUnit u = head_unit(a, hu);
-  if (!u.valid) return;
-  const int t0 = tile * kTokPerBlock;
+  char* lds0 = smem;
+  char* lds1 = smem + GE::kTileBytes;
+  const int tpb = a.g.tok_per_block;
+  const int t0 = tile * tpb;
   if (t0 >= u.n) return;
-  const int n_sub = (min(t0 + kTokPerBlock, u.n) - t0 + 31) / 32;
+  const int n_sub = (min(t0 + tpb, u.n) - t0 + 31) / 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const int n_mt = a.g.rows_pad / 32;
 
@@ -222,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
   for (int i = 0; i < MPW; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) { my[i][v] = 0.f; z[i][v] = 0.f; }
-  stats_sweep<T, D, MPW, false>(a, u, t0, n_sub, qf, my, z, lds[0], lds[1]);
+  stats_sweep<T, D, MPW, false>(a, u, t0, n_sub, qf, my, z, lds0, lds1);
 
   // Merge the 32 lanes of each half (they share rows); detect overflow.
   float zr[MPW][16];
@@ -236,7 +259,11 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
     }
   }
   if (__syncthreads_or(bad)) {
-    stats_sweep<T, D, MPW, true>(a, u, t0, n_sub, qf, my, z, lds[0], lds[1]);
+#pragma unroll
+    for (int i = 0; i < MPW; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { my[i][v] = -INFINITY; z[i][v] = 0.f; }
+    stats_sweep<T, D, MPW, true>(a, u, t0, n_sub, qf, my, z, lds0, lds1);
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
 #pragma unroll
@@ -263,25 +290,39 @@ __global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
-  const int hu = blockIdx.x;
+// Merge the tile pairs of every window row of one head unit in tile order:
+// beta_r = max_r + log2(Z_r) + log2(G*W) (whole workgroup, one row per thread;
+// tile pairs are loaded 16 at a time so the loads overlap).
+__device__ inline void combine_unit(const Args& a, int hu) {
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) {
     if (threadIdx.x == 0) raise_status(a, kStatusBadItem);
     return;
   }
-  const int n_tiles = (u.n + kTokPerBlock - 1) / kTokPerBlock;
+  const int n_tiles = (u.n + a.g.tok_per_block - 1) / a.g.tok_per_block;
   const float* part = a.part1 + size_t(hu) * a.g.n_t1 * a.g.rows_pad * 2;
   const float log2_gw = log2f(float(a.g.group * a.g.window));
+  constexpr int kBatch = 16;
   for (int rho = threadIdx.x; rho < a.g.rows_pad; rho += kThreads) {
     float beta = INFINITY;
     if (rho < a.g.rows) {
-      float m = -INFINITY;
-      for (int t = 0; t < n_tiles; ++t) m = fmaxf(m, part[(size_t(t) * a.g.rows_pad + rho) * 2]);
-      float zsum = 0.f;
-      for (int t = 0; t < n_tiles; ++t) {
-        const float2 p = *reinterpret_cast<const float2*>(part + (size_t(t) * a.g.rows_pad + rho) * 2);
-        zsum += p.y * __builtin_amdgcn_exp2f(p.x - m);
+      float m = -INFINITY, zsum = 0.f;
+      for (int t0 = 0; t0 < n_tiles; t0 += kBatch) {
+        float2 p[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          p[i] = t0 + i < n_tiles
+                     ? *reinterpret_cast<const float2*>(part + (size_t(t0 + i) * a.g.rows_pad + rho) * 2)
+                     : make_float2(-INFINITY, 0.f);
+        float mb = m;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) mb = fmaxf(mb, p[i].x);
+        float zb = zsum * __builtin_amdgcn_exp2f(m - mb);
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (t0 + i < n_tiles) zb += p[i].y * __builtin_amdgcn_exp2f(p[i].x - mb);
+        m = mb;
+        zsum = zb;
       }
       beta = m + log2f(zsum) + log2_gw;
     }
@@ -289,22 +330,32 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
   }
 }
 
+// Pass 2 on one (head unit, tile) item.
 template <typename T, int D, int MPW>
-__global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
+__device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
-  __shared__ __align__(16) char lds[2][GE::kTileBytes];
-  __shared__ float s_tok[kWaves][32];
-  __shared__ float s_walk[kMaxWalkRows][32];
-  const int hu = blockIdx.y, tile = blockIdx.x;
-  const HeadUnit u = head_unit(a, hu);
-  if (!u.valid) return;
-  const int t0 = tile * kTokPerBlock;
+  char* lds0 = smem;
+  char* lds1 = smem + GE::kTileBytes;
+  // per-token partial sums of each wave; raw walk rows (generic path); Gram
+  auto s_tok = reinterpret_cast<float (*)[32][kWaves]>(smem + 2 * GE::kTileBytes);
+  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(
+      smem + 2 * GE::kTileBytes + 2 * 32 * kWaves * sizeof(float));
+  auto s_gram = reinterpret_cast<float (*)[kMaxWalk * kMaxWalk]>(
+      smem + 2 * GE::kTileBytes + (2 * 32 * kWaves + 2 * kMaxWalkRows * 32) * sizeof(float));
+  const int tpb = a.g.tok_per_block;
+  const int t0 = tile * tpb;
   if (t0 >= u.n) return;
-  const int n_sub = (min(t0 + kTokPerBlock, u.n) - t0 + 31) / 32;
+  const int n_sub = (min(t0 + tpb, u.n) - t0 + 31) / 32;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const Geometry& g = a.g;
   const int n_mt = g.rows_pad / 32;
   const float c = a.c_log2;
+  // Walk rows live in M-tile 0 (wave 0) when G*H <= 32.  With G = 4 or 8 each
+  // walk row t covers whole 4-row groups of the MFMA output (rows 4q'..4q'+3,
+  // q' = 2*(v/4) + half), so wave 0 sums them in registers: P_t = S_t (G = 4)
+  // or S_2t + S_2t+1 (G = 8).  Other shapes go through LDS.
+  const int gpr = g.group / 4;   // 4-row groups per walk row
+  const bool fast_walk = g.walk_rows <= 32 && (gpr == 1 || gpr == 2);
 
   uint4 qf[MPW][GE::kChunks];
   load_q<T, D, MPW>(a, u, wave, nn, hh, qf);
@@ -326,14 +377,47 @@ __global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
   float* p_out = a.p + size_t(hu) * g.walk * g.max_tokens;
   const float wf = float(g.window);
 
-  uint4 pre[GE::kLoads];
-  load_tile_regs<T, D>(u.k, t0, u.n, pre);
-  store_tile_lds<T, D>(lds[0], pre);
-  __syncthreads();
-  for (int st = 0; st < n_sub; ++st) {
-    char* cur = lds[st & 1];
-    char* nxt = lds[(st + 1) & 1];
-    if (st + 1 < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * (st + 1), u.n, pre);
+  // P_t of one token (lanes 0..31 of the walk wave): store and accumulate
+  // the Gram partials (off-diagonal <P_t, P_t'>, diagonal |P_t|_1).
+  auto walk_out = [&](int tok, const float (&pt)[kMaxWalk]) {
+#pragma unroll
+    for (int t = 0; t < kMaxWalk; ++t) {
+      if (t < g.walk) {
+        p_out[size_t(t) * g.max_tokens + tok] = pt[t];
+#pragma unroll
+        for (int t2 = 0; t2 <= t; ++t2)
+          gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
+      }
+    }
+  };
+
+  // Direct score of sub-tile s, finalised during sub-tile s + 1 by wave s % 4.
+  auto finalize = [&](int s) {
+    if (wave != (s & (kWaves - 1)) || hh != 0) return;
+    const int b = s & 1;
+    const int tok = t0 + 32 * s + nn;
+    if (tok >= u.n) return;
+    const float4 p4 = *reinterpret_cast<const float4*>(&s_tok[b][nn][0]);
+    a_out[tok] = ((p4.x + p4.y) + p4.z) + p4.w;
+    if (!fast_walk && g.walk > 0) {
+      float pt[kMaxWalk];
+#pragma unroll
+      for (int t = 0; t < kMaxWalk; ++t) {
+        pt[t] = 0.f;
+        if (t < g.walk) {
+          float sum = 0.f;
+          for (int i = 0; i < g.group; ++i) sum += s_walk[b][t * g.group + i][nn];
+          pt[t] = wf * sum;
+        }
+      }
+      walk_out(tok, pt);
+    }
+  };
+
+  sweep_tiles<T, D>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
+    if (st > 0) finalize(st - 1);
+    const int b = st & 1;
+    const int tok = t0 + 32 * st + nn;
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     float tp = 0.f;
@@ -342,61 +426,100 @@ __global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
       const int mt = wave + kWaves * i;
       if (mt < n_mt) {
         const floatx16_t acc = mfma_tile<T, D>(qf[i], kf);
-        const bool walk_tile = mt * 32 < g.walk_rows;
+        float e[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
-          tp += e;
-          if (walk_tile) {
-            const int rho = mt * 32 + out_row(v, hh);
-            if (rho < g.walk_rows) s_walk[rho][nn] = e;
+          e[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
+          tp += e[v];
+        }
+        if (mt == 0 && g.walk > 0) {
+          if (fast_walk) {
+            float sg[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sg[q] = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
+            float grp[8];   // group sums S_q' in q' = 2q + half order
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float other = __shfl_xor(sg[q], 32, 64);
+              grp[2 * q] = hh == 0 ? sg[q] : other;
+              grp[2 * q + 1] = hh == 0 ? other : sg[q];
+            }
+            if (hh == 0 && tok < u.n) {
+              float pt[kMaxWalk];
+#pragma unroll
+              for (int t = 0; t < kMaxWalk; ++t) {
+                const float s1 = grp[t < 8 ? t : 7];
+                const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
+                pt[t] = wf * (gpr == 1 ? s1 : s2);
+              }
+              walk_out(tok, pt);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int rho = out_row(v, hh);
+              if (rho < g.walk_rows) s_walk[b][rho][nn] = e[v];
+            }
           }
         }
       }
     }
     tp += __shfl_xor(tp, 32, 64);
-    if (hh == 0) s_tok[wave][nn] = tp;
-    __syncthreads();
-    if (threadIdx.x < 32) {
-      const int j = threadIdx.x;
-      const int tok = t0 + 32 * st + j;
-      if (tok < u.n) {
-        a_out[tok] = ((s_tok[0][j] + s_tok[1][j]) + s_tok[2][j]) + s_tok[3][j];
-        float pt[kMaxWalk];
-#pragma unroll
-        for (int t = 0; t < kMaxWalk; ++t) {
-          pt[t] = 0.f;
-          if (t < g.walk) {
-            float s = 0.f;
-            for (int i = 0; i < g.group; ++i) s += s_walk[t * g.group + i][j];
-            pt[t] = wf * s;
-            p_out[size_t(t) * g.max_tokens + tok] = pt[t];
-          }
-        }
-        // Off-diagonal: <P_t, P_t'> for t' < t; diagonal: the row sum |P_t|_1.
-#pragma unroll
-        for (int t = 0; t < kMaxWalk; ++t)
-#pragma unroll
-          for (int t2 = 0; t2 <= t; ++t2)
-            gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
-      }
-    }
-    if (st + 1 < n_sub) store_tile_lds<T, D>(nxt, pre);
-    __syncthreads();
-  }
-  if (wave == 0) {
-    float* gout = a.gram + (size_t(hu) * g.n_t2 + tile) * (kMaxWalk * kMaxWalk);
+    if (hh == 0) s_tok[b][nn][wave] = tp;
+  });
+  finalize(n_sub - 1);
+
+  // Fixed-order Gram reduction: lanes within each wave, then waves 0..3.
+  if (hh == 0) {
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
 #pragma unroll
       for (int t2 = 0; t2 <= t; ++t2) {
         if (t < g.walk) {
-          const float s = half_sum(gacc[t][t2]);
-          if (lane == 0) gout[t * kMaxWalk + t2] = s;
+          const float sum = half_sum(gacc[t][t2]);
+          if (nn == 0) s_gram[wave][t * kMaxWalk + t2] = sum;
         }
       }
     }
   }
+  __syncthreads();
+  if (threadIdx.x < kMaxWalk * kMaxWalk) {
+    const int t = threadIdx.x / kMaxWalk, t2 = threadIdx.x % kMaxWalk;
+    if (t < g.walk && t2 <= t) {
+      float* gout = a.gram + (size_t(hu) * g.n_t2 + tile) * (kMaxWalk * kMaxWalk);
+      gout[threadIdx.x] = ((s_gram[0][threadIdx.x] + s_gram[1][threadIdx.x]) + s_gram[2][threadIdx.x]) +
+                          s_gram[3][threadIdx.x];
+    }
+  }
+}
+
+template <typename T, int D>
+constexpr int smem_bytes() {
+  return 2 * Geo<T, D>::kTileBytes +
+         int(sizeof(float)) * (2 * 32 * kWaves + 2 * kMaxWalkRows * 32 + kWaves * kMaxWalk * kMaxWalk);
+}
+
+// Pass 1: one workgroup per (tile, head unit).
+template <typename T, int D, int MPW>
+__global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
+  __shared__ __align__(16) char smem[2 * Geo<T, D>::kTileBytes];
+  const int tile = blockIdx.x, hu = blockIdx.y;
+  const HeadUnit u = head_unit(a, hu);
+  if (u.valid) stats_item<T, D, MPW>(a, u, hu, tile, smem);
+}
+
+// Row merge: one workgroup per head unit.
+__global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
+  combine_unit(a, blockIdx.x);
+}
+
+// Pass 2: one workgroup per (tile, head unit).
+template <typename T, int D, int MPW>
+__global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
+  __shared__ __align__(16) char smem[smem_bytes<T, D>()];
+  const int tile = blockIdx.x, hu = blockIdx.y;
+  const HeadUnit u = head_unit(a, hu);
+  if (u.valid) probs_item<T, D, MPW>(a, u, hu, tile, smem);
 }
 
 int mtiles_per_wave(const Geometry& g) {
@@ -405,38 +528,33 @@ int mtiles_per_wave(const Geometry& g) {
   return per <= 1 ? 1 : per <= 2 ? 2 : 4;
 }
 
-template <int MPW, typename T, int D>
-hipError_t launch_stats_t(const Args& a, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((score_stats_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-template <int MPW, typename T, int D>
-hipError_t launch_probs_t(const Args& a, hipStream_t s, dim3 grid) {
-  hipLaunchKernelGGL((score_probs_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
+template <bool kProbs, int MPW, typename T, int D>
+hipError_t launch_t(const Args& a, hipStream_t s) {
+  const dim3 grid(a.g.n_tmax, a.g.n_hu);
+  if (kProbs)
+    hipLaunchKernelGGL((score_probs_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_stats_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <bool kProbs>
 hipError_t launch_pass(const Args& a, hipStream_t s) {
   const Geometry& g = a.g;
-  const dim3 grid(kProbs ? g.n_t2 : g.n_t1, g.n_hu);
   const int mpw = mtiles_per_wave(g);
-#define NX_PASS(MPW, T, D) \
-  return kProbs ? launch_probs_t<MPW, T, D>(a, s, grid) : launch_stats_t<MPW, T, D>(a, s, grid)
-#define NX_PASS_MPW(T, D)                 \
-  switch (mpw) {                          \
-    case 1: NX_PASS(1, T, D);             \
-    case 2: NX_PASS(2, T, D);             \
-    default: NX_PASS(4, T, D);            \
+#define NX_MPW(T, D)                                 \
+  switch (mpw) {                                     \
+    case 1: return launch_t<kProbs, 1, T, D>(a, s);  \
+    case 2: return launch_t<kProbs, 2, T, D>(a, s);  \
+    default: return launch_t<kProbs, 4, T, D>(a, s); \
   }
   if (g.dtype == NX_BF16) {
-    if (g.head_dim == 128) { NX_PASS_MPW(uint16_t, 128) }
-    NX_PASS_MPW(uint16_t, 64)
+    if (g.head_dim == 128) { NX_MPW(uint16_t, 128) }
+    NX_MPW(uint16_t, 64)
   }
-  if (g.head_dim == 128) { NX_PASS_MPW(float, 128) }
-  NX_PASS_MPW(float, 64)
-#undef NX_PASS_MPW
-#undef NX_PASS
+  if (g.head_dim == 128) { NX_MPW(float, 128) }
+  NX_MPW(float, 64)
+#undef NX_MPW
 }
 
 }  // namespace

@@ -86,7 +86,8 @@ def test_status_strings(lib):
         assert lib.nx_status_str(code).decode().startswith("NX_")
     assert lib.nx_status_str(-99).decode() == "unknown nx_status"
     assert lib.nx_stage_name(0) == b"score_stats"
-    assert lib.nx_stage_name(5) == b"kv_compact"
+    assert lib.nx_stage_name(3) == b"walk_coef"
+    assert lib.nx_stage_name(6) == b"kv_compact"
 
 
 def test_workspace_query(lib):
