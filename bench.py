@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1-GiB device copy (3 times), the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the eviction path has no multi-GPU mode "
@@ -95,9 +98,19 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    wl = WORKLOADS["llama3_8b_stream32"]
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}))
+        return
+
+    wl = WORKLOADS["llama3_8b_stream32"]
     data = build_batch(wl, dev)
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)

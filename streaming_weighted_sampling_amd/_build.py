@@ -18,6 +18,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
     # Packed fp32 VALU ops stay disabled (plain v_fma_f32 / v_add_f32 only).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (no accvgpr copies before the softmax VALU work).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -37,6 +37,11 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   nx_status st = check_desc(d);
   if (st != NX_OK) return st;
   if (max_tokens < 1 || max_tokens > kMaxTokens || n_items < 1) return NX_EINVAL;
+  // One KV head's rows (and each per-head workspace array) stay below 2 GB so
+  // 32-bit buffer offsets address them.
+  if (int64_t(max_tokens) * d->head_dim * elem_size(d->dtype) > (int64_t(1) << 31) ||
+      int64_t(max_tokens) * kMaxWalk * 4 > (int64_t(1) << 31))
+    return NX_EUNSUPPORTED;
   if (walk < 0 || walk > d->window) return NX_EINVAL;
   const int32_t group = d->n_q_heads / d->n_kv_heads;
   const int64_t rows = int64_t(group) * d->window;

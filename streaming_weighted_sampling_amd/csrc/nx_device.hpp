@@ -8,6 +8,36 @@ namespace nx {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Global memory through a buffer resource (MUBUF instructions).  Unlike FLAT
+// accesses these count only against the vector-memory counter, so waiting for
+// an LDS read never waits for in-flight global loads; loads at offsets past
+// `bytes` return zero and stores there are dropped.  The base and size must
+// be uniform across the wavefront.
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9: raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;          // cache-policy bit for streaming stores
+
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ Buf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3)) {}
+  __device__ uint4 ld16(uint32_t off) const {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ float ldf(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+  template <int kAux = 0>
+  __device__ void st16(uint32_t off, uint4 v) const {
+    const u32x4_t x = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, kAux);
+  }
+  __device__ void stf(uint32_t off, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+  }
+};
 
 // One KV head of one (sequence, layer) item, resolved on the device.
 struct HeadUnit {

@@ -72,31 +72,27 @@ __device__ inline void load_q(const Args& a, const HeadUnit& u, int wave, int nn
                               uint4 (&qf)[MPW][Geo<T, D>::kChunks]) {
   using GE = Geo<T, D>;
   const int n_mt = a.g.rows_pad / 32;
+  const Buf qb(u.q, uint32_t(a.g.group * a.g.window * GE::kRowBytes));
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
     const int mt = wave + kWaves * i;
     int qh = 0, wpos = 0;
     const bool ok = mt < n_mt && row_source(a.g, mt * 32 + nn, qh, wpos);
-    const char* src = u.q + (int64_t(qh) * a.g.window + wpos) * GE::kRowBytes + hh * GE::kHalfBytes;
+    const uint32_t src = uint32_t((qh * a.g.window + wpos) * GE::kRowBytes + hh * GE::kHalfBytes);
 #pragma unroll
     for (int c = 0; c < GE::kChunks; ++c)
-      qf[i][c] = ok ? *reinterpret_cast<const uint4*>(src + 16 * c) : make_uint4(0, 0, 0, 0);
+      qf[i][c] = ok ? qb.ld16(src + 16 * c) : make_uint4(0, 0, 0, 0);
   }
 }
 
+// Sub-tile `st` of the block (32 tokens) into registers; kb covers exactly the
+// block's valid tokens, so rows past the cache end read as zero.
 template <typename T, int D>
-__device__ inline void load_tile_regs(const char* kbase, int tok0, int n,
-                                      uint4 (&r)[Geo<T, D>::kLoads]) {
+__device__ inline void load_tile_regs(const Buf& kb, int st, uint4 (&r)[Geo<T, D>::kLoads]) {
   using GE = Geo<T, D>;
-  constexpr int kPerRow = GE::kRowBytes / 16;
 #pragma unroll
-  for (int i = 0; i < GE::kLoads; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int row = c / kPerRow, col = c - row * kPerRow;
-    const int tok = tok0 + row;
-    r[i] = tok < n ? *reinterpret_cast<const uint4*>(kbase + int64_t(tok) * GE::kRowBytes + 16 * col)
-                   : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < GE::kLoads; ++i)
+    r[i] = kb.ld16(uint32_t(st * 32 * GE::kRowBytes + 16 * (threadIdx.x + kThreads * i)));
 }
 
 template <typename T, int D>
@@ -151,10 +147,12 @@ template <typename T, int D, typename Body>
 __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* lds0, char* lds1,
                                    Body&& body) {
   using GE = Geo<T, D>;
+  const int t1 = min(t0 + 32 * n_sub, u.n);
+  const Buf kb(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
   uint4 ring[kPrefetch][GE::kLoads];
 #pragma unroll
   for (int r = 0; r < kPrefetch; ++r)
-    if (r < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * r, u.n, ring[r]);
+    if (r < n_sub) load_tile_regs<T, D>(kb, r, ring[r]);
   store_tile_lds<T, D>(lds0, ring[0]);
   __syncthreads();
   for (int st0 = 0; st0 < n_sub; st0 += kPrefetch) {
@@ -163,7 +161,7 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* l
       const int st = st0 + r;
       if (st < n_sub) {
         // ring[r] held sub-tile st, already copied to LDS: refill it.
-        if (st + kPrefetch < n_sub) load_tile_regs<T, D>(u.k, t0 + 32 * (st + kPrefetch), u.n, ring[r]);
+        if (st + kPrefetch < n_sub) load_tile_regs<T, D>(kb, st + kPrefetch, ring[r]);
         body(st, (st & 1) ? lds1 : lds0);
         if (st + 1 < n_sub) store_tile_lds<T, D>((st & 1) ? lds0 : lds1, ring[(r + 1) % kPrefetch]);
         __syncthreads();
@@ -373,8 +371,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int t2 = 0; t2 < kMaxWalk; ++t2) gacc[t][t2] = 0.f;
 
-  float* a_out = a.a + size_t(hu) * g.max_tokens;
-  float* p_out = a.p + size_t(hu) * g.walk * g.max_tokens;
+  const Buf a_out(a.a + size_t(hu) * g.max_tokens, uint32_t(g.max_tokens * 4));
+  const Buf p_out(a.p + size_t(hu) * g.walk * g.max_tokens, uint32_t(g.walk * g.max_tokens * 4));
   const float wf = float(g.window);
 
   // P_t of one token (lanes 0..31 of the walk wave): store and accumulate
@@ -383,7 +381,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
       if (t < g.walk) {
-        p_out[size_t(t) * g.max_tokens + tok] = pt[t];
+        p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
 #pragma unroll
         for (int t2 = 0; t2 <= t; ++t2)
           gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
@@ -398,7 +396,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     const int tok = t0 + 32 * s + nn;
     if (tok >= u.n) return;
     const float4 p4 = *reinterpret_cast<const float4*>(&s_tok[b][nn][0]);
-    a_out[tok] = ((p4.x + p4.y) + p4.z) + p4.w;
+    a_out.stf(uint32_t(tok * 4), ((p4.x + p4.y) + p4.z) + p4.w);
     if (!fast_walk && g.walk > 0) {
       float pt[kMaxWalk];
 #pragma unroll

@@ -1,0 +1,91 @@
+"""Streaming eviction over every layer: append new rows, then evict back to B.
+
+[Nexus] ("Forget Without Compromise: Nexus Sampling for Streaming KV-Cache
+Eviction Under Fixed Budgets", section 2.1) treats eviction as a stream: the
+cache grows as tokens arrive and, whenever the budget is hit, keeps B
+positions and continues with those rows.  This driver holds two capacity
+buffers per layer and ping-pongs between them.  One `step()` is one
+nx_evict_batch call over all layers; its compaction also writes the rows
+that arrive before the next event right after the kept ones, so a step reads
+each resident row once and writes the next cache once.  Marshalling only:
+every byte of the path moves inside libnexus.so.
+"""
+
+import torch
+
+from .api import NexusConfig, make_units, new_workspace, nx_evict_batch
+
+
+class StreamingCache:
+    """Ping-pong K/V capacity buffers for `n_layers` layers of one sequence.
+
+    Layout of each buffer: [n_layers, n_kv_heads, capacity, head_dim].
+    `capacity` must hold max(initial tokens, budget + n_append).
+    """
+
+    def __init__(self, cfg: NexusConfig, n_layers, capacity, budget, n_append, walk_iters,
+                 seed=0, seq_id=0, device="cuda"):
+        self.cfg, self.n_layers, self.capacity = cfg, n_layers, capacity
+        self.budget, self.n_append, self.walk_iters = budget, n_append, walk_iters
+        self.seed, self.seq_id, self.device = seed, seq_id, device
+        shape = (n_layers, cfg.n_kv_heads, capacity, cfg.head_dim)
+        self.k = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(2)]
+        self.v = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(2)]
+        self.q = torch.zeros(n_layers, cfg.n_q_heads, cfg.window, cfg.head_dim, dtype=cfg.dtype,
+                             device=device)
+        self.app_k = torch.zeros(n_layers, cfg.n_kv_heads, n_append, cfg.head_dim,
+                                 dtype=cfg.dtype, device=device)
+        self.app_v = torch.zeros_like(self.app_k)
+        self.keep = torch.zeros(n_layers, cfg.n_kv_heads, budget, dtype=torch.int32, device=device)
+        self.ws = new_workspace(cfg, capacity, n_layers, walk_iters, device=device)
+        self.cur = 0          # which buffer holds the live cache
+        self.n_tokens = 0     # live rows per head
+        self.step_no = 0
+        self._units = {}
+
+    def load(self, k, v, n_tokens):
+        """Initial cache: k, v [n_layers, n_kv_heads, n_tokens, head_dim]."""
+        self.k[self.cur][:, :, :n_tokens].copy_(k)
+        self.v[self.cur][:, :, :n_tokens].copy_(v)
+        self.n_tokens = n_tokens
+
+    def _units_for(self, src, n_tokens):
+        key = (src, n_tokens)
+        if key not in self._units:
+            dst = 1 - src
+            rows = self.capacity * self.cfg.head_dim
+            items = [dict(q=self.q[l], k=self.k[src][l], v=self.v[src][l], keep=self.keep[l],
+                          out_k=self.k[dst][l], out_v=self.v[dst][l], app_k=self.app_k[l],
+                          app_v=self.app_v[l], kv_head_stride=rows, out_head_stride=rows,
+                          n_tokens=n_tokens, budget=self.budget, n_append=self.n_append,
+                          layer=l, seq_id=self.seq_id)
+                     for l in range(self.n_layers)]
+            self._units[key] = make_units(items, device=self.device)
+        return self._units[key]
+
+    def step(self):
+        """One eviction event: q, app_k and app_v must hold this event's window
+        queries and the rows that arrive before the next event."""
+        kept = min(self.budget, self.n_tokens)
+        if kept + self.n_append > self.capacity:
+            raise ValueError("capacity too small for budget + n_append")
+        units = self._units_for(self.cur, self.n_tokens)
+        nx_evict_batch(self.cfg, units, self.n_layers, self.n_tokens, self.walk_iters, self.seed,
+                       workspace=self.ws, step=self.step_no, max_out_rows=kept + self.n_append)
+        self.cur = 1 - self.cur
+        self.n_tokens = kept + self.n_append
+        self.step_no += 1
+
+    def live(self):
+        """(k, v) views of the live cache: [n_layers, n_kv_heads, n_tokens, head_dim]."""
+        return self.k[self.cur][:, :, :self.n_tokens], self.v[self.cur][:, :, :self.n_tokens]
+
+    def state(self):
+        """Host copy of everything a resumed stream needs."""
+        k, v = self.live()
+        return {"k": k.cpu(), "v": v.cpu(), "n_tokens": self.n_tokens, "step": self.step_no}
+
+    def restore(self, st):
+        self.cur = 0
+        self.load(st["k"].to(self.device), st["v"].to(self.device), st["n_tokens"])
+        self.step_no = st["step"]

@@ -206,6 +206,30 @@ def gen_layer(wl, *, layer=0, seq=0, n_tokens=None, device="cpu", capacity=None)
             "planted": planted}
 
 
+def gen_model(wl, *, device="cpu", n_tokens=None, seq=0, layers=None, capacity=None):
+    """Every layer of one sequence: q [L, H_q, W, D], k and v [L, H_kv, cap, D].
+
+    Rows N.. of each head (up to `capacity`) are zero.  Drawn layer by layer
+    through fp32 staging buffers, then rounded to the workload dtype.
+    """
+    n = wl.n_tokens if n_tokens is None else n_tokens
+    cap = n if capacity is None else capacity
+    layers = range(wl.n_layers) if layers is None else layers
+    L, dt = len(layers), _torch_dtype(wl)
+    q = torch.empty(L, wl.h_q, wl.window, wl.head_dim, dtype=dt, device=device)
+    k = torch.zeros(L, wl.h_kv, cap, wl.head_dim, dtype=dt, device=device)
+    v = torch.zeros_like(k)
+    q32 = torch.empty(wl.h_q, wl.window, wl.head_dim, device=device)
+    k32 = torch.empty(wl.h_kv, n, wl.head_dim, device=device)
+    v32 = torch.empty_like(k32)
+    for i, layer in enumerate(layers):
+        fill_layer_(wl, q32, k32, v32, layer=layer, seq=seq, n_tokens=n)
+        q[i].copy_(q32)
+        k[i, :, :n].copy_(k32)
+        v[i, :, :n].copy_(v32)
+    return q, k, v
+
+
 def gen_stream_rows(wl, *, layer, step, n_new, device="cpu"):
     """The N(0,1) K and V rows appended at a streaming event: [H_kv, n_new, D] each."""
     g = _gen(device, wl.index, layer, step, 3)
