@@ -136,14 +136,17 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
   return acc;
 }
 
+// Sub-tiles in flight per workgroup: pass 1 runs at 3 workgroups per CU, pass 2
+// (more registers) at 2, so pass 2 keeps more of its own tiles in flight.
+constexpr int kPrefetchStats = 4;
+constexpr int kPrefetchProbs = 4;
+
 // Streams the block's K sub-tiles (32 tokens each) through a two-slot LDS
 // buffer.  Global loads run kPrefetch sub-tiles ahead in a register ring so
 // that several 8-KB tiles per workgroup are in flight while the MFMA and
 // exponential work of the current one proceeds.  body(st, lds) consumes
 // sub-tile st; one barrier per sub-tile.
-constexpr int kPrefetch = 4;
-
-template <typename T, int D, typename Body>
+template <typename T, int D, int kPrefetch, typename Body>
 __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* lds0, char* lds1,
                                    Body&& body) {
   using GE = Geo<T, D>;
@@ -182,7 +185,7 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const int n_mt = a.g.rows_pad / 32;
   const float c = a.c_log2;
-  sweep_tiles<T, D>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
+  sweep_tiles<T, D, kPrefetchStats>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     const bool full = t0 + 32 * st + 32 <= u.n;      // wave-uniform
@@ -329,17 +332,25 @@ __device__ inline void combine_unit(const Args& a, int hu) {
 }
 
 // Pass 2 on one (head unit, tile) item.
+//
+// Every wave owns whole M-tiles (window rows) and all 32 tokens of each
+// sub-tile, so each wave writes its own partial sum of e over its rows for
+// every token (kAParts slots per token; reservoir_keys adds them in fixed
+// order): no cross-wave reduction sits between the tile barriers.  The walk
+// rows live in M-tile 0 (wave 0).  For G = 4 or 8 with G*H <= 32 each walk
+// row covers whole 4-row groups of the MFMA output, so wave 0 forms P_t from
+// in-lane group sums and one half-swap; all 64 lanes then hold every P_t of
+// their token and accumulate the Gram partials without divergence.  Other
+// shapes pass the walk rows through LDS and wave 0 sums them one sub-tile
+// later.
 template <typename T, int D, int MPW>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   char* lds0 = smem;
   char* lds1 = smem + GE::kTileBytes;
-  // per-token partial sums of each wave; raw walk rows (generic path); Gram
-  auto s_tok = reinterpret_cast<float (*)[32][kWaves]>(smem + 2 * GE::kTileBytes);
-  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(
-      smem + 2 * GE::kTileBytes + 2 * 32 * kWaves * sizeof(float));
+  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(smem + 2 * GE::kTileBytes);
   auto s_gram = reinterpret_cast<float (*)[kMaxWalk * kMaxWalk]>(
-      smem + 2 * GE::kTileBytes + (2 * 32 * kWaves + 2 * kMaxWalkRows * 32) * sizeof(float));
+      smem + 2 * GE::kTileBytes + 2 * kMaxWalkRows * 32 * sizeof(float));
   const int tpb = a.g.tok_per_block;
   const int t0 = tile * tpb;
   if (t0 >= u.n) return;
@@ -348,10 +359,6 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   const Geometry& g = a.g;
   const int n_mt = g.rows_pad / 32;
   const float c = a.c_log2;
-  // Walk rows live in M-tile 0 (wave 0) when G*H <= 32.  With G = 4 or 8 each
-  // walk row t covers whole 4-row groups of the MFMA output (rows 4q'..4q'+3,
-  // q' = 2*(v/4) + half), so wave 0 sums them in registers: P_t = S_t (G = 4)
-  // or S_2t + S_2t+1 (G = 8).  Other shapes go through LDS.
   const int gpr = g.group / 4;   // 4-row groups per walk row
   const bool fast_walk = g.walk_rows <= 32 && (gpr == 1 || gpr == 2);
 
@@ -371,49 +378,46 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int t2 = 0; t2 < kMaxWalk; ++t2) gacc[t][t2] = 0.f;
 
-  const Buf a_out(a.a + size_t(hu) * g.max_tokens, uint32_t(g.max_tokens * 4));
+  // This wave's slot of the direct-score partials, and the walk rows.
+  const Buf a_out(a.a + (size_t(hu) * kAParts + wave) * g.max_tokens, uint32_t(g.max_tokens * 4));
   const Buf p_out(a.p + size_t(hu) * g.walk * g.max_tokens, uint32_t(g.walk * g.max_tokens * 4));
   const float wf = float(g.window);
+  const bool has_rows = wave < n_mt;
 
-  // P_t of one token (lanes 0..31 of the walk wave): store and accumulate
-  // the Gram partials (off-diagonal <P_t, P_t'>, diagonal |P_t|_1).
+  // P_t of one token on every lane: store from half 0, accumulate the Gram
+  // partials (off-diagonal <P_t, P_t'>, diagonal |P_t|_1).
   auto walk_out = [&](int tok, const float (&pt)[kMaxWalk]) {
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
       if (t < g.walk) {
-        p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
+        if (hh == 0 && tok < u.n) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
+        if (tok < u.n) {
 #pragma unroll
-        for (int t2 = 0; t2 <= t; ++t2)
-          gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
-      }
-    }
-  };
-
-  // Direct score of sub-tile s, finalised during sub-tile s + 1 by wave s % 4.
-  auto finalize = [&](int s) {
-    if (wave != (s & (kWaves - 1)) || hh != 0) return;
-    const int b = s & 1;
-    const int tok = t0 + 32 * s + nn;
-    if (tok >= u.n) return;
-    const float4 p4 = *reinterpret_cast<const float4*>(&s_tok[b][nn][0]);
-    a_out.stf(uint32_t(tok * 4), ((p4.x + p4.y) + p4.z) + p4.w);
-    if (!fast_walk && g.walk > 0) {
-      float pt[kMaxWalk];
-#pragma unroll
-      for (int t = 0; t < kMaxWalk; ++t) {
-        pt[t] = 0.f;
-        if (t < g.walk) {
-          float sum = 0.f;
-          for (int i = 0; i < g.group; ++i) sum += s_walk[b][t * g.group + i][nn];
-          pt[t] = wf * sum;
+          for (int t2 = 0; t2 <= t; ++t2)
+            gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
         }
       }
-      walk_out(tok, pt);
     }
   };
+  // Generic walk rows of sub-tile s (LDS), summed by wave 0 one sub-tile later.
+  auto walk_generic = [&](int s) {
+    if (wave != 0 || hh != 0) return;
+    const int b = s & 1;
+    float pt[kMaxWalk];
+#pragma unroll
+    for (int t = 0; t < kMaxWalk; ++t) {
+      pt[t] = 0.f;
+      if (t < g.walk) {
+        float sum = 0.f;
+        for (int i = 0; i < g.group; ++i) sum += s_walk[b][t * g.group + i][nn];
+        pt[t] = wf * sum;
+      }
+    }
+    walk_out(t0 + 32 * s + nn, pt);
+  };
 
-  sweep_tiles<T, D>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
-    if (st > 0) finalize(st - 1);
+  sweep_tiles<T, D, kPrefetchProbs>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
+    if (!fast_walk && g.walk > 0 && st > 0) walk_generic(st - 1);
     const int b = st & 1;
     const int tok = t0 + 32 * st + nn;
     uint4 kf[GE::kChunks];
@@ -432,26 +436,25 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
         }
         if (mt == 0 && g.walk > 0) {
           if (fast_walk) {
-            float sg[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sg[q] = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
-            float grp[8];   // group sums S_q' in q' = 2q + half order
+            // Group sums S over rows 8q + 4*half .. +3; after the swap every
+            // lane holds S for q' = 2q (half 0) and q' = 2q + 1 (half 1).
+            float grp[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float other = __shfl_xor(sg[q], 32, 64);
-              grp[2 * q] = hh == 0 ? sg[q] : other;
-              grp[2 * q + 1] = hh == 0 ? other : sg[q];
+              const float sg = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sg),
+                                                               __float_as_uint(sg), false, false);
+              grp[2 * q] = __uint_as_float(sw[0]);
+              grp[2 * q + 1] = __uint_as_float(sw[1]);
             }
-            if (hh == 0 && tok < u.n) {
-              float pt[kMaxWalk];
+            float pt[kMaxWalk];
 #pragma unroll
-              for (int t = 0; t < kMaxWalk; ++t) {
-                const float s1 = grp[t < 8 ? t : 7];
-                const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
-                pt[t] = wf * (gpr == 1 ? s1 : s2);
-              }
-              walk_out(tok, pt);
+            for (int t = 0; t < kMaxWalk; ++t) {
+              const float s1 = grp[t < 8 ? t : 7];
+              const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
+              pt[t] = wf * (gpr == 1 ? s1 : s2);
             }
+            walk_out(tok, pt);
           } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -462,12 +465,15 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
         }
       }
     }
-    tp += __shfl_xor(tp, 32, 64);
-    if (hh == 0) s_tok[b][nn][wave] = tp;
+    // tp over this wave's rows: own half + the other half (same token).
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tp), __float_as_uint(tp),
+                                                     false, false);
+    tp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (has_rows && hh == 0 && tok < u.n) a_out.stf(uint32_t(tok * 4), tp);
   });
-  finalize(n_sub - 1);
+  if (!fast_walk && g.walk > 0) walk_generic(n_sub - 1);
 
-  // Fixed-order Gram reduction: lanes within each wave, then waves 0..3.
+  // Fixed-order Gram reduction: lanes 0..31 of each wave (half 0), then waves.
   if (hh == 0) {
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
@@ -494,7 +500,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 template <typename T, int D>
 constexpr int smem_bytes() {
   return 2 * Geo<T, D>::kTileBytes +
-         int(sizeof(float)) * (2 * 32 * kWaves + 2 * kMaxWalkRows * 32 + kWaves * kMaxWalk * kMaxWalk);
+         int(sizeof(float)) * (2 * kMaxWalkRows * 32 + kWaves * kMaxWalk * kMaxWalk);
 }
 
 // Pass 1: one workgroup per (tile, head unit).
