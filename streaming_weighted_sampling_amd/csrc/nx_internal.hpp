@@ -29,7 +29,6 @@ constexpr int kMinTokPerBlock = 256;   // smallest token range of a score workgr
 constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two)
 constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
-constexpr int kAParts = 4;           // per-wave partial sums of the direct score
 
 enum Stage {
   kStageScoreStats = 0,
@@ -69,7 +68,7 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.status = off; off = align256(off + 256);
   L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
-  L.a = off;      off = align256(off + hu * kAParts * nm * sizeof(float));
+  L.a = off;      off = align256(off + hu * nm * sizeof(float));
   L.p = off;      off = align256(off + hu * size_t(g.walk > 0 ? g.walk : 1) * nm * sizeof(float));
   L.gram = off;   off = align256(off + hu * g.n_t2 * kMaxWalk * kMaxWalk * sizeof(float));
   L.coef = off;   off = align256(off + hu * kMaxWalk * sizeof(float));
@@ -96,7 +95,7 @@ struct Args {
   uint32_t* status;
   float* part1;    // [n_hu][n_t1][rows_pad][2]: (max, sum) in log2 units
   float* beta;     // [n_hu][rows_pad]
-  float* a;        // [n_hu][kAParts][max_tokens]: per-wave partials of the direct score
+  float* a;        // [n_hu][max_tokens]: direct score
   float* p;        // [n_hu][walk][max_tokens]
   float* gram;     // [n_hu][n_t2][kMaxWalk * kMaxWalk]
   float* coef;     // [n_hu][kMaxWalk]: gamma_t / ||C||_1

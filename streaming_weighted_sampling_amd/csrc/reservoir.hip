@@ -91,8 +91,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
   __syncthreads();
 
-  const float* a_in = a.a + size_t(hu) * kAParts * g.max_tokens;
-  const int n_parts = min(g.rows_pad / 32, kAParts);   // waves that own window rows
+  const float* a_in = a.a + size_t(hu) * g.max_tokens;
   const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
   uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
   const size_t ext = size_t(u.h) * u.n;   // row of head h in [h_kv, n] exports
@@ -110,9 +109,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
 #pragma unroll
       for (int t = 0; t < kMaxWalk; ++t)
         if (t < g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * g.max_tokens + j], cj);
-      float aj = a_in[j];
-      for (int w2 = 1; w2 < n_parts; ++w2) aj += a_in[size_t(w2) * g.max_tokens + j];
-      w = aj + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+      w = a_in[j] + a.lambda * cj + a.eps_tie * (float(j) * ramp);
     }
     nonfinite |= !isfinite(w);
     if (a.w_out != nullptr) a.w_out[ext + j] = w;

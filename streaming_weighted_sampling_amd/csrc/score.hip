@@ -136,10 +136,10 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
   return acc;
 }
 
-// Sub-tiles in flight per workgroup: pass 1 runs at 3 workgroups per CU, pass 2
-// (more registers) at 2, so pass 2 keeps more of its own tiles in flight.
+// Sub-tiles in flight per workgroup, sized so that both passes run three
+// workgroups per CU (pass 2 fits 168 VGPRs only with a ring of two).
 constexpr int kPrefetchStats = 4;
-constexpr int kPrefetchProbs = 4;
+constexpr int kPrefetchProbs = 2;
 
 // Streams the block's K sub-tiles (32 tokens each) through a two-slot LDS
 // buffer.  Global loads run kPrefetch sub-tiles ahead in a register ring so
@@ -334,23 +334,32 @@ __device__ inline void combine_unit(const Args& a, int hu) {
 // Pass 2 on one (head unit, tile) item.
 //
 // Every wave owns whole M-tiles (window rows) and all 32 tokens of each
-// sub-tile, so each wave writes its own partial sum of e over its rows for
-// every token (kAParts slots per token; reservoir_keys adds them in fixed
-// order): no cross-wave reduction sits between the tile barriers.  The walk
-// rows live in M-tile 0 (wave 0).  For G = 4 or 8 with G*H <= 32 each walk
-// row covers whole 4-row groups of the MFMA output, so wave 0 forms P_t from
-// in-lane group sums and one half-swap; all 64 lanes then hold every P_t of
-// their token and accumulate the Gram partials without divergence.  Other
-// shapes pass the walk rows through LDS and wave 0 sums them one sub-tile
-// later.
+// sub-tile.  Work that combines values across waves runs one sub-tile late,
+// from LDS, in the shadow of the next sub-tile's MFMA and exponentials, so
+// the one barrier per sub-tile of the K sweep is the only synchronisation:
+//   * each wave leaves its partial of a_j for the sub-tile's 32 tokens in LDS;
+//     one half-wave adds the partials in wave order and stores a_j;
+//   * the walk rows live in M-tile 0 (wave 0).  For G = 4 or 8 with
+//     G*H <= 32 each walk row covers whole 4-row groups of the MFMA output,
+//     so wave 0 forms P_t in registers from in-lane group sums and one
+//     half-swap; other shapes leave the e values in LDS and wave 0 sums them
+//     one sub-tile later.  Either way P_t goes to global memory and to LDS;
+//   * the Gram partials <P_t, P_t'> (diagonal |P_t|_1) accumulate one (or,
+//     for the generic walk, two) sub-tiles late: half-wave k owns the pairs
+//     p = 7 - k, 15 - k, ..., (p = t(t+1)/2 + t') at one token per lane, so
+//     no lane holds more than five accumulators.
 template <typename T, int D, int MPW>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
+  constexpr int kPairs = kMaxWalk * (kMaxWalk + 1) / 2;
+  constexpr int kHalfWaves = 2 * kWaves;
+  constexpr int kPairsPerLane = (kPairs + kHalfWaves - 1) / kHalfWaves;
   char* lds0 = smem;
   char* lds1 = smem + GE::kTileBytes;
-  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(smem + 2 * GE::kTileBytes);
-  auto s_gram = reinterpret_cast<float (*)[kMaxWalk * kMaxWalk]>(
-      smem + 2 * GE::kTileBytes + 2 * kMaxWalkRows * 32 * sizeof(float));
+  char* extra = smem + 2 * GE::kTileBytes;
+  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(extra);
+  auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(extra + 2 * kMaxWalkRows * 32 * 4);
+  auto s_a = reinterpret_cast<float (*)[kWaves][32]>(extra + 2 * (kMaxWalkRows + kMaxWalk) * 32 * 4);
   const int tpb = a.g.tok_per_block;
   const int t0 = tile * tpb;
   if (t0 >= u.n) return;
@@ -358,9 +367,13 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const Geometry& g = a.g;
   const int n_mt = g.rows_pad / 32;
+  const int row_waves = min(n_mt, kWaves);
   const float c = a.c_log2;
   const int gpr = g.group / 4;   // 4-row groups per walk row
+  const bool walk = g.walk > 0;
   const bool fast_walk = g.walk_rows <= 32 && (gpr == 1 || gpr == 2);
+  const int n_pairs = g.walk * (g.walk + 1) / 2;
+  const int pg = kHalfWaves - 1 - (threadIdx.x >> 5);   // first Gram pair of this half-wave
 
   uint4 qf[MPW][GE::kChunks];
   load_q<T, D, MPW>(a, u, wave, nn, hh, qf);
@@ -372,54 +385,85 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     for (int v = 0; v < 16; ++v)
       bt[i][v] = mt < n_mt ? a.beta[size_t(hu) * g.rows_pad + mt * 32 + out_row(v, hh)] : INFINITY;
   }
-  float gacc[kMaxWalk][kMaxWalk];
+  // This lane's Gram pairs (t, t'), 3 bits each, packed 6 bits per pair.
+  uint32_t pairs = 0;
+  float gacc[kPairsPerLane];
 #pragma unroll
-  for (int t = 0; t < kMaxWalk; ++t)
-#pragma unroll
-    for (int t2 = 0; t2 < kMaxWalk; ++t2) gacc[t][t2] = 0.f;
+  for (int k = 0; k < kPairsPerLane; ++k) {
+    const int p = pg + kHalfWaves * k;
+    int t = 0;
+    while ((t + 1) * (t + 2) / 2 <= p) ++t;
+    const int t2 = p - t * (t + 1) / 2;
+    pairs |= uint32_t(((t & 7) << 3) | (t2 & 7)) << (6 * k);
+    gacc[k] = 0.f;
+  }
 
-  // This wave's slot of the direct-score partials, and the walk rows.
-  const Buf a_out(a.a + (size_t(hu) * kAParts + wave) * g.max_tokens, uint32_t(g.max_tokens * 4));
+  const Buf a_out(a.a + size_t(hu) * g.max_tokens, uint32_t(g.max_tokens * 4));
   const Buf p_out(a.p + size_t(hu) * g.walk * g.max_tokens, uint32_t(g.walk * g.max_tokens * 4));
   const float wf = float(g.window);
-  const bool has_rows = wave < n_mt;
 
-  // P_t of one token on every lane: store from half 0, accumulate the Gram
-  // partials (off-diagonal <P_t, P_t'>, diagonal |P_t|_1).
-  auto walk_out = [&](int tok, const float (&pt)[kMaxWalk]) {
+  // P_t of token t0 + 32 s + nn (lanes of half 0): global and LDS; tokens past
+  // the cache end enter the Gram as zero.
+  auto put_walk = [&](int s, const float (&pt)[kMaxWalk]) {
+    const int tok = t0 + 32 * s + nn;
+    const bool ok = tok < u.n;
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
       if (t < g.walk) {
-        if (hh == 0 && tok < u.n) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
-        if (tok < u.n) {
-#pragma unroll
-          for (int t2 = 0; t2 <= t; ++t2)
-            gacc[t][t2] = fmaf(pt[t], t2 == t ? 1.f : pt[t2], gacc[t][t2]);
-        }
+        if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
+        s_pt[s & 1][t][nn] = ok ? pt[t] : 0.f;
       }
     }
   };
-  // Generic walk rows of sub-tile s (LDS), summed by wave 0 one sub-tile later.
+  // Generic walk rows of sub-tile s from LDS (wave 0, half 0).
   auto walk_generic = [&](int s) {
     if (wave != 0 || hh != 0) return;
-    const int b = s & 1;
     float pt[kMaxWalk];
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t) {
       pt[t] = 0.f;
       if (t < g.walk) {
         float sum = 0.f;
-        for (int i = 0; i < g.group; ++i) sum += s_walk[b][t * g.group + i][nn];
+        for (int i = 0; i < g.group; ++i) sum += s_walk[s & 1][t * g.group + i][nn];
         pt[t] = wf * sum;
       }
     }
-    walk_out(t0 + 32 * s + nn, pt);
+    put_walk(s, pt);
+  };
+  auto gram_step = [&](int s) {
+    const float* sp = &s_pt[s & 1][0][nn];
+#pragma unroll
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      if (pg + kHalfWaves * k < n_pairs) {
+        const uint32_t t = (pairs >> (6 * k + 3)) & 7, t2 = (pairs >> (6 * k)) & 7;
+        const float x = sp[32 * t];
+        const float y = t2 == t ? 1.f : sp[32 * t2];
+        gacc[k] = fmaf(x, y, gacc[k]);
+      }
+    }
+  };
+  // a_j of sub-tile s: wave-ordered sum of the partials (wave 1, half 0).
+  auto a_final = [&](int s) {
+    if (threadIdx.x < 64 || threadIdx.x >= 96) return;
+    const int tok = t0 + 32 * s + nn;
+    float sum = s_a[s & 1][0][nn];
+    for (int w = 1; w < row_waves; ++w) sum += s_a[s & 1][w][nn];
+    if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
   };
 
   sweep_tiles<T, D, kPrefetchProbs>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
-    if (!fast_walk && g.walk > 0 && st > 0) walk_generic(st - 1);
-    const int b = st & 1;
-    const int tok = t0 + 32 * st + nn;
+    // Lagged work on slots the previous barrier made visible.
+    if (st > 0) {
+      a_final(st - 1);
+      if (walk) {
+        if (fast_walk) {
+          gram_step(st - 1);
+        } else {
+          walk_generic(st - 1);
+          if (st > 1) gram_step(st - 2);
+        }
+      }
+    }
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     float tp = 0.f;
@@ -434,7 +478,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
           e[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
           tp += e[v];
         }
-        if (mt == 0 && g.walk > 0) {
+        if (mt == 0 && walk) {
           if (fast_walk) {
             // Group sums S over rows 8q + 4*half .. +3; after the swap every
             // lane holds S for q' = 2q (half 0) and q' = 2q + 1 (half 1).
@@ -447,19 +491,21 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
               grp[2 * q] = __uint_as_float(sw[0]);
               grp[2 * q + 1] = __uint_as_float(sw[1]);
             }
-            float pt[kMaxWalk];
+            if (hh == 0) {
+              float pt[kMaxWalk];
 #pragma unroll
-            for (int t = 0; t < kMaxWalk; ++t) {
-              const float s1 = grp[t < 8 ? t : 7];
-              const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
-              pt[t] = wf * (gpr == 1 ? s1 : s2);
+              for (int t = 0; t < kMaxWalk; ++t) {
+                const float s1 = grp[t < 8 ? t : 7];
+                const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
+                pt[t] = wf * (gpr == 1 ? s1 : s2);
+              }
+              put_walk(st, pt);
             }
-            walk_out(tok, pt);
           } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int rho = out_row(v, hh);
-              if (rho < g.walk_rows) s_walk[b][rho][nn] = e[v];
+              if (rho < g.walk_rows) s_walk[st & 1][rho][nn] = e[v];
             }
           }
         }
@@ -469,38 +515,39 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tp), __float_as_uint(tp),
                                                      false, false);
     tp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (has_rows && hh == 0 && tok < u.n) a_out.stf(uint32_t(tok * 4), tp);
+    if (wave < row_waves && hh == 0) s_a[st & 1][wave][nn] = tp;
   });
-  if (!fast_walk && g.walk > 0) walk_generic(n_sub - 1);
-
-  // Fixed-order Gram reduction: lanes 0..31 of each wave (half 0), then waves.
-  if (hh == 0) {
+  // Drain the lagged work (the sweep ends on a barrier).
+  a_final(n_sub - 1);
+  if (walk) {
+    if (fast_walk) {
+      gram_step(n_sub - 1);
+    } else {
+      if (n_sub > 1) gram_step(n_sub - 2);
+      walk_generic(n_sub - 1);
+      __syncthreads();
+      gram_step(n_sub - 1);
+    }
+    // Each pair is owned by one half-wave: sum its 32 lanes in a fixed order.
+    float* gout = a.gram + (size_t(hu) * g.n_t2 + tile) * (kMaxWalk * kMaxWalk);
 #pragma unroll
-    for (int t = 0; t < kMaxWalk; ++t) {
-#pragma unroll
-      for (int t2 = 0; t2 <= t; ++t2) {
-        if (t < g.walk) {
-          const float sum = half_sum(gacc[t][t2]);
-          if (nn == 0) s_gram[wave][t * kMaxWalk + t2] = sum;
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      const int p = pg + kHalfWaves * k;
+      if (p < n_pairs) {
+        const float sum = half_sum(gacc[k]);
+        if (nn == 0) {
+          int t = 0;
+          while ((t + 1) * (t + 2) / 2 <= p) ++t;
+          gout[t * kMaxWalk + (p - t * (t + 1) / 2)] = sum;
         }
       }
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < kMaxWalk * kMaxWalk) {
-    const int t = threadIdx.x / kMaxWalk, t2 = threadIdx.x % kMaxWalk;
-    if (t < g.walk && t2 <= t) {
-      float* gout = a.gram + (size_t(hu) * g.n_t2 + tile) * (kMaxWalk * kMaxWalk);
-      gout[threadIdx.x] = ((s_gram[0][threadIdx.x] + s_gram[1][threadIdx.x]) + s_gram[2][threadIdx.x]) +
-                          s_gram[3][threadIdx.x];
     }
   }
 }
 
 template <typename T, int D>
 constexpr int smem_bytes() {
-  return 2 * Geo<T, D>::kTileBytes +
-         int(sizeof(float)) * (2 * kMaxWalkRows * 32 + kWaves * kMaxWalk * kMaxWalk);
+  return 2 * Geo<T, D>::kTileBytes + int(sizeof(float)) * 2 * 32 * (kMaxWalkRows + kMaxWalk + kWaves);
 }
 
 // Pass 1: one workgroup per (tile, head unit).
