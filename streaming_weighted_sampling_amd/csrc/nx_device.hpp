@@ -39,6 +39,46 @@ struct Buf {
   }
 };
 
+// Global -> LDS copies that bypass the VGPRs (buffer_load_dwordx4 with the lds
+// modifier): lane l of the wavefront writes its 16 bytes to LDS address
+// M0 + 16 * l, so one instruction fills 1 KB of LDS.  Issued through inline
+// assembly so that the compiler does not order every later LDS read behind
+// all such copies; the caller waits with vm_wait<>() and a barrier.  Offsets
+// at or past `bytes` read as zero.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+struct LdsDma {
+  i32x4_t r;
+  __device__ LdsDma(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    r = i32x4_t{__builtin_amdgcn_readfirstlane(int(uint32_t(b))),
+                __builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32) & 0xFFFF)),
+                __builtin_amdgcn_readfirstlane(int(bytes)), kRsrcWord3};
+  }
+  // lds_addr: wave-uniform LDS byte address of this wavefront's 1 KB block.
+  __device__ void load16(uint32_t lds_addr, uint32_t voff) const {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+};
+
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_address(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ inline void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // One KV head of one (sequence, layer) item, resolved on the device.
 struct HeadUnit {
   const char* q;       // first query row of the GQA group (query head h * G)

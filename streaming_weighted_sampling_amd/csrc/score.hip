@@ -43,10 +43,18 @@ struct Geo {
   static constexpr int kRowBytes = D * int(sizeof(T));
   static constexpr int kHalfBytes = kRowBytes / 2;
   static constexpr int kChunks = kHalfBytes / 16;              // 16-B chunks per lane
-  static constexpr int kPitch = kRowBytes + 16;                // LDS row pitch, bytes
-  static constexpr int kTileBytes = 32 * kPitch;
-  static constexpr int kLoads = (32 * kRowBytes / 16) / kThreads;
-  static_assert(kLoads >= 1, "tile smaller than one 16-B load per thread");
+  static constexpr int kCpr = kRowBytes / 16;                  // 16-B chunks per row
+  static constexpr int kTileBytes = 32 * kRowBytes;            // one sub-tile, no padding
+  static_assert(kCpr == 8 || kCpr == 16 || kCpr == 32, "row of 128, 256 or 512 bytes");
+  // LDS holds chunk s of row r at slot s ^ swz(r): the 16 rows that a
+  // ds_read_b128 serves together then fall in 16 different 16-B bank groups.
+  __device__ static int swz(int row) { return kCpr == 8 ? (row >> 1) & 7 : row & 15; }
+  // Ring slots: LDS for the K sub-tiles in flight (pass 1 at four
+  // workgroups per CU, pass 2 at three next to its walk buffers; 160 KB of
+  // LDS per CU).
+  static constexpr int kSlotsStats = kTileBytes <= 4096 ? 8 : (39 * 1024) / kTileBytes;
+  static constexpr int kSlotsProbs = kTileBytes <= 4096 ? 8 : (32 * 1024) / kTileBytes;
+  static_assert(kSlotsStats >= 2 && kSlotsProbs >= 2, "ring needs two slots");
 };
 
 __device__ inline int out_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
@@ -85,34 +93,14 @@ __device__ inline void load_q(const Args& a, const HeadUnit& u, int wave, int nn
   }
 }
 
-// Sub-tile `st` of the block (32 tokens) into registers; kb covers exactly the
-// block's valid tokens, so rows past the cache end read as zero.
-template <typename T, int D>
-__device__ inline void load_tile_regs(const Buf& kb, int st, uint4 (&r)[Geo<T, D>::kLoads]) {
-  using GE = Geo<T, D>;
-#pragma unroll
-  for (int i = 0; i < GE::kLoads; ++i)
-    r[i] = kb.ld16(uint32_t(st * 32 * GE::kRowBytes + 16 * (threadIdx.x + kThreads * i)));
-}
-
-template <typename T, int D>
-__device__ inline void store_tile_lds(char* lds, const uint4 (&r)[Geo<T, D>::kLoads]) {
-  using GE = Geo<T, D>;
-  constexpr int kPerRow = GE::kRowBytes / 16;
-#pragma unroll
-  for (int i = 0; i < GE::kLoads; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int row = c / kPerRow, col = c - row * kPerRow;
-    *reinterpret_cast<uint4*>(lds + row * GE::kPitch + 16 * col) = r[i];
-  }
-}
-
 template <typename T, int D>
 __device__ inline void read_frag(const char* lds, int nn, int hh, uint4 (&kf)[Geo<T, D>::kChunks]) {
   using GE = Geo<T, D>;
-  const char* p = lds + nn * GE::kPitch + hh * GE::kHalfBytes;
+  const char* p = lds + nn * GE::kRowBytes;
+  const int x = GE::swz(nn);
 #pragma unroll
-  for (int c = 0; c < GE::kChunks; ++c) kf[c] = *reinterpret_cast<const uint4*>(p + 16 * c);
+  for (int c = 0; c < GE::kChunks; ++c)
+    kf[c] = *reinterpret_cast<const uint4*>(p + (((hh * GE::kChunks + c) ^ x) << 4));
 }
 
 // Raw dot products of 32 query rows with 32 tokens (no scaling).
@@ -136,41 +124,65 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
   return acc;
 }
 
-// Sub-tiles in flight per workgroup, sized so that both passes run three
-// workgroups per CU (pass 2 fits 168 VGPRs only with a ring of two).
-constexpr int kPrefetchStats = 4;
-constexpr int kPrefetchProbs = 2;
-
-// Streams the block's K sub-tiles (32 tokens each) through a two-slot LDS
-// buffer.  Global loads run kPrefetch sub-tiles ahead in a register ring so
-// that several 8-KB tiles per workgroup are in flight while the MFMA and
-// exponential work of the current one proceeds.  body(st, lds) consumes
-// sub-tile st; one barrier per sub-tile.
-template <typename T, int D, int kPrefetch, typename Body>
-__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* lds0, char* lds1,
+// Streams the block's K sub-tiles (32 tokens each) through a ring of kSlots
+// LDS slots filled by global -> LDS copies, kSlots - 1 sub-tiles ahead of the
+// one being consumed, without holding them in registers.  The copies are
+// issued by the wavefronts of the last kLoaders roles only (role: a
+// permutation of the wavefront index): every vector-memory operation
+// of a wavefront counts against the one vmcnt, so a wavefront that also
+// stores to global memory would, when it waits for its copies, wait for its
+// stores as well.  Per sub-tile: the loaders wait for their copies of it, one
+// barrier (everyone's copies landed, everyone is done with the slot about to
+// be refilled), refill, body(st, lds).  Rows past the cache end read as zero.
+// Ends on a barrier.
+template <typename T, int D, int kSlots, int kLoaders, typename Body>
+__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role,
                                    Body&& body) {
   using GE = Geo<T, D>;
+  constexpr int kPerWave = GE::kTileBytes / (1024 * kLoaders);   // copies per loader per tile
+  static_assert(kPerWave >= 1 && kPerWave * 1024 * kLoaders == GE::kTileBytes, "tile split");
+  static_assert((kSlots - 2) * kPerWave < 64, "vmcnt range");
   const int t1 = min(t0 + 32 * n_sub, u.n);
-  const Buf kb(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
-  uint4 ring[kPrefetch][GE::kLoads];
+  const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
+  const int lw = role - (kWaves - kLoaders);   // loader index, < 0: not a loader
+  const bool loader = lw >= 0;
+  const int lane = threadIdx.x & 63;
+  // Copy i of loader lw fills LDS chunk (i * kLoaders + lw) * 64 + lane.
+  uint32_t voff[kPerWave];
 #pragma unroll
-  for (int r = 0; r < kPrefetch; ++r)
-    if (r < n_sub) load_tile_regs<T, D>(kb, r, ring[r]);
-  store_tile_lds<T, D>(lds0, ring[0]);
-  __syncthreads();
-  for (int st0 = 0; st0 < n_sub; st0 += kPrefetch) {
-#pragma unroll
-    for (int r = 0; r < kPrefetch; ++r) {
-      const int st = st0 + r;
-      if (st < n_sub) {
-        // ring[r] held sub-tile st, already copied to LDS: refill it.
-        if (st + kPrefetch < n_sub) load_tile_regs<T, D>(kb, st + kPrefetch, ring[r]);
-        body(st, (st & 1) ? lds1 : lds0);
-        if (st + 1 < n_sub) store_tile_lds<T, D>((st & 1) ? lds0 : lds1, ring[(r + 1) % kPrefetch]);
-        __syncthreads();
-      }
-    }
+  for (int i = 0; i < kPerWave; ++i) {
+    const int lc = (i * kLoaders + lw) * 64 + lane;
+    const int row = lc / GE::kCpr, slot = lc % GE::kCpr;
+    voff[i] = uint32_t(row * GE::kRowBytes + ((slot ^ GE::swz(row)) << 4));
   }
+  const uint32_t ring_lds = lds_address(ring) + uint32_t(lw * 1024);
+  auto issue = [&](int st) {
+    if (!loader) return;
+    const uint32_t dst = ring_lds + uint32_t((st % kSlots) * GE::kTileBytes);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      dma.load16(dst + uint32_t(i * kLoaders * 1024), voff[i] + uint32_t(st * GE::kTileBytes));
+  };
+#pragma unroll
+  for (int r = 0; r < kSlots - 1; ++r)
+    if (r < n_sub) issue(r);
+  // The caller's own loads (query fragments, row offsets) were issued before
+  // the ring: let them and the prologue land together, once.  Otherwise the
+  // compiler, which does not see the ring copies, would place a full vmcnt(0)
+  // in front of the first use of those registers inside the loop.
+  vm_wait<0>();
+  for (int st = 0; st < n_sub; ++st) {
+    if (loader) {
+      if (st + kSlots - 2 < n_sub)
+        vm_wait<(kSlots - 2) * kPerWave>();
+      else
+        vm_wait<0>();
+    }
+    __syncthreads();
+    if (st + kSlots - 1 < n_sub) issue(st + kSlots - 1);
+    body(st, ring + (st % kSlots) * GE::kTileBytes);
+  }
+  __syncthreads();
 }
 
 // Pass 1 over the block's tokens.  kExact = false keeps one shift per row (the
@@ -180,12 +192,12 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* l
 template <typename T, int D, int MPW, bool kExact>
 __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int n_sub,
                                    const uint4 (&qf)[MPW][Geo<T, D>::kChunks],
-                                   float (&my)[MPW][16], float (&z)[MPW][16], char* lds0, char* lds1) {
+                                   float (&my)[MPW][16], float (&z)[MPW][16], char* ring) {
   using GE = Geo<T, D>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const int n_mt = a.g.rows_pad / 32;
   const float c = a.c_log2;
-  sweep_tiles<T, D, kPrefetchStats>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
+  sweep_tiles<T, D, GE::kSlotsStats, kWaves>(u, t0, n_sub, ring, wave, [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     const bool full = t0 + 32 * st + 32 <= u.n;      // wave-uniform
@@ -230,8 +242,6 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
 template <typename T, int D, int MPW>
 __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
-  char* lds0 = smem;
-  char* lds1 = smem + GE::kTileBytes;
   const int tpb = a.g.tok_per_block;
   const int t0 = tile * tpb;
   if (t0 >= u.n) return;
@@ -246,7 +256,7 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
   for (int i = 0; i < MPW; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) { my[i][v] = 0.f; z[i][v] = 0.f; }
-  stats_sweep<T, D, MPW, false>(a, u, t0, n_sub, qf, my, z, lds0, lds1);
+  stats_sweep<T, D, MPW, false>(a, u, t0, n_sub, qf, my, z, smem);
 
   // Merge the 32 lanes of each half (they share rows); detect overflow.
   float zr[MPW][16];
@@ -264,7 +274,7 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
     for (int i = 0; i < MPW; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) { my[i][v] = -INFINITY; z[i][v] = 0.f; }
-    stats_sweep<T, D, MPW, true>(a, u, t0, n_sub, qf, my, z, lds0, lds1);
+    stats_sweep<T, D, MPW, true>(a, u, t0, n_sub, qf, my, z, smem);
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
 #pragma unroll
@@ -331,56 +341,72 @@ __device__ inline void combine_unit(const Args& a, int hu) {
   }
 }
 
+// Walk modes of pass 2 (template parameter, chosen on the host).
+constexpr int kWalkNone = 0;    // H = 0
+constexpr int kWalkFast4 = 1;   // G = 4, G*H <= 32: P_t from register group sums
+constexpr int kWalkFast8 = 2;   // G = 8, G*H <= 32
+constexpr int kWalkLds = 3;     // any other shape: walk rows through LDS
+
 // Pass 2 on one (head unit, tile) item.
 //
 // Every wave owns whole M-tiles (window rows) and all 32 tokens of each
 // sub-tile.  Work that combines values across waves runs one sub-tile late,
 // from LDS, in the shadow of the next sub-tile's MFMA and exponentials, so
-// the one barrier per sub-tile of the K sweep is the only synchronisation:
-//   * each wave leaves its partial of a_j for the sub-tile's 32 tokens in LDS;
-//     one half-wave adds the partials in wave order and stores a_j;
-//   * the walk rows live in M-tile 0 (wave 0).  For G = 4 or 8 with
+// the one barrier per sub-tile of the K sweep is the only synchronisation.
+// Roles are numbered r = (wave + blockIdx.x + blockIdx.y) mod 4, so that the
+// extra work of roles 0 and 1 does not always land on the same SIMDs:
+//   * role r owns M-tiles r, r + 4, ...; it leaves its partial of a_j for the
+//     sub-tile's 32 tokens in LDS, and half 0 of role 1 adds the partials in
+//     role (= M-tile) order and stores a_j;
+//   * the walk rows live in M-tile 0 (role 0).  For G = 4 or 8 with
 //     G*H <= 32 each walk row covers whole 4-row groups of the MFMA output,
-//     so wave 0 forms P_t in registers from in-lane group sums and one
-//     half-swap; other shapes leave the e values in LDS and wave 0 sums them
-//     one sub-tile later.  Either way P_t goes to global memory and to LDS;
+//     so role 0 forms P_t in registers from in-lane group sums and one
+//     half-swap; other shapes leave the e values in LDS and role 0 sums them
+//     one sub-tile later.  Either way P_t goes to global memory and to LDS.
+//     Roles 0 and 1 issue every global store of the pass and roles 2 and 3
+//     every K copy, so that no ring wait also waits for stores;
 //   * the Gram partials <P_t, P_t'> (diagonal |P_t|_1) accumulate one (or,
-//     for the generic walk, two) sub-tiles late: half-wave k owns the pairs
-//     p = 7 - k, 15 - k, ..., (p = t(t+1)/2 + t') at one token per lane, so
-//     no lane holds more than five accumulators.
-template <typename T, int D, int MPW>
+//     for the LDS walk, two) sub-tiles late: half-wave k = 2r + half owns the
+//     pairs p = 7 - k, 15 - k, ... (p = t(t+1)/2 + t') at one token per lane.
+// Every sum runs in a fixed order, whatever the roles.
+template <typename T, int D, int kWalk>
+constexpr int probs_smem_bytes() {
+  return Geo<T, D>::kSlotsProbs * Geo<T, D>::kTileBytes +
+         int(sizeof(float)) * 2 * 32 * ((kWalk == kWalkLds ? kMaxWalkRows : 0) + kMaxWalk + kWaves);
+}
+
+template <typename T, int D, int MPW, int kWalk>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
-  constexpr int kPairs = kMaxWalk * (kMaxWalk + 1) / 2;
+  constexpr bool kHasWalk = kWalk != kWalkNone;
+  constexpr int kMaxT = kWalk == kWalkFast8 ? 4 : kMaxWalk;   // deepest walk of this mode
   constexpr int kHalfWaves = 2 * kWaves;
-  constexpr int kPairsPerLane = (kPairs + kHalfWaves - 1) / kHalfWaves;
-  char* lds0 = smem;
-  char* lds1 = smem + GE::kTileBytes;
-  char* extra = smem + 2 * GE::kTileBytes;
-  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(extra);
-  auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(extra + 2 * kMaxWalkRows * 32 * 4);
-  auto s_a = reinterpret_cast<float (*)[kWaves][32]>(extra + 2 * (kMaxWalkRows + kMaxWalk) * 32 * 4);
+  constexpr int kPairsPerLane = (kMaxT * (kMaxT + 1) / 2 + kHalfWaves - 1) / kHalfWaves;
+  auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(smem + GE::kSlotsProbs * GE::kTileBytes);
+  auto s_a = reinterpret_cast<float (*)[kWaves][32]>(smem + GE::kSlotsProbs * GE::kTileBytes +
+                                                     2 * kMaxWalk * 32 * 4);
+  auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(
+      smem + GE::kSlotsProbs * GE::kTileBytes + 2 * (kMaxWalk + kWaves) * 32 * 4);
   const int tpb = a.g.tok_per_block;
   const int t0 = tile * tpb;
   if (t0 >= u.n) return;
   const int n_sub = (min(t0 + tpb, u.n) - t0 + 31) / 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
+  const int lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
+  const int role = ((threadIdx.x >> 6) + blockIdx.x + blockIdx.y) & (kWaves - 1);
   const Geometry& g = a.g;
   const int n_mt = g.rows_pad / 32;
-  const int row_waves = min(n_mt, kWaves);
+  const int row_roles = min(n_mt, kWaves);
   const float c = a.c_log2;
-  const int gpr = g.group / 4;   // 4-row groups per walk row
-  const bool walk = g.walk > 0;
-  const bool fast_walk = g.walk_rows <= 32 && (gpr == 1 || gpr == 2);
-  const int n_pairs = g.walk * (g.walk + 1) / 2;
-  const int pg = kHalfWaves - 1 - (threadIdx.x >> 5);   // first Gram pair of this half-wave
+  const int walk = min(g.walk, kMaxT);          // == g.walk for the mode the host picked
+  const int n_pairs = walk * (walk + 1) / 2;
+  const int pg = kHalfWaves - 1 - (2 * role + hh);   // first Gram pair of this half-wave
 
   uint4 qf[MPW][GE::kChunks];
-  load_q<T, D, MPW>(a, u, wave, nn, hh, qf);
+  load_q<T, D, MPW>(a, u, role, nn, hh, qf);
   float bt[MPW][16];
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
-    const int mt = wave + kWaves * i;
+    const int mt = role + kWaves * i;
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       bt[i][v] = mt < n_mt ? a.beta[size_t(hu) * g.rows_pad + mt * 32 + out_row(v, hh)] : INFINITY;
@@ -404,25 +430,25 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 
   // P_t of token t0 + 32 s + nn (lanes of half 0): global and LDS; tokens past
   // the cache end enter the Gram as zero.
-  auto put_walk = [&](int s, const float (&pt)[kMaxWalk]) {
+  auto put_walk = [&](int s, const float (&pt)[kMaxT]) {
     const int tok = t0 + 32 * s + nn;
     const bool ok = tok < u.n;
 #pragma unroll
-    for (int t = 0; t < kMaxWalk; ++t) {
-      if (t < g.walk) {
+    for (int t = 0; t < kMaxT; ++t) {
+      if (t < walk) {
         if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
         s_pt[s & 1][t][nn] = ok ? pt[t] : 0.f;
       }
     }
   };
-  // Generic walk rows of sub-tile s from LDS (wave 0, half 0).
-  auto walk_generic = [&](int s) {
-    if (wave != 0 || hh != 0) return;
-    float pt[kMaxWalk];
+  // LDS walk rows of sub-tile s (role 0, half 0).
+  auto walk_lds = [&](int s) {
+    if (role != 0 || hh != 0) return;
+    float pt[kMaxT];
 #pragma unroll
-    for (int t = 0; t < kMaxWalk; ++t) {
+    for (int t = 0; t < kMaxT; ++t) {
       pt[t] = 0.f;
-      if (t < g.walk) {
+      if (t < walk) {
         float sum = 0.f;
         for (int i = 0; i < g.group; ++i) sum += s_walk[s & 1][t * g.group + i][nn];
         pt[t] = wf * sum;
@@ -442,26 +468,26 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       }
     }
   };
-  // a_j of sub-tile s: wave-ordered sum of the partials (wave 1, half 0).
+  // a_j of sub-tile s: M-tile-ordered sum of the partials (role 1, half 0).
   auto a_final = [&](int s) {
-    if (threadIdx.x < 64 || threadIdx.x >= 96) return;
+    if (role != 1 || hh != 0) return;
     const int tok = t0 + 32 * s + nn;
     float sum = s_a[s & 1][0][nn];
-    for (int w = 1; w < row_waves; ++w) sum += s_a[s & 1][w][nn];
+#pragma unroll
+    for (int r = 1; r < kWaves; ++r)
+      if (r < row_roles) sum += s_a[s & 1][r][nn];
     if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
   };
 
-  sweep_tiles<T, D, kPrefetchProbs>(u, t0, n_sub, lds0, lds1, [&](int st, const char* cur) {
+  sweep_tiles<T, D, GE::kSlotsProbs, 2>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
     // Lagged work on slots the previous barrier made visible.
     if (st > 0) {
       a_final(st - 1);
-      if (walk) {
-        if (fast_walk) {
-          gram_step(st - 1);
-        } else {
-          walk_generic(st - 1);
-          if (st > 1) gram_step(st - 2);
-        }
+      if constexpr (kWalk == kWalkFast4 || kWalk == kWalkFast8) {
+        gram_step(st - 1);
+      } else if constexpr (kWalk == kWalkLds) {
+        walk_lds(st - 1);
+        if (st > 1) gram_step(st - 2);
       }
     }
     uint4 kf[GE::kChunks];
@@ -469,7 +495,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     float tp = 0.f;
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-      const int mt = wave + kWaves * i;
+      const int mt = role + kWaves * i;
       if (mt < n_mt) {
         const floatx16_t acc = mfma_tile<T, D>(qf[i], kf);
         float e[16];
@@ -478,8 +504,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
           e[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
           tp += e[v];
         }
-        if (mt == 0 && walk) {
-          if (fast_walk) {
+        if constexpr (kWalk == kWalkFast4 || kWalk == kWalkFast8) {
+          if (i == 0 && role == 0) {
             // Group sums S over rows 8q + 4*half .. +3; after the swap every
             // lane holds S for q' = 2q (half 0) and q' = 2q + 1 (half 1).
             float grp[8];
@@ -492,16 +518,15 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
               grp[2 * q + 1] = __uint_as_float(sw[1]);
             }
             if (hh == 0) {
-              float pt[kMaxWalk];
+              float pt[kMaxT];
 #pragma unroll
-              for (int t = 0; t < kMaxWalk; ++t) {
-                const float s1 = grp[t < 8 ? t : 7];
-                const float s2 = (2 * t + 1 < 8) ? grp[2 * t] + grp[2 * t + 1] : 0.f;
-                pt[t] = wf * (gpr == 1 ? s1 : s2);
-              }
+              for (int t = 0; t < kMaxT; ++t)
+                pt[t] = wf * (kWalk == kWalkFast4 ? grp[t] : grp[2 * t] + grp[2 * t + 1]);
               put_walk(st, pt);
             }
-          } else {
+          }
+        } else if constexpr (kWalk == kWalkLds) {
+          if (i == 0 && role == 0) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
               const int rho = out_row(v, hh);
@@ -515,19 +540,17 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tp), __float_as_uint(tp),
                                                      false, false);
     tp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (wave < row_waves && hh == 0) s_a[st & 1][wave][nn] = tp;
+    if (role < row_roles && hh == 0) s_a[st & 1][role][nn] = tp;
   });
   // Drain the lagged work (the sweep ends on a barrier).
   a_final(n_sub - 1);
-  if (walk) {
-    if (fast_walk) {
-      gram_step(n_sub - 1);
-    } else {
+  if constexpr (kHasWalk) {
+    if constexpr (kWalk == kWalkLds) {
       if (n_sub > 1) gram_step(n_sub - 2);
-      walk_generic(n_sub - 1);
+      walk_lds(n_sub - 1);
       __syncthreads();
-      gram_step(n_sub - 1);
     }
+    gram_step(n_sub - 1);
     // Each pair is owned by one half-wave: sum its 32 lanes in a fixed order.
     float* gout = a.gram + (size_t(hu) * g.n_t2 + tile) * (kMaxWalk * kMaxWalk);
 #pragma unroll
@@ -545,15 +568,10 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   }
 }
 
-template <typename T, int D>
-constexpr int smem_bytes() {
-  return 2 * Geo<T, D>::kTileBytes + int(sizeof(float)) * 2 * 32 * (kMaxWalkRows + kMaxWalk + kWaves);
-}
-
 // Pass 1: one workgroup per (tile, head unit).
 template <typename T, int D, int MPW>
 __global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
-  __shared__ __align__(16) char smem[2 * Geo<T, D>::kTileBytes];
+  __shared__ __align__(16) char smem[Geo<T, D>::kSlotsStats * Geo<T, D>::kTileBytes];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (u.valid) stats_item<T, D, MPW>(a, u, hu, tile, smem);
@@ -565,12 +583,19 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 }
 
 // Pass 2: one workgroup per (tile, head unit).
-template <typename T, int D, int MPW>
+template <typename T, int D, int MPW, int kWalk>
 __global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
-  __shared__ __align__(16) char smem[smem_bytes<T, D>()];
+  __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk>()];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
-  if (u.valid) probs_item<T, D, MPW>(a, u, hu, tile, smem);
+  if (u.valid) probs_item<T, D, MPW, kWalk>(a, u, hu, tile, smem);
+}
+
+int walk_mode(const Geometry& g) {
+  if (g.walk == 0) return kWalkNone;
+  if (g.walk_rows <= 32 && g.group == 4) return kWalkFast4;
+  if (g.walk_rows <= 32 && g.group == 8) return kWalkFast8;
+  return kWalkLds;
 }
 
 int mtiles_per_wave(const Geometry& g) {
@@ -582,10 +607,23 @@ int mtiles_per_wave(const Geometry& g) {
 template <bool kProbs, int MPW, typename T, int D>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   const dim3 grid(a.g.n_tmax, a.g.n_hu);
-  if (kProbs)
-    hipLaunchKernelGGL((score_probs_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
-  else
+  if constexpr (kProbs) {
+    switch (walk_mode(a.g)) {
+      case kWalkNone:
+        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkNone>), grid, dim3(kThreads), 0, s, a);
+        break;
+      case kWalkFast4:
+        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4>), grid, dim3(kThreads), 0, s, a);
+        break;
+      case kWalkFast8:
+        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast8>), grid, dim3(kThreads), 0, s, a);
+        break;
+      default:
+        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkLds>), grid, dim3(kThreads), 0, s, a);
+    }
+  } else {
     hipLaunchKernelGGL((score_stats_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
