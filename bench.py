@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +32,42 @@ from workloads import WORKLOADS, fill_layer_, bf16_bits  # noqa: E402
 METRIC = "KV tokens scored+sampled/sec and eviction-step latency at N=32K, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "eviction_step_llama3_8b_stream32_hbm_bytes.txt")
+CSRC = os.path.join(ROOT, "streaming_weighted_sampling_amd", "csrc")
+
+
+def csrc_digest():
+    """sha256 over the kernel sources (sorted names and contents)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (already scaled by the copy calibration), or None when
+    the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    digest, found = None, None
+    for line in lines:
+        parts = line.split()
+        if len(parts) == 2 and parts[0] == "csrc_sha256:":
+            digest = parts[1]
+        if len(parts) == 4 and parts[0] == "traffic_bytes_per_launch:" and parts[1] == kernel:
+            found = int(parts[2]) + int(parts[3])
+    if digest != csrc_digest() or found is None:
+        return None
+    return {"bytes": found, "source": os.path.relpath(PROFILE_COUNTERS, ROOT)}
 
 
 def build_batch(wl, device):
@@ -141,23 +178,30 @@ def main():
     tokens = units * wl.n_tokens
     value = tokens / (ms_per_step * 1e-3)
 
-    # Algorithmic work per launch (one launch per stage per step covers every layer).
+    # Algorithmic work per launch (one launch per stage per step covers every layer):
+    # per (KV head, resident token) d*e bytes of K read once and 2*G*W*d flops per
+    # sweep; per kept row 4*d*e bytes (K and V read and written) plus a 4-byte index.
     d, e = wl.head_dim, 2
-    k_bytes = tokens * d * e                                  # one read of the resident K
-    compact_bytes = units * wl.budget * (4 * d * e + 4)       # K,V read+write of kept rows + index
-    qk_flops = tokens * 2 * wl.group * wl.window * d          # one QK^T sweep
+    k_bytes = tokens * d * e
+    compact_bytes = units * wl.budget * (4 * d * e + 4)
+    qk_flops = tokens * 2 * wl.group * wl.window * d
     per_launch = {name: (ms / max(cnt, 1), cnt) for name, (ms, cnt) in stages.items() if cnt}
-    # Algorithmic work of each stage's launch: (amount, unit, peak, bound).
+    # (algorithmic amount per launch, unit, peak, bound) of the stages that move the bulk.
     work = {
         "score_stats": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
-        "score_probs": (qk_flops / 1e12, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+        "score_probs": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
         "kv_compact": (compact_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
     }
     dominant = max((s for s in per_launch if s in work), key=lambda s: per_launch[s][0])
     amount, unit, peak, bound = work[dominant]
     achieved = amount / (per_launch[dominant][0] * 1e-3)
+    traffic = counter_traffic(dominant)
     roofline = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant}
+                "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else traffic["bytes"],
+                "kernel": dominant, "algorithmic_bytes": int(amount * 1e9),
+                "traffic_source": None if traffic is None else traffic["source"]}
+    score_ms = per_launch["score_stats"][0] + per_launch["score_probs"][0]
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
@@ -173,6 +217,8 @@ def main():
         "score_probs_mfma_tflops": round(qk_flops / (per_launch["score_probs"][0] * 1e-3) / 1e12, 1),
         "stage_gbs": {
             "score_stats_k_read": round(k_bytes / (per_launch["score_stats"][0] * 1e-3) / 1e9, 1),
+            "score_probs_k_read": round(k_bytes / (per_launch["score_probs"][0] * 1e-3) / 1e9, 1),
+            "score_k_once_over_both_sweeps": round(k_bytes / (score_ms * 1e-3) / 1e9, 1),
             "kv_compact": round(compact_bytes / (per_launch["kv_compact"][0] * 1e-3) / 1e9, 1),
             "step_algorithmic": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         },
