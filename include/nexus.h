@@ -93,7 +93,9 @@ typedef struct nx_desc {
  * head ([n_kv_heads][n_append * head_dim], contiguous) written right after the
  * kept rows, so that a streaming cache is compacted and extended in one pass
  * (the append-then-evict loop of section 2.1).  out_head_stride must then
- * hold kept + n_append rows.
+ * hold kept + n_append rows, and those rows of one KV head must span less
+ * than 2^31 bytes.  An item that breaks a rule here is skipped and sets the
+ * bad-item bit of the device status (NX_EINVAL from nx_read_device_status).
  */
 typedef struct nx_unit {
   const void* q;

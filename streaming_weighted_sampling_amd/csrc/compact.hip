@@ -7,6 +7,7 @@
 // optional appended rows out[h, kept + i, :] = app[h, i, :].  Each workgroup
 // moves kCompactRows rows of K and of V; every lane moves 16-B chunks, so a
 // 256-B row is one fully used 256-B segment read and written by 16 lanes.
+// Loads and stores go through buffer resources sized to the head's rows.
 // Output stores are non-temporal: the compacted cache is consumed by later
 // decode steps, not by this event.
 #include "nx_device.hpp"
@@ -15,39 +16,63 @@ namespace nx {
 namespace {
 
 constexpr int kThreads = 256;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// kRowBytes: 128, 256 or 512.  A block of kCompactRows rows is kCompactRows *
+// kRowBytes / 16 chunks; each lane owns kPer of them (chunk c = lane + 256 i),
+// loads every index, then every K and V chunk, then stores them all, so that
+// 2 * kPer loads per lane are in flight at once.
+template <int kRowBytes>
 __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
+  constexpr int kPerRow = kRowBytes / 16;
+  constexpr int kPer = kCompactRows * kPerRow / kThreads;
+  static_assert(kPer * kThreads == kCompactRows * kPerRow, "block split");
   const int hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid || u.out_k == nullptr || u.out_v == nullptr || u.keep == nullptr) return;
   const int rows = u.kept + u.n_append;
-  if (int(blockIdx.x) * kCompactRows >= rows) return;
-  const int row_bytes = a.g.head_dim * (a.g.dtype == NX_BF16 ? 2 : 4);
-  const int per_row = row_bytes / 16;
+  const uint32_t src_bytes = uint32_t(u.n) * kRowBytes;
+  const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
+  const Buf kb(u.k, src_bytes), vb(u.v, src_bytes);
+  const Buf kab(u.app_k, app_bytes), vab(u.app_v, app_bytes);
+  const Buf okb(u.out_k, uint32_t(rows) * kRowBytes), ovb(u.out_v, uint32_t(rows) * kRowBytes);
   bool bad = false;
   // Row blocks are strided by the grid, so any grid width covers every row.
   for (int r0 = blockIdx.x * kCompactRows; r0 < rows; r0 += gridDim.x * kCompactRows) {
-  const int r1 = min(r0 + kCompactRows, rows);
-  for (int c = threadIdx.x; c < (r1 - r0) * per_row; c += kThreads) {
-    const int r = r0 + c / per_row;
-    const int col = c - (c / per_row) * per_row;
-    const char* sk;
-    const char* sv;
-    if (r < u.kept) {
-      const int idx = u.keep[r];
-      if (idx < 0 || idx >= u.n) { bad = true; continue; }
-      sk = u.k + int64_t(idx) * row_bytes;
-      sv = u.v + int64_t(idx) * row_bytes;
-    } else {
-      sk = u.app_k + int64_t(r - u.kept) * row_bytes;
-      sv = u.app_v + int64_t(r - u.kept) * row_bytes;
+    int src[kPer];    // byte offset of the chunk in its source, or -1
+    bool app[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = threadIdx.x + kThreads * i;
+      const int r = r0 + c / kPerRow;
+      const int off = (c % kPerRow) * 16;
+      src[i] = -1;
+      app[i] = false;
+      if (r < u.kept) {
+        const int idx = u.keep[r];
+        if (idx >= 0 && idx < u.n) src[i] = idx * kRowBytes + off;
+        else bad = true;
+      } else if (r < rows) {
+        src[i] = (r - u.kept) * kRowBytes + off;
+        app[i] = true;
+      }
     }
-    const u32x4 xk = *reinterpret_cast<const u32x4*>(sk + 16 * col);
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(sv + 16 * col);
-    __builtin_nontemporal_store(xk, reinterpret_cast<u32x4*>(u.out_k + int64_t(r) * row_bytes + 16 * col));
-    __builtin_nontemporal_store(xv, reinterpret_cast<u32x4*>(u.out_v + int64_t(r) * row_bytes + 16 * col));
-  }
+    uint4 xk[kPer], xv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (src[i] >= 0) {
+        xk[i] = app[i] ? kab.ld16(uint32_t(src[i])) : kb.ld16(uint32_t(src[i]));
+        xv[i] = app[i] ? vab.ld16(uint32_t(src[i])) : vb.ld16(uint32_t(src[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (src[i] >= 0) {
+        const int c = threadIdx.x + kThreads * i;
+        const uint32_t dst = uint32_t((r0 + c / kPerRow) * kRowBytes + (c % kPerRow) * 16);
+        okb.st16<kNonTemporal>(dst, xk[i]);
+        ovb.st16<kNonTemporal>(dst, xv[i]);
+      }
+    }
   }
   if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(a, kStatusBadItem);
 }
@@ -57,7 +82,12 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
 hipError_t launch_kv_compact(const Args& a, hipStream_t s) {
   const int max_rows = a.g.max_out_rows > 0 ? a.g.max_out_rows : a.g.max_tokens;
   const dim3 grid((max_rows + kCompactRows - 1) / kCompactRows, a.g.n_hu);
-  hipLaunchKernelGGL(kv_compact_kernel, grid, dim3(kThreads), 0, s, a);
+  const int row_bytes = a.g.head_dim * (a.g.dtype == NX_BF16 ? 2 : 4);
+  switch (row_bytes) {
+    case 128: hipLaunchKernelGGL(kv_compact_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(kv_compact_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(kv_compact_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -128,7 +128,8 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
             u.n_append >= 0 && a.n_sink + a.n_recent <= u.budget &&
             u.kv_head_stride >= int64_t(u.n_tokens) * d && u.q != nullptr && u.k != nullptr;
   if (u.out_k || u.out_v)
-    ok = ok && u.out_head_stride >= int64_t(r.kept + u.n_append) * d;
+    ok = ok && u.out_head_stride >= int64_t(r.kept + u.n_append) * d &&
+         (int64_t(r.kept) + u.n_append) * d * esz <= INT32_MAX;
   if (u.n_append > 0) ok = ok && u.app_k != nullptr && u.app_v != nullptr;
   r.valid = ok;
   return r;

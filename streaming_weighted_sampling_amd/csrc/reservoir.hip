@@ -99,24 +99,37 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   uint64_t v_or = 0, v_and = ~0ull;
   bool nonfinite = false;
-  const int j_end = min(j0 + kKeysPerBlock, u.n);
-  for (int j = j0 + threadIdx.x; j < j_end; j += kKeysThreads) {
-    float w;
+  // Each lane owns kPer tokens j0 + lane + 256 i: every input load of the
+  // lane is issued before the first Philox / log, so one memory latency
+  // covers all of them.
+  constexpr int kPer = kKeysPerBlock / kKeysThreads;
+  float w[kPer];
+  bool in[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    in[i] = j < u.n;
+    const int jc = in[i] ? j : j0;   // a valid token for the lanes past the end
     if (a.w_in != nullptr) {
-      w = a.w_in[ext + j];
+      w[i] = a.w_in[ext + jc];
     } else {
       float cj = 0.f;
 #pragma unroll
       for (int t = 0; t < kMaxWalk; ++t)
-        if (t < g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * g.max_tokens + j], cj);
-      w = a_in[j] + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+        if (t < g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * g.max_tokens + jc], cj);
+      w[i] = a_in[jc] + a.lambda * cj + a.eps_tie * (float(jc) * ramp);
     }
-    nonfinite |= !isfinite(w);
-    if (a.w_out != nullptr) a.w_out[ext + j] = w;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (!in[i]) continue;
+    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    nonfinite |= !isfinite(w[i]);
+    if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
     if (a.stop_after_weights) continue;
     const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
     const double uj = philox_uniform53(x.x, x.y);
-    double key = w > 0.f ? log(uj) / double(w) : -INFINITY;
+    double key = w[i] > 0.f ? log(uj) / double(w[i]) : -INFINITY;
     if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
     if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
     const uint64_t code = key_code(key);
