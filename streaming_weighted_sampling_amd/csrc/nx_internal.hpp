@@ -29,6 +29,8 @@ constexpr int kMinTokPerBlock = 256;   // smallest token range of a score workgr
 constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two)
 constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
+constexpr int kFusedPer = 32;        // tokens per lane of the fused keys + select kernel
+constexpr int kFusedMaxTokens = 1024 * kFusedPer;   // largest n it handles
 
 enum Stage {
   kStageScoreStats = 0,
@@ -38,6 +40,7 @@ enum Stage {
   kStageReservoirKeys,
   kStageTopbSelect,
   kStageKvCompact,
+  kStageSampleSelect,   // keys + select fused (n <= kFusedMaxTokens)
   kNumStages
 };
 
@@ -114,6 +117,7 @@ hipError_t launch_score_probs(const Args& a, hipStream_t s);
 hipError_t launch_walk_coef(const Args& a, hipStream_t s);
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
 hipError_t launch_topb_select(const Args& a, hipStream_t s);
+hipError_t launch_sample_select(const Args& a, hipStream_t s);
 hipError_t launch_kv_compact(const Args& a, hipStream_t s);
 
 }  // namespace nx

@@ -21,6 +21,8 @@
 //     count or all 64 bits are fixed (true ties: larger index wins)
 //   * writes the kept indices in ascending order with ballot / popcount
 //     prefix sums, 1024 tokens per round.
+#include <type_traits>
+
 #include "nx_device.hpp"
 
 namespace nx {
@@ -29,6 +31,7 @@ namespace {
 constexpr int kKeysThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+static_assert(kFusedMaxTokens == kSelThreads * kFusedPer, "fused select covers 1024 lanes");
 
 // One wavefront per head unit: fixed-order reduction of the per-tile Gram
 // partials (lane-strided sums, then a butterfly), then the walk recurrence
@@ -308,6 +311,212 @@ __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) 
   }
 }
 
+// Keys and selection in one workgroup per head unit, for n <= kFusedMaxTokens:
+// lane l computes the codes of tokens l + 1024 i (i < kFusedPer) into
+// registers exactly as reservoir_keys does, and the MSD radix passes of
+// topb_select then run over those registers, so the codes never go through
+// memory.  Same keys, same selection rule, same output as the two kernels.
+__device__ inline float token_weight(const Args& a, const float* s_coef, const float* a_in,
+                                     const float* p_in, float ramp, int j) {
+  float cj = 0.f;
+#pragma unroll
+  for (int t = 0; t < kMaxWalk; ++t)
+    if (t < a.g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * a.g.max_tokens + j], cj);
+  return a_in[j] + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+}
+
+__global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int n = u.n;
+  __shared__ float s_coef[kMaxWalk];
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ int s_need, s_eq, s_done, s_start;
+  __shared__ int s_cnt[kSelWaves];
+  __shared__ int s_cut;
+  __shared__ uint64_t s_or[kSelWaves], s_and[kSelWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (tid < kMaxWalk)
+    s_coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
+  __syncthreads();
+
+  const float* a_in = a.a + size_t(hu) * g.max_tokens;
+  const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
+  const size_t ext = size_t(u.h) * u.n;   // row of head h in [h_kv, n] exports
+  const float ramp = n > 1 ? 1.f / float(n - 1) : 0.f;
+  const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
+  uint64_t code[kFusedPer];
+  uint64_t v_or = 0, v_and = ~0ull;
+  bool nonfinite = false;
+  constexpr int kBatch = 4;   // tokens whose inputs are loaded together
+  // One batch at compile-time offset b; the eight batches are spelled out so
+  // that every index into code[] is a constant (a loop over all 32 tokens is
+  // too large for the unroller, and a runtime index would put code[] in
+  // scratch memory).
+  auto batch = [&](auto b_const) {
+    constexpr int b = decltype(b_const)::value;
+    float w[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = tid + kSelThreads * (b + i);
+      const int jc = j < n ? j : 0;
+      w[i] = a.w_in != nullptr ? a.w_in[ext + jc] : token_weight(a, s_coef, a_in, p_in, ramp, jc);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int j = tid + kSelThreads * (b + i);
+      code[b + i] = 0;
+      if (j < n) {
+        nonfinite |= !isfinite(w[i]);
+        if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
+        const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
+        const double uj = philox_uniform53(x.x, x.y);
+        double key = w[i] > 0.f ? log(uj) / double(w[i]) : -INFINITY;
+        if (j < a.n_sink || j >= n - a.n_recent) key = INFINITY;
+        if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
+        code[b + i] = key_code(key);
+        v_or |= code[b + i];
+        v_and &= code[b + i];
+      }
+    }
+  };
+  static_assert(kFusedPer == 8 * kBatch, "eight batches");
+  batch(std::integral_constant<int, 0>{});
+  batch(std::integral_constant<int, kBatch>{});
+  batch(std::integral_constant<int, 2 * kBatch>{});
+  batch(std::integral_constant<int, 3 * kBatch>{});
+  batch(std::integral_constant<int, 4 * kBatch>{});
+  batch(std::integral_constant<int, 5 * kBatch>{});
+  batch(std::integral_constant<int, 6 * kBatch>{});
+  batch(std::integral_constant<int, 7 * kBatch>{});
+  if (__syncthreads_or(nonfinite) && tid == 0) raise_status(a, kStatusNonFinite);
+  if (u.keep == nullptr) return;
+  if (u.budget >= n) {
+    for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+    return;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    v_or |= __shfl_xor(v_or, m, 64);
+    v_and &= __shfl_xor(v_and, m, 64);
+  }
+  if (lane == 0) { s_or[wave] = v_or; s_and[wave] = v_and; }
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t o = 0, an = ~0ull;
+    for (int w = 0; w < kSelWaves; ++w) { o |= s_or[w]; an &= s_and[w]; }
+    const uint64_t diff = o ^ an;
+    s_need = u.budget;
+    s_eq = n;
+    if (diff == 0) {                       // every code equal: pure ties
+      s_prefix = an;
+      s_mask = ~0ull;
+      s_done = 1;
+    } else {
+      const int top = 63 - __clzll(diff);  // highest bit that differs
+      const uint64_t above = top == 63 ? 0ull : (~0ull << (top + 1));
+      s_prefix = an & above;
+      s_mask = above;
+      s_done = 0;
+      s_start = top;
+    }
+  }
+  __syncthreads();
+
+  // MSD radix passes over the unresolved bits (at most 8, see topb_select).
+  int start = s_start;
+  while (!s_done && start >= 0) {
+    const int shift = start >= 7 ? start - 7 : 0;
+    const int width = start - shift + 1;
+    const uint32_t dmask = (1u << width) - 1u;
+    if (tid < 256) s_hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = s_prefix, mask = s_mask;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      const int j = tid + kSelThreads * i;
+      if (j < n && (code[i] & mask) == prefix)
+        atomicAdd(&s_hist[uint32_t(code[i] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t h0 = s_hist[4 * lane], h1 = s_hist[4 * lane + 1], h2 = s_hist[4 * lane + 2],
+                     h3 = s_hist[4 * lane + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t suf = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_down(suf, off, 64);
+        if (lane + off < 64) suf += v;
+      }
+      const uint32_t higher = suf - own;
+      const uint32_t need = uint32_t(s_need);
+      if (higher < need && need <= suf) {
+        const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
+        const int bb = need <= c3 ? 3 : need <= c2 ? 2 : need <= c1 ? 1 : 0;
+        const uint32_t acc = bb == 3 ? higher : bb == 2 ? c3 : bb == 1 ? c2 : c1;
+        const uint32_t hb = bb == 3 ? h3 : bb == 2 ? h2 : bb == 1 ? h1 : h0;
+        s_need = int(need - acc);
+        s_eq = int(hb);
+        s_prefix = prefix | (uint64_t(4 * lane + bb) << shift);
+        s_mask = mask | (uint64_t(dmask) << shift);
+        s_done = (hb == need - acc) || shift == 0;
+      }
+    }
+    __syncthreads();
+    start = shift - 1;
+  }
+
+  if (!s_done) {
+    if (tid == 0) raise_status(a, kStatusBadItem);
+    for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+    return;
+  }
+  const uint64_t prefix = s_prefix, mask = s_mask;
+  const int need = s_need;
+  const bool ties = s_eq != need;
+  if (tid == 0) s_cut = 0;
+  __syncthreads();
+  const int n_rounds = (n + kSelThreads - 1) / kSelThreads;
+  if (ties) {
+    int seen = 0;
+#pragma unroll
+    for (int r = kFusedPer - 1; r >= 0; --r) {
+      if (r < n_rounds && seen < need) {
+        const int j = r * kSelThreads + tid;
+        const bool eq = j < n && (code[r] & mask) == prefix;
+        int tot;
+        const int below = block_rank(eq, s_cnt, &tot);
+        const int above = tot - below - (eq ? 1 : 0);
+        if (eq && seen + above + 1 == need) s_cut = j;
+        seen += tot;
+      }
+    }
+    __syncthreads();
+  }
+  const int cut = s_cut;
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < kFusedPer; ++r) {
+    if (r < n_rounds) {
+      const int j = r * kSelThreads + tid;
+      bool keep = false;
+      if (j < n) {
+        const uint64_t top = code[r] & mask;
+        keep = top > prefix || (top == prefix && (!ties || j >= cut));
+      }
+      int tot;
+      const int pos = block_rank(keep, s_cnt, &tot);
+      if (keep && base + pos < u.budget) u.keep[base + pos] = j;
+      base += tot;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
@@ -317,6 +526,11 @@ hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
 
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL(reservoir_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_select(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(sample_select_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 

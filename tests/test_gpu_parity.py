@@ -83,15 +83,17 @@ def test_reservoir_select_bitexact_on_given_weights(n, budget, sink, recent):
         assert gc.overlap_fraction(got, ref_keep[h]) >= 1 - 2.0 / kept
 
 
-def test_reservoir_select_ties_and_nonpositive_weights():
-    """Many -inf keys (w <= 0) and duplicates: ties go to the larger index."""
-    h_kv, n = 2, 3000
+@pytest.mark.parametrize("n", [3000, 40000])
+def test_reservoir_select_ties_and_nonpositive_weights(n):
+    """Many -inf keys (w <= 0) and duplicates: ties go to the larger index.
+    n = 3000 runs the fused keys + select kernel, n = 40000 the two-kernel path."""
+    h_kv = 2
     cfg = _cfg(2, h_kv, 64, 4)
     ws = _ws(cfg, n, walk=0)
     w = np.zeros((h_kv, n), dtype=np.float32)
     w[:, ::3] = 1e-3                      # a third positive, the rest -inf keys
     w[1, 5] = -1.0
-    for budget in (500, 1000, 1500, 2999):
+    for budget in (n // 6, n // 3, n // 2, n - 1):
         keep, _ = nx.nx_reservoir_select(cfg, torch.from_numpy(w).to(DEV), budget, 7, workspace=ws)
         nx.nx_read_device_status(cfg, ws)
         _, ref = nexus.select_from_weights(w, budget, 7)
@@ -119,6 +121,38 @@ def test_reservoir_inclusion_frequencies_match_enumeration():
     pi = np.array(inclusion_probabilities_float(wv.astype(np.float64), budget))
     sigma = np.sqrt(pi * (1 - pi) / draws)
     assert np.all(np.abs(freq - pi) < 5 * sigma), (freq, pi)
+
+
+@pytest.mark.parametrize("n", [32768, 20001])
+def test_fused_and_two_kernel_selection_agree(n):
+    """Keys + select run fused when max_tokens <= 32768 and as two kernels
+    otherwise; the same items must give the same kept rows either way."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window)
+    budget = n // 5
+    layers = 2
+    data = [gen_layer(wl, device=DEV, n_tokens=n, layer=l) for l in range(layers)]
+    outs = []
+    for max_tokens in (n, 32769):
+        keep = torch.full((layers, wl.h_kv, budget), -1, dtype=torch.int32, device=DEV)
+        ok = torch.empty(layers, wl.h_kv, budget, wl.head_dim, dtype=torch.bfloat16, device=DEV)
+        ov = torch.empty_like(ok)
+        items = [dict(q=q, k=k, v=v, keep=keep[l], out_k=ok[l], out_v=ov[l],
+                      kv_head_stride=n * wl.head_dim, out_head_stride=budget * wl.head_dim,
+                      n_tokens=n, budget=budget, layer=l)
+                 for l, (q, k, v) in enumerate((d["q"], d["k"], d["v"]) for d in data)]
+        units = nx.make_units(items, device=DEV)
+        ws = _ws(cfg, max_tokens, layers, wl.walk_iters)
+        nx.nx_evict_batch(cfg, units, layers, max_tokens, wl.walk_iters, 3, workspace=ws, step=2,
+                          max_out_rows=budget)
+        nx.nx_read_device_status(cfg, ws)
+        outs.append((keep.clone(), ok.clone(), ov.clone()))
+    for l in range(layers):
+        for h in range(wl.h_kv):
+            gc.check_keep_valid(outs[0][0][l, h].cpu().numpy(), n, budget)
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    assert torch.equal(outs[0][2].view(torch.int16), outs[1][2].view(torch.int16))
 
 
 # --------------------------------------------------------------- compaction --
