@@ -145,8 +145,9 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 }
 
 // Enqueue stages [first, last] in order.
-// Keys and select run as one kernel when every item fits its registers and the
-// call goes on to selection (not the weights-only export).
+// Items of up to kFusedMaxTokens tokens select on estimate codes held in the
+// select kernel's registers (estimate_keys + sample_select) when the call goes
+// on to selection (not the weights-only export).
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   hipError_t err = hipSuccess;
   const bool fused = a.g.max_tokens <= kFusedMaxTokens && !a.stop_after_weights &&
@@ -159,12 +160,15 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
       case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
       case kStageReservoirKeys:
         if (fused)
-          err = run_stage(kStageSampleSelect, s, [&] { return launch_sample_select(a, s); });
+          err = run_stage(kStageEstimateKeys, s, [&] { return launch_estimate_keys(a, s); });
         else
           err = run_stage(st, s, [&] { return launch_reservoir_keys(a, s); });
         break;
       case kStageTopbSelect:
-        if (!fused) err = run_stage(st, s, [&] { return launch_topb_select(a, s); });
+        if (fused)
+          err = run_stage(kStageSampleSelect, s, [&] { return launch_sample_select(a, s); });
+        else
+          err = run_stage(st, s, [&] { return launch_topb_select(a, s); });
         break;
       case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(a, s); }); break;
       default: break;
@@ -378,7 +382,7 @@ int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_st
 const char* nx_stage_name(int32_t stage) {
   static const char* names[kNumStages] = {"score_stats", "score_combine",  "score_probs",
                                           "walk_coef",   "reservoir_keys", "topb_select",
-                                          "kv_compact",  "sample_select"};
+                                          "kv_compact",  "sample_select", "estimate_keys"};
   return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
 }
 

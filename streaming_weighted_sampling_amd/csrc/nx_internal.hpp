@@ -40,7 +40,8 @@ enum Stage {
   kStageReservoirKeys,
   kStageTopbSelect,
   kStageKvCompact,
-  kStageSampleSelect,   // keys + select fused (n <= kFusedMaxTokens)
+  kStageSampleSelect,   // select on estimate codes in registers (n <= kFusedMaxTokens)
+  kStageEstimateKeys,   // estimate codes of the keys (n <= kFusedMaxTokens)
   kNumStages
 };
 
@@ -118,6 +119,7 @@ hipError_t launch_walk_coef(const Args& a, hipStream_t s);
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
 hipError_t launch_topb_select(const Args& a, hipStream_t s);
 hipError_t launch_sample_select(const Args& a, hipStream_t s);
+hipError_t launch_estimate_keys(const Args& a, hipStream_t s);
 hipError_t launch_kv_compact(const Args& a, hipStream_t s);
 
 }  // namespace nx

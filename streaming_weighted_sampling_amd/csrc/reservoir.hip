@@ -178,6 +178,146 @@ __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
   return off + below;
 }
 
+// Shared state of one radix selection.  After the passes: keys whose bits
+// under `mask` exceed `prefix` are kept; of the `eq` keys equal to it under
+// the mask, `need` are kept (all of them when eq == need, else the ones with
+// the largest indices: true ties, every bit fixed).
+struct SelCore {
+  uint32_t hist[256];
+  uint64_t prefix, mask;
+  int need, eq, done, start, cut;
+  int cnt[kSelWaves];
+  uint64_t red_or[kSelWaves], red_and[kSelWaves];
+};
+
+// Thread 0: the state before the passes, from the OR and AND of all codes
+// (the bits above the highest differing one are common to every code).
+__device__ inline void sel_init(SelCore& sh, uint64_t o, uint64_t an, int n, int budget) {
+  const uint64_t diff = o ^ an;
+  sh.need = budget;
+  sh.eq = n;
+  if (diff == 0) {                       // every code equal: pure ties
+    sh.prefix = an;
+    sh.mask = ~0ull;
+    sh.done = 1;
+  } else {
+    const int top = 63 - __clzll(diff);  // highest bit that differs
+    const uint64_t above = top == 63 ? 0ull : (~0ull << (top + 1));
+    sh.prefix = an & above;
+    sh.mask = above;
+    sh.done = 0;
+    sh.start = top;
+  }
+}
+
+// Wave 0 after a histogram pass: lane l owns bins 4l..4l+3; suffix sums over
+// the lanes find the bin that holds the need-th largest candidate.
+__device__ inline void sel_pick_bin(SelCore& sh, int shift, uint32_t dmask) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1], h2 = sh.hist[4 * lane + 2],
+                 h3 = sh.hist[4 * lane + 3];
+  const uint32_t own = h0 + h1 + h2 + h3;
+  uint32_t suf = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += v;
+  }
+  const uint32_t higher = suf - own;   // candidates in bins above this lane's
+  const uint32_t need = uint32_t(sh.need);
+  if (higher < need && need <= suf) {
+    const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
+    const int b = need <= c3 ? 3 : need <= c2 ? 2 : need <= c1 ? 1 : 0;
+    const uint32_t acc = b == 3 ? higher : b == 2 ? c3 : b == 1 ? c2 : c1;
+    const uint32_t hb = b == 3 ? h3 : b == 2 ? h2 : b == 1 ? h1 : h0;
+    sh.need = int(need - acc);
+    sh.eq = int(hb);
+    sh.prefix = sh.prefix | (uint64_t(4 * lane + b) << shift);
+    sh.mask = sh.mask | (uint64_t(dmask) << shift);
+    sh.done = (hb == need - acc) || shift == 0;
+  }
+}
+
+// MSD radix passes with 8-bit digits over the unresolved bits, highest first,
+// until the boundary bin holds exactly the missing count or every bit is
+// fixed; at most 64 bits, so at most 8 passes.  code_at(i) gives the code of
+// the i-th candidate slot of this thread (slot count `slots`, valid(i)).
+template <typename CodeAt, typename Valid>
+__device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Valid&& valid) {
+  int start = sh.start;
+  while (!sh.done && start >= 0) {
+    const int shift = start >= 7 ? start - 7 : 0;
+    const int width = start - shift + 1;
+    const uint32_t dmask = (1u << width) - 1u;
+    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    for (int i = 0; i < slots; ++i) {
+      if (valid(i)) {
+        const uint64_t c = code_at(i);
+        if ((c & mask) == prefix) atomicAdd(&sh.hist[uint32_t(c >> shift) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) sel_pick_bin(sh, shift, dmask);
+    __syncthreads();
+    start = shift - 1;
+  }
+}
+
+// Selection over codes in global memory (keys[j], j < n): the common prefix
+// from (o, an), the radix passes, then the kept indices in ascending order.
+__device__ inline void select_global(const Args& a, const HeadUnit& u, const uint64_t* keys,
+                                     uint64_t o, uint64_t an, SelCore& sh) {
+  const int n = u.n, tid = threadIdx.x;
+  if (tid == 0) sel_init(sh, o, an, n, u.budget);
+  __syncthreads();
+  const int slots = (n + kSelThreads - 1) / kSelThreads;
+  sel_passes(sh, slots, [&](int i) { return keys[tid + kSelThreads * i]; },
+             [&](int i) { return tid + kSelThreads * i < n; });
+  if (!sh.done) {
+    // Unreachable with consistent inputs; report and keep the oldest tokens.
+    if (tid == 0) raise_status(a, kStatusBadItem);
+    for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+    return;
+  }
+  const uint64_t prefix = sh.prefix, mask = sh.mask;
+  const int need = sh.need;
+  const bool ties = sh.eq != need;   // only possible with all 64 bits fixed
+  if (tid == 0) sh.cut = 0;
+  __syncthreads();
+  if (ties) {
+    // Among codes equal to the threshold keep the `need` largest indices:
+    // scan rounds from the end and find the index where the count reaches need.
+    int seen = 0;
+    for (int r = slots - 1; r >= 0; --r) {
+      const int j = r * kSelThreads + tid;
+      const bool eq = j < n && (keys[j] & mask) == prefix;
+      int tot;
+      const int below = block_rank(eq, sh.cnt, &tot);
+      const int above = tot - below - (eq ? 1 : 0);   // ties at larger j in this round
+      if (eq && seen + above + 1 == need) sh.cut = j;
+      seen += tot;
+      if (seen >= need) break;
+    }
+    __syncthreads();
+  }
+  const int cut = sh.cut;
+  int base = 0;
+  for (int r = 0; r < slots; ++r) {
+    const int j = r * kSelThreads + tid;
+    bool keep = false;
+    if (j < n) {
+      const uint64_t top = keys[j] & mask;
+      keep = top > prefix || (top == prefix && (!ties || j >= cut));
+    }
+    int tot;
+    const int pos = block_rank(keep, sh.cnt, &tot);
+    if (keep && base + pos < u.budget) u.keep[base + pos] = j;
+    base += tot;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) {
   const Geometry& g = a.g;
   const int hu = blockIdx.x;
@@ -188,141 +328,177 @@ __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) 
     for (int j = threadIdx.x; j < n; j += kSelThreads) u.keep[j] = j;
     return;
   }
-  const uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ int s_need, s_eq, s_done, s_start;
-  __shared__ int s_cnt[kSelWaves];
-  __shared__ int s_cut;
-
+  __shared__ SelCore sh;
+  uint64_t o = 0, an = ~0ull;
   if (threadIdx.x == 0) {
     const int n_chunks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
     const uint64_t* sp = a.selp + size_t(hu) * g.n_kc * 2;
-    uint64_t o = 0, an = ~0ull;
     for (int c = 0; c < n_chunks; ++c) { o |= sp[2 * c]; an &= sp[2 * c + 1]; }
-    const uint64_t diff = o ^ an;
-    s_need = u.budget;
-    if (diff == 0) {                       // every code equal: pure ties
-      s_prefix = an;
-      s_mask = ~0ull;
-      s_eq = n;
-      s_done = 1;
-    } else {
-      const int top = 63 - __clzll(diff);  // highest bit that differs
-      const uint64_t above = top == 63 ? 0ull : (~0ull << (top + 1));
-      s_prefix = an & above;
-      s_mask = above;
-      s_eq = n;
-      s_done = 0;
-      s_start = top;
-    }
   }
-  __syncthreads();
-
-  // MSD radix passes over the unresolved bits, highest first.  At most 64
-  // bits are resolved, so the loop ends after at most 8 passes even if the
-  // codes were inconsistent with the OR/AND summary.
-  int start = s_start;
-  while (!s_done && start >= 0) {
-    const int shift = start >= 7 ? start - 7 : 0;
-    const int width = start - shift + 1;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int b = threadIdx.x; b < 256; b += kSelThreads) s_hist[b] = 0;
-    __syncthreads();
-    const uint64_t prefix = s_prefix, mask = s_mask;
-    for (int j = threadIdx.x; j < n; j += kSelThreads) {
-      const uint64_t c = keys[j];
-      if ((c & mask) == prefix) atomicAdd(&s_hist[uint32_t(c >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      // Lane l owns bins 4l..4l+3; suffix sums over lanes find the bin that
-      // holds the need-th largest candidate.
-      const int l = threadIdx.x;
-      const uint32_t h0 = s_hist[4 * l], h1 = s_hist[4 * l + 1], h2 = s_hist[4 * l + 2],
-                     h3 = s_hist[4 * l + 3];
-      const uint32_t own = h0 + h1 + h2 + h3;
-      uint32_t suf = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(suf, off, 64);
-        if (l + off < 64) suf += v;
-      }
-      const uint32_t higher = suf - own;   // candidates in bins above this lane's
-      const uint32_t need = uint32_t(s_need);
-      if (higher < need && need <= suf) {
-        const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
-        const int b = need <= c3 ? 3 : need <= c2 ? 2 : need <= c1 ? 1 : 0;
-        const uint32_t acc = b == 3 ? higher : b == 2 ? c3 : b == 1 ? c2 : c1;
-        const uint32_t hb = b == 3 ? h3 : b == 2 ? h2 : b == 1 ? h1 : h0;
-        s_need = int(need - acc);
-        s_eq = int(hb);
-        s_prefix = prefix | (uint64_t(4 * l + b) << shift);
-        s_mask = mask | (uint64_t(dmask) << shift);
-        s_done = (hb == need - acc) || shift == 0;
-      }
-    }
-    __syncthreads();
-    start = shift - 1;
-  }
-
-  if (!s_done) {
-    // Unreachable with consistent inputs; report and keep the oldest tokens.
-    if (threadIdx.x == 0) raise_status(a, kStatusBadItem);
-    for (int j = threadIdx.x; j < u.budget; j += kSelThreads) u.keep[j] = j;
-    return;
-  }
-  const uint64_t prefix = s_prefix, mask = s_mask;
-  const int need = s_need;
-  const bool ties = s_eq != need;   // only possible with all 64 bits fixed
-  if (threadIdx.x == 0) s_cut = 0;
-  __syncthreads();
-  if (ties) {
-    // Among codes equal to the threshold keep the `need` largest indices:
-    // scan rounds from the end and find the index where the count reaches need.
-    int seen = 0;
-    const int n_rounds = (n + kSelThreads - 1) / kSelThreads;
-    for (int r = n_rounds - 1; r >= 0; --r) {
-      const int j = r * kSelThreads + threadIdx.x;
-      const bool eq = j < n && (keys[j] & mask) == prefix;
-      int tot;
-      const int below = block_rank(eq, s_cnt, &tot);
-      const int above = tot - below - (eq ? 1 : 0);   // ties at larger j in this round
-      if (eq && seen + above + 1 == need) s_cut = j;
-      seen += tot;
-      if (seen >= need) break;
-    }
-    __syncthreads();
-  }
-  const int cut = s_cut;
-  int base = 0;
-  const int n_rounds = (n + kSelThreads - 1) / kSelThreads;
-  for (int r = 0; r < n_rounds; ++r) {
-    const int j = r * kSelThreads + threadIdx.x;
-    bool keep = false;
-    if (j < n) {
-      const uint64_t top = keys[j] & mask;
-      keep = top > prefix || (top == prefix && (!ties || j >= cut));
-    }
-    int tot;
-    const int pos = block_rank(keep, s_cnt, &tot);
-    if (keep && base + pos < u.budget) u.keep[base + pos] = j;
-    base += tot;
-  }
+  select_global(a, u, a.keys + size_t(hu) * g.max_tokens, o, an, sh);
 }
 
-// Keys and selection in one workgroup per head unit, for n <= kFusedMaxTokens:
-// lane l computes the codes of tokens l + 1024 i (i < kFusedPer) into
-// registers exactly as reservoir_keys does, and the MSD radix passes of
-// topb_select then run over those registers, so the codes never go through
-// memory.  Same keys, same selection rule, same output as the two kernels.
-__device__ inline float token_weight(const Args& a, const float* s_coef, const float* a_in,
-                                     const float* p_in, float ramp, int j) {
+// Keys and selection in one workgroup per head unit, for n <= kFusedMaxTokens.
+// Lane l owns tokens l + 1024 i (i < kFusedPer).
+//
+// The order of the keys ln(u)/w equals the reverse order of
+// s = log2(-ln u) - log2(w), which fp32 estimates within 1e-4 (estimate_code).
+// A radix select on 32-bit codes of -s, held in registers, finds the B-th
+// largest estimate; tokens whose estimate lies more than kBand from it are
+// provably on their side of the exact threshold (kBand >= 2 x the estimate
+// error, strictly, so no tie crosses it), and only the tokens inside the band
+// get the exact fp64 key of reservoir_keys, which decides among them.  The
+// result equals selecting on the exact keys.  The -inf class (w <= 0) and the
+// +inf class (forced slots) are exact in both.  Fallback (key export
+// requested, or more than kBandCap band tokens): exact keys of every token
+// into the workspace and the global-memory selection of topb_select.
+constexpr int kBandCap = 2048;
+constexpr float kBand = 0x1p-9f;
+constexpr float kLn2f = 0.693147180559945309f;
+
+struct SelShared {
+  SelCore core;
+  float coef[kMaxWalk];
+  int n_band, n_above;
+  uint32_t cb;
+  uint32_t band_idx[kBandCap];
+  uint64_t band_code[kBandCap];
+  uint32_t chosen[kFusedMaxTokens / 32];
+  int round_cnt[kFusedPer * kSelWaves];
+};
+
+__device__ __attribute__((always_inline)) inline float token_weight(
+    const Args& a, const float* s_coef, const float* a_in, const float* p_in, float ramp, int j) {
   float cj = 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxWalk; ++t)
     if (t < a.g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * a.g.max_tokens + j], cj);
   return a_in[j] + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+}
+
+// Weight of token j of this head unit (given weights, or a + lambda c~ + ramp).
+struct WeightSrc {
+  const float* w_in;   // [h_kv, n] row of this head, or nullptr
+  const float* a_in;
+  const float* p_in;
+  float ramp;
+  __device__ __attribute__((always_inline)) float operator()(const Args& a, const float* s_coef,
+                                                             int j) const {
+    return w_in != nullptr ? w_in[j] : token_weight(a, s_coef, a_in, p_in, ramp, j);
+  }
+};
+
+// Order-preserving 32-bit code of a float (-0 folded into +0).
+__device__ inline uint32_t f32_code(float x) {
+  const uint32_t b = __float_as_uint(x + 0.f);
+  return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float f32_decode(uint32_t c) {
+  return __uint_as_float((c >> 31) ? (c & 0x7FFFFFFFu) : ~c);
+}
+
+// Estimate code of the key ln(u)/w: 0 for w <= 0 (key -inf), ~0 for a forced
+// slot (+inf), else the code of -s.  With u = m 2^-53 (m = k53 + 1) and
+// E = -ln u, x = (2^53 - m) 2^-53:
+//   x < 2^-7:    E = x (1 + x/2 + x^2/3 + x^3/4)        (relative error < 1e-7)
+//   otherwise:   E = -log2(u) ln 2, u rounded to fp32 (within 2^-23): since
+//                E >= 2^-7 here the rounding costs at most 2^-16 relative, and
+//                v_log_f32 is within one ulp of its output (measured on gfx950
+//                down to inputs 2^-24 below 1).
+// Then s = (eE - ew) + log2(mE / mw) from the exact binary exponents and
+// mantissas of E and w (subnormal w included).  |error of s| < 5e-5, twenty
+// times inside kBand.
+__device__ inline uint32_t estimate_code(uint32_t x0, uint32_t x1, float w, bool forced) {
+  if (forced) return 0xFFFFFFFFu;
+  if (!(w > 0.f)) return 0u;
+  const uint64_t m = (((uint64_t(x0) << 32) | uint64_t(x1)) >> 11) + 1;
+  const uint64_t d = (1ull << 53) - m;
+  if (d == 0) return f32_code(INFINITY);   // u = 1: key 0, the largest finite key
+  float e;
+  if (d < (1ull << 46)) {
+    const float x = float(uint32_t(d)) * 0x1p-53f + float(uint32_t(d >> 32)) * 0x1p-21f;
+    e = x * (1.f + x * (0.5f + x * (0.333333343f + x * 0.25f)));
+  } else {
+    const float uf = (float(uint32_t(m >> 21)) * 0x1p21f + float(uint32_t(m) & 0x1FFFFFu)) * 0x1p-53f;
+    e = -__builtin_amdgcn_logf(uf) * kLn2f;
+  }
+  int ee, ew;
+  const float me = __builtin_frexpf(e, &ee);
+  const float mw = __builtin_frexpf(w, &ew);
+  const float sv = float(ee - ew) + __builtin_amdgcn_logf(me * __builtin_amdgcn_rcpf(mw));
+  return min(max(f32_code(-sv), 1u), 0xFFFFFFFEu);
+}
+
+// Exact fp64 key of token j (reservoir_keys' definition).
+__device__ __attribute__((always_inline)) inline double exact_key(const Args& a, const HeadUnit& u,
+                                                                  int j, float w, uint32_t k0,
+                                                                  uint32_t k1) {
+  const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
+  const double uj = philox_uniform53(x.x, x.y);
+  double key = w > 0.f ? log(uj) / double(w) : -INFINITY;
+  if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
+  return key;
+}
+
+// f(integral_constant<int, i>) for i = B .. E-1, expanded at compile time, so
+// that register arrays indexed by i stay in registers where the body is too
+// large for the loop unroller.
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Whether a head unit's selection runs on estimate codes (no key export, a
+// keep array, and something to drop).
+__device__ inline bool uses_estimate(const Args& a, const HeadUnit& u) {
+  return a.keys_out == nullptr && u.keep != nullptr && u.budget < u.n;
+}
+
+// Estimate codes of kKeysPerBlock tokens of one head unit (many workgroups
+// per head unit, like reservoir_keys), stored as uint32 at the start of the
+// head unit's key array; also the non-finite check and the weight export.
+__global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.y, chunk = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int j0 = chunk * kKeysPerBlock;
+  if (j0 >= u.n) return;
+  __shared__ float s_coef[kMaxWalk];
+  if (threadIdx.x < kMaxWalk)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
+  __syncthreads();
+  const int n = u.n;
+  const size_t ext = size_t(u.h) * n;
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
+                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
+  const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
+  const bool estimate = uses_estimate(a, u);
+  uint32_t* codes = reinterpret_cast<uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
+  constexpr int kPer = kKeysPerBlock / kKeysThreads;
+  float w[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    w[i] = ws(a, s_coef, j < n ? j : j0);
+  }
+  bool nonfinite = false;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    if (j < n) {
+      nonfinite |= !isfinite(w[i]);
+      if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
+      if (estimate) {
+        const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
+        codes[j] = estimate_code(x.x, x.y, w[i], j < a.n_sink || j >= n - a.n_recent);
+      }
+    }
+  }
+  if (__syncthreads_or(nonfinite) && threadIdx.x == 0) raise_status(a, kStatusNonFinite);
 }
 
 __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a) {
@@ -331,188 +507,199 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) return;
   const int n = u.n;
-  __shared__ float s_coef[kMaxWalk];
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint64_t s_prefix, s_mask;
-  __shared__ int s_need, s_eq, s_done, s_start;
-  __shared__ int s_cnt[kSelWaves];
-  __shared__ int s_cut;
-  __shared__ uint64_t s_or[kSelWaves], s_and[kSelWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ SelShared sh;
+  SelCore& core = sh.core;
+  const int tid = threadIdx.x;
 
-  if (tid < kMaxWalk)
-    s_coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
+  if (tid < kMaxWalk) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
   __syncthreads();
 
-  const float* a_in = a.a + size_t(hu) * g.max_tokens;
-  const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
   const size_t ext = size_t(u.h) * u.n;   // row of head h in [h_kv, n] exports
-  const float ramp = n > 1 ? 1.f / float(n - 1) : 0.f;
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
+                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
-  uint64_t code[kFusedPer];
-  uint64_t v_or = 0, v_and = ~0ull;
-  bool nonfinite = false;
-  constexpr int kBatch = 4;   // tokens whose inputs are loaded together
-  // One batch at compile-time offset b; the eight batches are spelled out so
-  // that every index into code[] is a constant (a loop over all 32 tokens is
-  // too large for the unroller, and a runtime index would put code[] in
-  // scratch memory).
-  auto batch = [&](auto b_const) {
-    constexpr int b = decltype(b_const)::value;
-    float w[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int j = tid + kSelThreads * (b + i);
-      const int jc = j < n ? j : 0;
-      w[i] = a.w_in != nullptr ? a.w_in[ext + jc] : token_weight(a, s_coef, a_in, p_in, ramp, jc);
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int j = tid + kSelThreads * (b + i);
-      code[b + i] = 0;
-      if (j < n) {
-        nonfinite |= !isfinite(w[i]);
-        if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
-        const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
-        const double uj = philox_uniform53(x.x, x.y);
-        double key = w[i] > 0.f ? log(uj) / double(w[i]) : -INFINITY;
-        if (j < a.n_sink || j >= n - a.n_recent) key = INFINITY;
-        if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
-        code[b + i] = key_code(key);
-        v_or |= code[b + i];
-        v_and &= code[b + i];
-      }
-    }
-  };
-  static_assert(kFusedPer == 8 * kBatch, "eight batches");
-  batch(std::integral_constant<int, 0>{});
-  batch(std::integral_constant<int, kBatch>{});
-  batch(std::integral_constant<int, 2 * kBatch>{});
-  batch(std::integral_constant<int, 3 * kBatch>{});
-  batch(std::integral_constant<int, 4 * kBatch>{});
-  batch(std::integral_constant<int, 5 * kBatch>{});
-  batch(std::integral_constant<int, 6 * kBatch>{});
-  batch(std::integral_constant<int, 7 * kBatch>{});
-  if (__syncthreads_or(nonfinite) && tid == 0) raise_status(a, kStatusNonFinite);
-  if (u.keep == nullptr) return;
-  if (u.budget >= n) {
+  const bool estimate = uses_estimate(a, u);
+  if (u.keep != nullptr && u.budget >= n && a.keys_out == nullptr) {
     for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
     return;
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    v_or |= __shfl_xor(v_or, m, 64);
-    v_and &= __shfl_xor(v_and, m, 64);
-  }
-  if (lane == 0) { s_or[wave] = v_or; s_and[wave] = v_and; }
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t o = 0, an = ~0ull;
-    for (int w = 0; w < kSelWaves; ++w) { o |= s_or[w]; an &= s_and[w]; }
-    const uint64_t diff = o ^ an;
-    s_need = u.budget;
-    s_eq = n;
-    if (diff == 0) {                       // every code equal: pure ties
-      s_prefix = an;
-      s_mask = ~0ull;
-      s_done = 1;
-    } else {
-      const int top = 63 - __clzll(diff);  // highest bit that differs
-      const uint64_t above = top == 63 ? 0ull : (~0ull << (top + 1));
-      s_prefix = an & above;
-      s_mask = above;
-      s_done = 0;
-      s_start = top;
-    }
-  }
-  __syncthreads();
-
-  // MSD radix passes over the unresolved bits (at most 8, see topb_select).
-  int start = s_start;
-  while (!s_done && start >= 0) {
-    const int shift = start >= 7 ? start - 7 : 0;
-    const int width = start - shift + 1;
-    const uint32_t dmask = (1u << width) - 1u;
-    if (tid < 256) s_hist[tid] = 0;
-    __syncthreads();
-    const uint64_t prefix = s_prefix, mask = s_mask;
+  // This lane's estimate codes (written by estimate_keys_kernel).
+  uint32_t code[kFusedPer];
+  if (estimate) {
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
 #pragma unroll
     for (int i = 0; i < kFusedPer; ++i) {
       const int j = tid + kSelThreads * i;
-      if (j < n && (code[i] & mask) == prefix)
-        atomicAdd(&s_hist[uint32_t(code[i] >> shift) & dmask], 1u);
+      code[i] = j < n ? codes[j] : 0u;
     }
-    __syncthreads();
-    if (tid < 64) {
-      const uint32_t h0 = s_hist[4 * lane], h1 = s_hist[4 * lane + 1], h2 = s_hist[4 * lane + 2],
-                     h3 = s_hist[4 * lane + 3];
-      const uint32_t own = h0 + h1 + h2 + h3;
-      uint32_t suf = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(suf, off, 64);
-        if (lane + off < 64) suf += v;
-      }
-      const uint32_t higher = suf - own;
-      const uint32_t need = uint32_t(s_need);
-      if (higher < need && need <= suf) {
-        const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
-        const int bb = need <= c3 ? 3 : need <= c2 ? 2 : need <= c1 ? 1 : 0;
-        const uint32_t acc = bb == 3 ? higher : bb == 2 ? c3 : bb == 1 ? c2 : c1;
-        const uint32_t hb = bb == 3 ? h3 : bb == 2 ? h2 : bb == 1 ? h1 : h0;
-        s_need = int(need - acc);
-        s_eq = int(hb);
-        s_prefix = prefix | (uint64_t(4 * lane + bb) << shift);
-        s_mask = mask | (uint64_t(dmask) << shift);
-        s_done = (hb == need - acc) || shift == 0;
-      }
-    }
-    __syncthreads();
-    start = shift - 1;
   }
 
-  if (!s_done) {
-    if (tid == 0) raise_status(a, kStatusBadItem);
-    for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
-    return;
-  }
-  const uint64_t prefix = s_prefix, mask = s_mask;
-  const int need = s_need;
-  const bool ties = s_eq != need;
-  if (tid == 0) s_cut = 0;
-  __syncthreads();
-  const int n_rounds = (n + kSelThreads - 1) / kSelThreads;
-  if (ties) {
-    int seen = 0;
+  bool fallback = !estimate;
+  uint32_t lo = 0, hi = 0;
+  int need2 = 0, m = 0;
+  if (estimate) {
+    // Radix select on the estimate codes.
+    uint32_t v_or = 0, v_and = 0xFFFFFFFFu;
 #pragma unroll
-    for (int r = kFusedPer - 1; r >= 0; --r) {
-      if (r < n_rounds && seen < need) {
-        const int j = r * kSelThreads + tid;
-        const bool eq = j < n && (code[r] & mask) == prefix;
-        int tot;
-        const int below = block_rank(eq, s_cnt, &tot);
-        const int above = tot - below - (eq ? 1 : 0);
-        if (eq && seen + above + 1 == need) s_cut = j;
-        seen += tot;
-      }
+    for (int i = 0; i < kFusedPer; ++i)
+      if (tid + kSelThreads * i < n) { v_or |= code[i]; v_and &= code[i]; }
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      v_or |= uint32_t(__shfl_xor(int(v_or), mm, 64));
+      v_and &= uint32_t(__shfl_xor(int(v_and), mm, 64));
+    }
+    if ((tid & 63) == 0) { core.red_or[tid >> 6] = v_or; core.red_and[tid >> 6] = v_and; }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t o = 0, an = 0xFFFFFFFFull;
+      for (int w = 0; w < kSelWaves; ++w) { o |= core.red_or[w]; an &= core.red_and[w]; }
+      // The codes enter the 64-bit passes with their upper 32 bits set.
+      sel_init(core, o | 0xFFFFFFFF00000000ull, an | 0xFFFFFFFF00000000ull, n, u.budget);
+      sh.n_band = 0;
+      sh.n_above = 0;
+      sh.cb = 0xFFFFFFFFu;
     }
     __syncthreads();
+    sel_passes(core, kFusedPer, [&](int i) { return uint64_t(code[i]) | 0xFFFFFFFF00000000ull; },
+               [&](int i) { return tid + kSelThreads * i < n; });
+    if (!core.done) {
+      if (tid == 0) raise_status(a, kStatusBadItem);
+      for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+      return;
+    }
+    // The B-th largest estimate is the smallest code of the boundary bin
+    // (prefix under mask): the bin is either taken whole or fully resolved.
+    {
+      uint32_t mn = 0xFFFFFFFFu;
+      const uint64_t prefix = core.prefix, mask = core.mask;
+#pragma unroll
+      for (int i = 0; i < kFusedPer; ++i)
+        if (tid + kSelThreads * i < n && ((uint64_t(code[i]) | 0xFFFFFFFF00000000ull) & mask) == prefix)
+          mn = min(mn, code[i]);
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), mm, 64)));
+      if ((tid & 63) == 0) atomicMin(&sh.cb, mn);
+    }
+    __syncthreads();
+    const uint32_t cb = sh.cb;
+    if (cb == 0u || cb == 0xFFFFFFFFu) {
+      // Boundary in the -inf or +inf class: the estimate codes are exact
+      // there, so the band is just the boundary class, decided by index.
+      lo = hi = cb;
+    } else {
+      const float v = f32_decode(cb);   // -s of the B-th largest estimate
+      lo = min(max(f32_code(v - kBand), 1u), 0xFFFFFFFEu);
+      hi = min(max(f32_code(v + kBand), 1u), 0xFFFFFFFEu);
+    }
+    int above = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedPer; ++i) {
+      const int j = tid + kSelThreads * i;
+      if (j < n) {
+        if (code[i] > hi) {
+          ++above;
+        } else if (code[i] >= lo) {
+          const int pos = atomicAdd(&sh.n_band, 1);
+          if (pos < kBandCap) sh.band_idx[pos] = uint32_t(j);
+        }
+      }
+    }
+    for (int c = tid; c < kFusedMaxTokens / 32; c += kSelThreads) sh.chosen[c] = 0;
+    atomicAdd(&sh.n_above, above);
+    __syncthreads();
+    m = sh.n_band;
+    need2 = u.budget - sh.n_above;
+    fallback = m > kBandCap || need2 < 1 || need2 > m;
   }
-  const int cut = s_cut;
-  int base = 0;
+
+  if (fallback) {
+    // Exact keys of every token into the workspace, then the global selection.
+    uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
+    uint64_t o = 0, an = ~0ull;
+    for (int j = tid; j < n; j += kSelThreads) {
+      const double key = exact_key(a, u, j, ws(a, sh.coef, j), k0, k1);
+      if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
+      const uint64_t c = key_code(key);
+      keys[j] = c;
+      o |= c;
+      an &= c;
+    }
+    if (u.keep == nullptr) return;
+    if (u.budget >= n) {
+      for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+      return;
+    }
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      o |= __shfl_xor(o, mm, 64);
+      an &= __shfl_xor(an, mm, 64);
+    }
+    if ((tid & 63) == 0) { core.red_or[tid >> 6] = o; core.red_and[tid >> 6] = an; }
+    __syncthreads();
+    uint64_t ob = 0, anb = ~0ull;
+    for (int w = 0; w < kSelWaves; ++w) { ob |= core.red_or[w]; anb &= core.red_and[w]; }
+    __syncthreads();
+    select_global(a, u, keys, ob, anb, core);
+    return;
+  }
+
+  // Exact keys of the band, one list entry per lane, then the exact order
+  // inside the band ((code, index) descending): the first need2 win.
+  for (int t = tid; t < m; t += kSelThreads) {
+    const int j = int(sh.band_idx[t]);
+    sh.band_code[t] = key_code(exact_key(a, u, j, ws(a, sh.coef, j), k0, k1));
+  }
+  __syncthreads();
+  for (int t = tid; t < m; t += kSelThreads) {
+    const uint64_t ct = sh.band_code[t];
+    const uint32_t it = sh.band_idx[t];
+    int rank = 0;
+    for (int q = 0; q < m; ++q) {
+      const uint64_t cq = sh.band_code[q];
+      rank += (cq > ct || (cq == ct && sh.band_idx[q] > it)) ? 1 : 0;
+    }
+    if (rank < need2) atomicOr(&sh.chosen[it >> 5], 1u << (it & 31));
+  }
+  __syncthreads();
+  // Ascending write in one pass: bit r of kmask keeps token r * 1024 + tid;
+  // per (round, wave) counts, one exclusive scan over them in token order.
+  uint32_t kmask = 0;
 #pragma unroll
   for (int r = 0; r < kFusedPer; ++r) {
-    if (r < n_rounds) {
-      const int j = r * kSelThreads + tid;
-      bool keep = false;
-      if (j < n) {
-        const uint64_t top = code[r] & mask;
-        keep = top > prefix || (top == prefix && (!ties || j >= cut));
-      }
-      int tot;
-      const int pos = block_rank(keep, s_cnt, &tot);
-      if (keep && base + pos < u.budget) u.keep[base + pos] = j;
-      base += tot;
+    const int j = r * kSelThreads + tid;
+    if (j < n && (code[r] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u))) kmask |= 1u << r;
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below_lane = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < kFusedPer; ++r) {
+    const uint64_t bal = __ballot((kmask >> r) & 1u);
+    if (lane == 0) sh.round_cnt[r * kSelWaves + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // 512 counts in (round, wave) order, eight per lane: exclusive scan.
+    constexpr int kPerLane = kFusedPer * kSelWaves / 64;
+    int loc[kPerLane], sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += sh.round_cnt[lane * kPerLane + q]; }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    const int excl = incl - sum;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) sh.round_cnt[lane * kPerLane + q] = excl + loc[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kFusedPer; ++r) {
+    const uint64_t bal = __ballot((kmask >> r) & 1u);
+    if ((kmask >> r) & 1u) {
+      const int pos = sh.round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
+      if (pos < u.budget) u.keep[pos] = r * kSelThreads + tid;
     }
   }
 }
@@ -526,6 +713,11 @@ hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
 
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL(reservoir_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(estimate_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
   return hipGetLastError();
 }
 

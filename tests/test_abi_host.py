@@ -89,7 +89,8 @@ def test_status_strings(lib):
     assert lib.nx_stage_name(3) == b"walk_coef"
     assert lib.nx_stage_name(6) == b"kv_compact"
     assert lib.nx_stage_name(7) == b"sample_select"
-    assert lib.nx_stage_name(8) == b"unknown"
+    assert lib.nx_stage_name(8) == b"estimate_keys"
+    assert lib.nx_stage_name(9) == b"unknown"
 
 
 def test_workspace_query(lib):

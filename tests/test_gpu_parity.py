@@ -83,6 +83,53 @@ def test_reservoir_select_bitexact_on_given_weights(n, budget, sink, recent):
         assert gc.overlap_fraction(got, ref_keep[h]) >= 1 - 2.0 / kept
 
 
+def _weights(kind, h_kv, n, gen):
+    """Weight rows that stress the order estimate of the fused select."""
+    u = torch.rand(h_kv, n, generator=gen, dtype=torch.float64)
+    if kind == "cubic":
+        w = u ** 3 / n
+    elif kind == "zeros_negative":
+        w = u / n
+        w[:, ::7] = 0.0
+        w[:, 3::11] = -1.0
+    elif kind == "subnormal":
+        w = u / n
+        w[:, ::5] = 1e-40 * (1 + u[:, ::5])
+        w[:, 1::13] = 1e-44
+    elif kind == "wide_range":
+        w = 10.0 ** (-30 * u)
+    elif kind == "equal":
+        w = torch.full((h_kv, n), 1.0 / n, dtype=torch.float64)
+    else:
+        raise ValueError(kind)
+    return w.float()
+
+
+@pytest.mark.parametrize("kind", ["cubic", "zeros_negative", "subnormal", "wide_range", "equal"])
+@pytest.mark.parametrize("n,budget,sink,recent", [
+    (32768, 6554, 0, 0), (20001, 1, 0, 0), (5000, 4999, 0, 0), (9000, 3000, 7, 9), (1000, 250, 0, 0),
+])
+def test_estimate_select_equals_exact_select(kind, n, budget, sink, recent):
+    """Without a key export the fused kernel ranks tokens by an fp32 estimate and
+    computes fp64 keys only near the boundary; with the export every key is
+    exact.  Both must keep exactly the same tokens."""
+    h_kv = 8
+    cfg = _cfg(8, h_kv, 128, 8, n_sink=sink, n_recent=recent)
+    ws = _ws(cfg, n, walk=0)
+    gen = torch.Generator(device="cpu").manual_seed(zlib.crc32(f"{kind}/{n}/{budget}".encode()))
+    w = _weights(kind, h_kv, n, gen)
+    wd = w.to(DEV)
+    for step in range(3):
+        fast, _ = nx.nx_reservoir_select(cfg, wd, budget, 77, workspace=ws, layer=2, step=step)
+        exact, keys = nx.nx_reservoir_select(cfg, wd, budget, 77, workspace=ws, layer=2, step=step,
+                                             with_keys=True)
+        nx.nx_read_device_status(cfg, ws)
+        assert torch.equal(fast, exact), (kind, step)
+        k = keys.cpu().numpy()
+        for h in range(h_kv):
+            np.testing.assert_array_equal(exact[h].cpu().numpy(), nexus.select_top(k[h], budget))
+
+
 @pytest.mark.parametrize("n", [3000, 40000])
 def test_reservoir_select_ties_and_nonpositive_weights(n):
     """Many -inf keys (w <= 0) and duplicates: ties go to the larger index.
