@@ -129,10 +129,14 @@ def head_weights(q_grp, k, walk_iters, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT):
 # ------------------------------------------------------- reservoir select ----
 
 def reservoir_keys(w, u, n_sink=0, n_recent=0):
-    """A-Res keys for one KV head; [Nexus] section 2.3, Eq. (6) with n = 1.
+    """Reservoir keys for one KV head; [Nexus] section 2.3, Eq. (6).
 
-    Ranking by u^(1/w) equals ranking by ln(u)/w (ln is increasing), computed
-    here in fp64.  w <= 0 gives -inf.  The forced sink / recency positions
+    u: [N] (one draw per token, n = 1) or [N, n].  The priority is
+    pi_j = (1/n) sum_i u_ji^(1/w_j); the key is ln(pi_j), which orders the
+    tokens the same way.  For n = 1 that is ln(u)/w (A-Res).  For n > 1 the
+    sum is taken in the log domain, ln pi = logsumexp_i(ln(u_ji)/w_j) - ln n,
+    because u^(1/w) underflows fp64 for the small weights of long caches.
+    All in fp64.  w <= 0 gives -inf; the forced sink / recency positions
     (section 2.3) get +inf so that they always survive.
     """
     w = np.asarray(w, dtype=np.float64)
@@ -142,12 +146,51 @@ def reservoir_keys(w, u, n_sink=0, n_recent=0):
     n = w.shape[-1]
     pos = w > 0
     keys = np.full(n, -np.inf)
-    keys[pos] = np.log(u[pos]) / w[pos]
+    if u.ndim == 1:
+        keys[pos] = np.log(u[pos]) / w[pos]
+    else:
+        t = np.log(u[pos]) / w[pos][:, None]          # ln(u_ji^(1/w_j))
+        m = t.max(axis=1)
+        keys[pos] = m + np.log(np.exp(t - m[:, None]).sum(axis=1)) - np.log(u.shape[1])
     if n_sink:
         keys[:n_sink] = np.inf
     if n_recent:
         keys[n - n_recent:] = np.inf
     return keys
+
+
+def topk_keys(w, n_sink=0, n_recent=0):
+    """Keys of the deterministic limit n -> infinity of Eq. (6).
+
+    [Nexus] appendix 8.2: the n-averaged priority tends to E[u^(1/w)] =
+    w/(w+1), increasing in w, so the limit ranks by w itself: key = w (w > 0),
+    -inf otherwise, +inf at the forced positions.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite Nexus weight")
+    n = w.shape[-1]
+    keys = np.where(w > 0, w, -np.inf)
+    if n_sink:
+        keys[:n_sink] = np.inf
+    if n_recent:
+        keys[n - n_recent:] = np.inf
+    return keys
+
+
+def head_keys(w, n_tokens, unit_id, layer, step, seed, n_avg, n_sink=0, n_recent=0):
+    """Keys of one KV head for averaging count n_avg: 0 or 1 -> n = 1,
+    n >= 2 -> n draws, -1 -> the deterministic limit (top-B by w)."""
+    if n_avg == -1:
+        return topk_keys(w, n_sink, n_recent)
+    if n_avg in (0, 1):
+        u = unit_uniforms(n_tokens, unit_id, layer, step, seed)
+    elif n_avg >= 2:
+        j = np.arange(n_tokens, dtype=np.uint64)
+        u = philox.uniforms_n(j, unit_id, layer, step, seed, n_avg)
+    else:
+        raise ValueError("n_avg must be -1, 0 or >= 1")
+    return reservoir_keys(w, u, n_sink, n_recent)
 
 
 def select_top(keys, budget):
@@ -174,14 +217,15 @@ def unit_uniforms(n_tokens, unit_id, layer, step, seed):
 
 def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
                step=0, seq_id=0, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT,
-               n_sink=0, n_recent=0, heads=None):
+               n_sink=0, n_recent=0, heads=None, n_avg=1):
     """One eviction event for one (sequence, layer): every KV head.
 
     [Nexus] section 2.1 (streaming view): keep `budget` of the N resident
     positions per KV head and continue with the kept K and V rows.
     q: [H_q, W, D]; k, v: [H_kv, N, D] (raw bf16 bits when dtype == 'bf16').
     Query head g reads KV head g // G.  `heads` restricts the work to a
-    subset of KV heads (results for the others are left out).
+    subset of KV heads (results for the others are left out).  n_avg: the
+    priority averaging count of Eq. (6), see head_keys.
     Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v.
     """
     q = np.asarray(q)
@@ -202,8 +246,8 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
         q_grp = as_f64(q[h * g:(h + 1) * g], dtype)
         kh = as_f64(k[h], dtype)
         sc = head_weights(q_grp, kh, walk_iters, lam, eps)
-        u = unit_uniforms(n, seq_id * h_kv + h, layer, step, seed)
-        keys = reservoir_keys(sc["w"], u, n_sink, n_recent)
+        keys = head_keys(sc["w"], n, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
+                         n_recent)
         keep = select_top(keys, budget)
         out["w"][h] = sc["w"]
         out["keys"][h] = keys
@@ -214,7 +258,7 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
 
 
 def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
-                        n_sink=0, n_recent=0):
+                        n_sink=0, n_recent=0, n_avg=1):
     """Reservoir selection on given weights w: [H_kv, N] (any precision).
 
     The oracle run on someone else's scores: same Philox stream, fp64 keys,
@@ -225,7 +269,7 @@ def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
     keys = np.empty((h_kv, n))
     keeps = []
     for h in range(h_kv):
-        u = unit_uniforms(n, seq_id * h_kv + h, layer, step, seed)
-        keys[h] = reservoir_keys(w[h], u, n_sink, n_recent)
+        keys[h] = head_keys(w[h], n, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
+                            n_recent)
         keeps.append(select_top(keys[h], budget))
     return keys, keeps

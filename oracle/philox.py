@@ -16,6 +16,11 @@ this implementation's reading:
     counter = (token j, seq * H_kv + kv_head, layer, step), key = (seed lo, seed hi)
     u = (((x0 << 32) | x1) >> 11) + 1) * 2^-53  in (0, 1], exact in fp64.
 
+For the n-averaged priority of [Nexus] section 2.3 (Eq. 6) a token needs n
+draws: draws 2c and 2c + 1 come from block c, the same counter under key
+(seed lo, seed hi + c mod 2^32), built from words (x0, x1) and (x2, x3).
+Draw 0 is the single-draw uniform above.
+
 Pins (tests/test_oracle_philox.py): bit-exact agreement with the independent
 Philox4x32-10 engine in ROCm's rocRAND headers (compiled for the host, called
 only by the test) on > 1e6 counters, plus uniformity (KS) and counter
@@ -57,6 +62,24 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
             ka = (ka + W0) & MASK32
             kb = (kb + W1) & MASK32
     return x0, x1, x2, x3
+
+
+def _u53(hi, lo):
+    k53 = ((hi << np.uint64(32)) | lo) >> np.uint64(11)
+    # k53 + 1 <= 2^53 is exactly representable, and so is the scaled result.
+    return (k53 + np.uint64(1)).astype(np.float64) * (2.0 ** -53)
+
+
+def uniforms_n(token, unit_id, layer, step, seed, n):
+    """n draws per counter (Eq. 6): array of shape broadcast(...) + (n,)."""
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    draws = []
+    for c in range((n + 1) // 2):
+        x0, x1, x2, x3 = philox4x32_10(token, unit_id, layer, step, seed & 0xFFFFFFFF,
+                                       ((seed >> 32) + c) & 0xFFFFFFFF)
+        draws.append(_u53(x0, x1))
+        draws.append(_u53(x2, x3))
+    return np.stack(draws[:n], axis=-1)
 
 
 def uniforms(token, unit_id, layer, step, seed):

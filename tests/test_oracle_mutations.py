@@ -163,3 +163,46 @@ def test_philox_pin_catches_missing_key_bump(monkeypatch, rocrand_bin):  # noqa:
 
     monkeypatch.setattr(philox, "philox4x32_10", no_bump)
     assert _fails(ppins.test_matches_rocrand_on_the_token_counter_layout, rocrand_bin)
+
+
+# --------------------------------------------------- n-averaged priority ----
+
+from tests import test_oracle_navg as npins  # noqa: E402
+
+_real_reservoir_keys = nexus.reservoir_keys
+_real_uniforms_n = philox.uniforms_n
+
+
+def _keys_without_log_n(w, u, n_sink=0, n_recent=0):
+    """Slip: the 1/n of Eq. (6) dropped (ln pi off by ln n)."""
+    keys = _real_reservoir_keys(w, u, n_sink, n_recent)
+    u = np.asarray(u)
+    return keys + (np.log(u.shape[1]) if u.ndim == 2 else 0.0)
+
+
+def _keys_geometric_mean(w, u, n_sink=0, n_recent=0):
+    """Slip: averaging the logs, (1/n) sum ln(u)/w, instead of the log of the average."""
+    u = np.asarray(u, dtype=np.float64)
+    if u.ndim == 1:
+        return _real_reservoir_keys(w, u, n_sink, n_recent)
+    return _real_reservoir_keys(w, np.exp(np.log(u).mean(axis=1)), n_sink, n_recent)
+
+
+def _uniforms_n_one_block(token, unit_id, layer, step, seed, n):
+    """Slip: every pair of draws from the same Philox block (no per-block key)."""
+    one = _real_uniforms_n(token, unit_id, layer, step, seed, 2)
+    return np.concatenate([one] * ((n + 1) // 2), axis=-1)[..., :n]
+
+
+@pytest.mark.parametrize("slip, pin, args", [
+    (_keys_without_log_n, npins.test_priority_is_unbiased_with_variance_over_n, (0.5, 5)),
+    (_keys_geometric_mean, npins.test_priority_is_unbiased_with_variance_over_n, (0.5, 5)),
+])
+def test_navg_key_slips_are_caught(monkeypatch, slip, pin, args):
+    monkeypatch.setattr(nexus, "reservoir_keys", slip)
+    assert _fails(pin, *args)
+
+
+def test_navg_shared_block_slip_is_caught(monkeypatch):
+    monkeypatch.setattr(philox, "uniforms_n", _uniforms_n_one_block)
+    assert _fails(npins.test_draws_come_from_independent_blocks)
