@@ -94,7 +94,7 @@ def build_batch(wl, device):
     return dict(q=q, k=k, v=v, keep=keep, out_k=out_k, out_v=out_v, units=units)
 
 
-def cpu_baseline(wl, data, budget_s):
+def cpu_baseline(wl, data, budget_s, n_avg=1):
     """The fp64 oracle, whole KV heads in layer order, until ~budget_s seconds pass."""
     from oracle import nexus
     try:
@@ -108,7 +108,8 @@ def cpu_baseline(wl, data, budget_s):
         q = bf16_bits(data["q"][layer, h * wl.group:(h + 1) * wl.group])
         k = bf16_bits(data["k"][layer, h:h + 1])
         v = bf16_bits(data["v"][layer, h:h + 1])
-        nexus.evict_step(q, k, v, wl.budget, wl.walk_iters, 0, dtype="bf16", layer=layer)
+        nexus.evict_step(q, k, v, wl.budget, wl.walk_iters, 0, dtype="bf16", layer=layer,
+                         n_avg=n_avg)
         heads_done += 1
     dt = time.perf_counter() - t0
     return {"value": round(heads_done * wl.n_tokens / dt, 1), "unit": "KV tokens/s",
@@ -125,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-avg", type=int, default=1,
+                    help="priority averaging count of Eq. 6 (1: A-Res key; -1: top-B by weight)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1-GiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -149,7 +152,8 @@ def main():
 
     wl = WORKLOADS["llama3_8b_stream32"]
     data = build_batch(wl, dev)
-    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16)
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
+                         n_avg=args.n_avg)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -211,7 +215,8 @@ def main():
         "config": {"workload": "llama3_8b_stream32 eviction event at N=32768 (32 layers x 8 KV "
                                "heads, GQA 32:8, head_dim 128, W=32, H=3, B=6554)",
                    "layers": wl.n_layers, "kv_heads": wl.h_kv, "n_tokens": wl.n_tokens,
-                   "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters},
+                   "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters,
+                   "n_avg": args.n_avg},
         "step_latency_ms": round(ms_per_step, 4),
         "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},
         "score_probs_mfma_tflops": round(qk_flops / (per_launch["score_probs"][0] * 1e-3) / 1e12, 1),
@@ -225,7 +230,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg)
     print(json.dumps(out))
 
 

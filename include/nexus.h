@@ -84,7 +84,17 @@ typedef struct nx_desc {
                                before first use and not modified by the caller afterwards */
   size_t workspace_bytes;
   void* stream;             /* hipStream_t */
+  int32_t n_avg;            /* priority averaging count n of section 2.3 Eq. 6:
+                               0 or 1: one draw per token, the key ln(u)/w (A-Res);
+                               2 .. NX_MAX_AVG: pi = (1/n) sum_i u_i^(1/w), key ln(pi);
+                               NX_TOPK (-1): the deterministic n -> infinity limit of
+                               appendix 8.2, the B largest weights (key w);
+                               anything else: NX_EINVAL */
+  int32_t reserved;         /* must be 0 */
 } nx_desc;
+
+#define NX_MAX_AVG 64
+#define NX_TOPK (-1)
 
 /*
  * One (sequence, layer) item of a batched eviction event.  An array of these

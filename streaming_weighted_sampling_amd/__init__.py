@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     NX_BF16, NX_F32, NxDesc, NxUnit, NexusError, LIB_PATH, load, status_str,
 )
 from .api import (  # noqa: F401
-    NexusConfig, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,
+    NexusConfig, TOPK, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,
     nx_reservoir_select, nx_kv_compact, make_units, nx_evict_batch, nx_read_device_status,
     profile_enable, profile_read,
 )

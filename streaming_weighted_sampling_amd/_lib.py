@@ -37,6 +37,8 @@ class NxDesc(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("n_avg", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

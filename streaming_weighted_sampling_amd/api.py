@@ -16,6 +16,9 @@ from ._lib import NX_BF16, NX_F32, NxDesc, NxUnit, check, load
 _DTYPES = {torch.bfloat16: NX_BF16, torch.float32: NX_F32}
 
 
+TOPK = -1                     # n_avg value of the deterministic top-B-by-weight limit
+
+
 @dataclass
 class NexusConfig:
     """Shape and parameters shared by the calls of one eviction event."""
@@ -28,6 +31,7 @@ class NexusConfig:
     eps_tie: float = 1e-6     # [Nexus] section 5.1 tie-break magnitude
     n_sink: int = 0
     n_recent: int = 0
+    n_avg: int = 1            # [Nexus] Eq. 6 averaging count; TOPK (-1) = deterministic limit
 
     def desc(self, workspace=None, *, layer=0, step=0, seq_id=0, kv_head_stride=0,
              out_head_stride=0, max_out_rows=0, stream=None):
@@ -41,6 +45,7 @@ class NexusConfig:
         d.eps_tie = self.eps_tie
         d.n_sink = self.n_sink
         d.n_recent = self.n_recent
+        d.n_avg = self.n_avg
         d.layer = layer
         d.step = step
         d.seq_id = seq_id

@@ -26,6 +26,8 @@ nx_status check_desc(const nx_desc* d) {
     return NX_EINVAL;
   if (d->window < 1 || d->n_sink < 0 || d->n_recent < 0) return NX_EINVAL;
   if (!std::isfinite(d->lambda) || !std::isfinite(d->eps_tie)) return NX_EINVAL;
+  if (d->n_avg != NX_TOPK && (d->n_avg < 0 || d->n_avg > NX_MAX_AVG)) return NX_EINVAL;
+  if (d->reserved != 0) return NX_EINVAL;
   if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return NX_EUNSUPPORTED;
   return NX_OK;
@@ -103,6 +105,7 @@ Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
   a.n_recent = d->n_recent;
   a.step = d->step;
   a.seed = seed;
+  a.n_avg = d->n_avg == 0 ? 1 : d->n_avg;
   return a;
 }
 
@@ -147,10 +150,10 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 // Enqueue stages [first, last] in order.
 // Items of up to kFusedMaxTokens tokens select on estimate codes held in the
 // select kernel's registers (estimate_keys + sample_select) when the call goes
-// on to selection (not the weights-only export).
+// on to selection (not the weights-only export) with one draw per token.
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   hipError_t err = hipSuccess;
-  const bool fused = a.g.max_tokens <= kFusedMaxTokens && !a.stop_after_weights &&
+  const bool fused = a.g.max_tokens <= kFusedMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {

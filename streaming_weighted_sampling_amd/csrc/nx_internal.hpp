@@ -94,6 +94,7 @@ struct Args {
   float lambda, eps_tie, c_log2;   // c_log2 = log2(e) / sqrt(D)
   int32_t n_sink, n_recent;
   uint32_t step;
+  int32_t n_avg;   // 1, 2 .. NX_MAX_AVG draws, or NX_TOPK
   uint64_t seed;
   // workspace
   uint32_t* status;

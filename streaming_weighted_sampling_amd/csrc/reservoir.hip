@@ -80,6 +80,48 @@ __global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
   }
 }
 
+// The fp64 key of token j with weight w (section 2.3 Eq. 6).  n = 1: ln(u)/w
+// (A-Res).  n >= 2: ln(pi), pi = (1/n) sum_i u_i^(1/w), by an online
+// log-sum-exp of t_i = ln(u_i)/w (u^(1/w) underflows for small w); draws 2c
+// and 2c + 1 come from Philox block c, the token's counter under key
+// (seed lo, seed hi + c), words (x, y) and (z, w).  NX_TOPK: the key is w
+// itself (the n -> infinity limit ranks by w/(w+1), appendix 8.2).  w <= 0
+// gives -inf, a forced slot +inf.
+__device__ inline double token_key(const Args& a, const HeadUnit& u, int j, float w, uint32_t k0,
+                                   uint32_t k1) {
+  double key;
+  if (!(w > 0.f)) {
+    key = -INFINITY;
+  } else if (a.n_avg == NX_TOPK) {
+    key = double(w);
+  } else if (a.n_avg <= 1) {
+    const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
+    key = log(philox_uniform53(x.x, x.y)) / double(w);
+  } else {
+    const double rw = 1.0 / double(w);
+    double m = -INFINITY, sum = 0.0;
+    for (int c = 0; 2 * c < a.n_avg; ++c) {
+      const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0,
+                                    k1 + uint32_t(c));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (2 * c + h < a.n_avg) {
+          const double t = log(h == 0 ? philox_uniform53(x.x, x.y) : philox_uniform53(x.z, x.w)) * rw;
+          if (t > m) {
+            sum = sum * exp(m - t) + 1.0;
+            m = t;
+          } else {
+            sum += exp(t - m);
+          }
+        }
+      }
+    }
+    key = m + log(sum) - log(double(a.n_avg));
+  }
+  if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
+  return key;
+}
+
 __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args a) {
   const Geometry& g = a.g;
   const int hu = blockIdx.y, chunk = blockIdx.x;
@@ -130,10 +172,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     nonfinite |= !isfinite(w[i]);
     if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
     if (a.stop_after_weights) continue;
-    const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
-    const double uj = philox_uniform53(x.x, x.y);
-    double key = w[i] > 0.f ? log(uj) / double(w[i]) : -INFINITY;
-    if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
+    const double key = token_key(a, u, j, w[i], k0, k1);
     if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
     const uint64_t code = key_code(key);
     keys[j] = code;
@@ -433,11 +472,7 @@ __device__ inline uint32_t estimate_code(uint32_t x0, uint32_t x1, float w, bool
 __device__ __attribute__((always_inline)) inline double exact_key(const Args& a, const HeadUnit& u,
                                                                   int j, float w, uint32_t k0,
                                                                   uint32_t k1) {
-  const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
-  const double uj = philox_uniform53(x.x, x.y);
-  double key = w > 0.f ? log(uj) / double(w) : -INFINITY;
-  if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
-  return key;
+  return token_key(a, u, j, w, k0, k1);
 }
 
 // f(integral_constant<int, i>) for i = B .. E-1, expanded at compile time, so

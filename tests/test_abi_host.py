@@ -51,7 +51,7 @@ def test_struct_layout_matches_c(tmp_path):
 int main(void) {
   printf("nx_desc %zu\nnx_unit %zu\n", sizeof(nx_desc), sizeof(nx_unit));
   F(nx_desc, max_out_rows); F(nx_desc, kv_head_stride); F(nx_desc, workspace);
-  F(nx_desc, stream); F(nx_unit, app_v); F(nx_unit, kv_head_stride); F(nx_unit, n_tokens);
+  F(nx_desc, stream); F(nx_desc, n_avg); F(nx_unit, app_v); F(nx_unit, kv_head_stride); F(nx_unit, n_tokens);
   F(nx_unit, seq_id);
   return 0;
 }''')
@@ -66,6 +66,7 @@ int main(void) {
     assert int(out["nx_desc.kv_head_stride"]) == NxDesc.kv_head_stride.offset
     assert int(out["nx_desc.workspace"]) == NxDesc.workspace.offset
     assert int(out["nx_desc.stream"]) == NxDesc.stream.offset
+    assert int(out["nx_desc.n_avg"]) == NxDesc.n_avg.offset
     assert int(out["nx_unit.app_v"]) == NxUnit.app_v.offset
     assert int(out["nx_unit.kv_head_stride"]) == NxUnit.kv_head_stride.offset
     assert int(out["nx_unit.n_tokens"]) == NxUnit.n_tokens.offset

@@ -202,6 +202,74 @@ def test_fused_and_two_kernel_selection_agree(n):
     assert torch.equal(outs[0][2].view(torch.int16), outs[1][2].view(torch.int16))
 
 
+# ------------------------------------------ n-averaged priority (Eq. 6) --
+
+
+@pytest.mark.parametrize("n_avg", [2, 5, 64, nx.TOPK])
+@pytest.mark.parametrize("n,budget,sink,recent", [
+    (4097, 819, 0, 0), (32768, 6554, 0, 0), (40000, 8000, 3, 5), (50, 7, 0, 0),
+])
+def test_averaged_priority_on_given_weights(n_avg, n, budget, sink, recent):
+    """Keys of Eq. (6) with n draws (and its top-B-by-weight limit) against the
+    oracle; the selection is exactly the oracle's selection on the GPU's keys."""
+    h_kv = 4
+    cfg = _cfg(8, h_kv, 128, 8, n_sink=sink, n_recent=recent, n_avg=n_avg)
+    ws = _ws(cfg, n, walk=0)
+    g = torch.Generator(device="cpu").manual_seed(zlib.crc32(f"navg/{n_avg}/{n}".encode()))
+    w = (torch.rand(h_kv, n, generator=g) ** 3 / n).float()
+    w[:, ::17] = 0.0
+    keep, keys = nx.nx_reservoir_select(cfg, w.to(DEV), budget, 31, workspace=ws, layer=3,
+                                        step=4, seq_id=2, with_keys=True)
+    nx.nx_read_device_status(cfg, ws)
+    keep, keys = keep.cpu().numpy(), keys.cpu().numpy()
+    ref_keys, ref_keep = nexus.select_from_weights(w.numpy(), budget, 31, layer=3, step=4,
+                                                   seq_id=2, n_sink=sink, n_recent=recent,
+                                                   n_avg=n_avg)
+    kept = min(budget, n)
+    for h in range(h_kv):
+        if n_avg == nx.TOPK:
+            np.testing.assert_array_equal(keys[h], ref_keys[h])
+        else:
+            # device log / exp against glibc: a few ulp after the log-sum-exp
+            np.testing.assert_array_max_ulp(keys[h], ref_keys[h], maxulp=16)
+        got = gc.check_keep_valid(keep[h], n, budget)
+        np.testing.assert_array_equal(got, nexus.select_top(keys[h], budget))
+        assert gc.overlap_fraction(got, ref_keep[h]) >= 1 - 2.0 / kept
+
+
+@pytest.mark.parametrize("n_avg", [5, nx.TOPK])
+def test_averaged_priority_end_to_end(n_avg):
+    """One event of the llama3 8B layer workload with Eq. (6) at n = 5 and with
+    the deterministic limit, through the batched path."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, n_avg=n_avg)
+    d = gen_layer(wl, device=DEV)
+    n, B = wl.n_tokens, wl.budget
+    keep = torch.full((wl.h_kv, B), -1, dtype=torch.int32, device=DEV)
+    ok = torch.empty(wl.h_kv, B, wl.head_dim, dtype=torch.bfloat16, device=DEV)
+    ov = torch.empty_like(ok)
+    units = nx.make_units([dict(q=d["q"], k=d["k"], v=d["v"], keep=keep, out_k=ok, out_v=ov,
+                                kv_head_stride=n * wl.head_dim, out_head_stride=B * wl.head_dim,
+                                n_tokens=n, budget=B, layer=4)], device=DEV)
+    ws = _ws(cfg, n, 1, wl.walk_iters)
+    nx.nx_evict_batch(cfg, units, 1, n, wl.walk_iters, 9, workspace=ws, step=6, max_out_rows=B)
+    nx.nx_read_device_status(cfg, ws)
+    ws1 = _ws(cfg, n, 1, wl.walk_iters)
+    w_gpu = nx.nx_nexus_weights(cfg, d["q"], d["k"], n, wl.walk_iters, workspace=ws1).cpu().numpy()
+    qh, dt = gc.host(d["q"])
+    kh, _ = gc.host(d["k"])
+    vh, _ = gc.host(d["v"])
+    ref = nexus.evict_step(qh, kh, vh, B, wl.walk_iters, 9, dtype=dt, layer=4, step=6,
+                           n_avg=n_avg)
+    _, on_gpu_w = nexus.select_from_weights(w_gpu, B, 9, layer=4, step=6, n_avg=n_avg)
+    for h in range(wl.h_kv):
+        got = gc.check_keep_valid(keep[h].cpu().numpy(), n, B)
+        np.testing.assert_array_equal(got, on_gpu_w[h])
+        assert gc.overlap_fraction(got, ref["keep"][h]) >= 0.999
+        assert gc.rows_equal(ok[h], d["k"][h], got)
+        assert gc.rows_equal(ov[h], d["v"][h], got)
+
+
 # --------------------------------------------------------------- compaction --
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
