@@ -6,8 +6,12 @@ says which passage.  No blocking, fusion or reordering beyond the definitions:
 one BLAS matmul for the logits, then elementwise numpy.
 
 Readings of passages the pages leave open (each also listed in the design doc):
-  granularity  tokens, i.e. block size b = 1, so BlockSum_b and rownorm of
-               section 2.1 Eq. (1) are identities on softmax rows.
+  granularity  tokens by default, i.e. block size b = 1, so BlockSum_b and
+               rownorm of section 2.1 Eq. (1) are identities on softmax rows;
+               block = b > 1 scores, samples and keeps blocks of b tokens
+               (the last block may be shorter), with the budget, the forced
+               slots and the kept indices counted in blocks and the block
+               index as the token word of the Philox counter.
   GQA          "head-averaged representations" (section 2.1): for KV head h the
                softmax rows of its G query heads h*G .. h*G+G-1 are averaged,
                per window row, in probability space.
@@ -15,7 +19,8 @@ Readings of passages the pages leave open (each also listed in the design doc):
                rows W-H .. W-1, oldest first; H = 0 gives c~ = 0.
   ramp         Eq. (5) r_j = j/(N-1) with 0-based j (0 oldest, 1 newest);
                r = 0 when N = 1.
-  n            Eq. (6) with n = 1; its ordering equals the A-Res key ln(u)/w.
+  n            Eq. (6) with n = 1 by default, its ordering that of the A-Res
+               key ln(u)/w; n > 1 and the n -> infinity limit in head_keys.
   ties         equal keys: the larger (newer) index wins.
   w <= 0       key -inf (kept only when needed to fill B); non-finite w is an
                error.
@@ -77,6 +82,22 @@ def window_rows(q_grp, k):
     return p.mean(axis=0)
 
 
+def block_rows(P, block):
+    """[Nexus] section 2.1, Eq. (1) at block size b: rownorm(BlockSum_b(rows)).
+
+    Block k holds tokens k*b .. min((k+1)*b, N) - 1 (N_k = ceil(N / b) blocks,
+    the last one possibly shorter); each row is then divided by its sum.
+    P: [W, N] -> [W, N_k].  b = 1 returns the rows renormalised only.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    W, N = P.shape
+    nk = -(-N // block)
+    pad = np.zeros((W, nk * block))
+    pad[:, :N] = P
+    S = pad.reshape(W, nk, block).sum(axis=2)
+    return S / S.sum(axis=1, keepdims=True)
+
+
 def direct_score(P):
     """[Nexus] section 2.2, Eq. (3): a = (1/W) sum_q a^(q), the uniform row average."""
     return np.asarray(P, dtype=np.float64).mean(axis=0)
@@ -116,9 +137,12 @@ def recency_weights(s, eps=EPS_TIE_DEFAULT):
     return s + eps * r
 
 
-def head_weights(q_grp, k, walk_iters, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT):
-    """All scoring stages for one KV head; returns a dict of the intermediates."""
+def head_weights(q_grp, k, walk_iters, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT, block=1):
+    """All scoring stages for one KV head; returns a dict of the intermediates.
+    block > 1 scores blocks of that many tokens (Eq. 1's BlockSum_b, rownorm)."""
     P = window_rows(q_grp, k)
+    if block > 1:
+        P = block_rows(P, block)
     a = direct_score(P)
     c = nexus_walk(P, walk_iters)
     s = nexus_score(a, c, lam)
@@ -217,7 +241,7 @@ def unit_uniforms(n_tokens, unit_id, layer, step, seed):
 
 def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
                step=0, seq_id=0, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT,
-               n_sink=0, n_recent=0, heads=None, n_avg=1):
+               n_sink=0, n_recent=0, heads=None, n_avg=1, block=1):
     """One eviction event for one (sequence, layer): every KV head.
 
     [Nexus] section 2.1 (streaming view): keep `budget` of the N resident
@@ -225,7 +249,10 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
     q: [H_q, W, D]; k, v: [H_kv, N, D] (raw bf16 bits when dtype == 'bf16').
     Query head g reads KV head g // G.  `heads` restricts the work to a
     subset of KV heads (results for the others are left out).  n_avg: the
-    priority averaging count of Eq. (6), see head_keys.
+    priority averaging count of Eq. (6), see head_keys.  block = b > 1: the
+    units scored, sampled and kept are blocks of b tokens (section 2.1); then
+    budget, n_sink and n_recent count blocks, keep holds block indices, and
+    out_k / out_v are the rows of the kept blocks in ascending block order.
     Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v.
     """
     q = np.asarray(q)
@@ -239,21 +266,25 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
         raise ValueError("budget and n_tokens must be >= 1")
     if n_sink + n_recent > budget:
         raise ValueError("forced slots exceed the budget")
+    if block < 1:
+        raise ValueError("block must be >= 1")
     g = h_q // h_kv
     heads = range(h_kv) if heads is None else heads
     out = {"w": {}, "keys": {}, "keep": {}, "out_k": {}, "out_v": {}}
     for h in heads:
         q_grp = as_f64(q[h * g:(h + 1) * g], dtype)
         kh = as_f64(k[h], dtype)
-        sc = head_weights(q_grp, kh, walk_iters, lam, eps)
-        keys = head_keys(sc["w"], n, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
+        sc = head_weights(q_grp, kh, walk_iters, lam, eps, block)
+        nu = sc["w"].shape[-1]
+        keys = head_keys(sc["w"], nu, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
                          n_recent)
         keep = select_top(keys, budget)
+        rows = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in keep])
         out["w"][h] = sc["w"]
         out["keys"][h] = keys
         out["keep"][h] = keep
-        out["out_k"][h] = k[h][keep]
-        out["out_v"][h] = v[h][keep]
+        out["out_k"][h] = k[h][rows]
+        out["out_v"][h] = v[h][rows]
     return out
 
 

@@ -206,3 +206,35 @@ def test_navg_key_slips_are_caught(monkeypatch, slip, pin, args):
 def test_navg_shared_block_slip_is_caught(monkeypatch):
     monkeypatch.setattr(philox, "uniforms_n", _uniforms_n_one_block)
     assert _fails(npins.test_draws_come_from_independent_blocks)
+
+
+# ------------------------------------------------------ block granularity ----
+
+from tests import test_oracle_blocks as bpins  # noqa: E402
+
+_real_block_rows = nexus.block_rows
+
+
+def _block_rows_shifted(P, block):
+    """Slip: token j assigned to block (j + 1) // b."""
+    P = np.asarray(P, dtype=np.float64)
+    return _real_block_rows(np.concatenate([np.zeros((P.shape[0], 1)), P], axis=1)[:, :-1] +
+                            np.concatenate([P[:, -1:] * 0, np.zeros((P.shape[0], P.shape[1] - 1))],
+                                           axis=1), block)
+
+
+def _block_rows_no_partial(P, block):
+    """Slip: the shorter last block dropped (floor instead of ceil)."""
+    P = np.asarray(P, dtype=np.float64)
+    nk = P.shape[1] // block
+    S = P[:, :nk * block].reshape(P.shape[0], nk, block).sum(axis=2)
+    return S / S.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("slip", [_block_rows_shifted, _block_rows_no_partial])
+def test_block_slips_are_caught(monkeypatch, golden, slip):
+    monkeypatch.setattr(nexus, "block_rows", slip)
+    with open(bpins.GOLDEN) as f:
+        import json
+        g = json.load(f)
+    assert _fails(bpins.test_golden_blocks, g)
