@@ -70,8 +70,15 @@ def counter_traffic(kernel):
     return {"bytes": found, "source": os.path.relpath(PROFILE_COUNTERS, ROOT)}
 
 
-def build_batch(wl, device):
-    L, H, N, D, B = wl.n_layers, wl.h_kv, wl.n_tokens, wl.head_dim, wl.budget
+def budget_units(wl, block):
+    """Kept units per head: B tokens, or round(B / b) blocks of b tokens."""
+    return wl.budget if block == 1 else max(1, round(wl.budget / block))
+
+
+def build_batch(wl, device, block=1):
+    L, H, N, D = wl.n_layers, wl.h_kv, wl.n_tokens, wl.head_dim
+    B = budget_units(wl, block)
+    R = min(B * block, N)            # kept rows per head
     q = torch.empty(L, wl.h_q, wl.window, D, dtype=torch.bfloat16, device=device)
     k = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
     v = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
@@ -85,16 +92,17 @@ def build_batch(wl, device):
         v[layer].copy_(v32)
     del q32, k32, v32
     keep = torch.empty(L, H, B, dtype=torch.int32, device=device)
-    out_k = torch.empty(L, H, B, D, dtype=torch.bfloat16, device=device)
+    out_k = torch.empty(L, H, R, D, dtype=torch.bfloat16, device=device)
     out_v = torch.empty_like(out_k)
     items = [dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=out_k[l], out_v=out_v[l],
-                  kv_head_stride=N * D, out_head_stride=B * D, n_tokens=N, budget=B, layer=l)
+                  kv_head_stride=N * D, out_head_stride=R * D, n_tokens=N, budget=B, layer=l)
              for l in range(L)]
     units = nx.make_units(items, device=device)
-    return dict(q=q, k=k, v=v, keep=keep, out_k=out_k, out_v=out_v, units=units)
+    return dict(q=q, k=k, v=v, keep=keep, out_k=out_k, out_v=out_v, units=units, budget=B,
+                rows=R)
 
 
-def cpu_baseline(wl, data, budget_s, n_avg=1):
+def cpu_baseline(wl, data, budget_s, n_avg=1, block=1):
     """The fp64 oracle, whole KV heads in layer order, until ~budget_s seconds pass."""
     from oracle import nexus
     try:
@@ -108,8 +116,8 @@ def cpu_baseline(wl, data, budget_s, n_avg=1):
         q = bf16_bits(data["q"][layer, h * wl.group:(h + 1) * wl.group])
         k = bf16_bits(data["k"][layer, h:h + 1])
         v = bf16_bits(data["v"][layer, h:h + 1])
-        nexus.evict_step(q, k, v, wl.budget, wl.walk_iters, 0, dtype="bf16", layer=layer,
-                         n_avg=n_avg)
+        nexus.evict_step(q, k, v, data["budget"], wl.walk_iters, 0, dtype="bf16", layer=layer,
+                         n_avg=n_avg, block=block)
         heads_done += 1
     dt = time.perf_counter() - t0
     return {"value": round(heads_done * wl.n_tokens / dt, 1), "unit": "KV tokens/s",
@@ -126,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", type=int, default=1,
+                    help="selection unit of Eq. 1: 1 = tokens, else blocks of that many tokens")
     ap.add_argument("--n-avg", type=int, default=1,
                     help="priority averaging count of Eq. 6 (1: A-Res key; -1: top-B by weight)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -151,15 +161,15 @@ def main():
         return
 
     wl = WORKLOADS["llama3_8b_stream32"]
-    data = build_batch(wl, dev)
+    data = build_batch(wl, dev, args.block)
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
-                         n_avg=args.n_avg)
+                         n_avg=args.n_avg, block=args.block)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
         nx.nx_evict_batch(cfg, data["units"], wl.n_layers, wl.n_tokens, wl.walk_iters, 0,
-                          workspace=ws, step=i, max_out_rows=wl.budget)
+                          workspace=ws, step=i, max_out_rows=data["rows"])
 
     for i in range(args.warmup):
         step(i)
@@ -187,7 +197,7 @@ def main():
     # sweep; per kept row 4*d*e bytes (K and V read and written) plus a 4-byte index.
     d, e = wl.head_dim, 2
     k_bytes = tokens * d * e
-    compact_bytes = units * wl.budget * (4 * d * e + 4)
+    compact_bytes = units * (data["rows"] * 4 * d * e + data["budget"] * 4)
     qk_flops = tokens * 2 * wl.group * wl.window * d
     per_launch = {name: (ms / max(cnt, 1), cnt) for name, (ms, cnt) in stages.items() if cnt}
     # (algorithmic amount per launch, unit, peak, bound) of the stages that move the bulk.
@@ -216,7 +226,8 @@ def main():
                                "heads, GQA 32:8, head_dim 128, W=32, H=3, B=6554)",
                    "layers": wl.n_layers, "kv_heads": wl.h_kv, "n_tokens": wl.n_tokens,
                    "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters,
-                   "n_avg": args.n_avg},
+                   "n_avg": args.n_avg, "block": args.block,
+                   "budget_units": data["budget"]},
         "step_latency_ms": round(ms_per_step, 4),
         "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},
         "score_probs_mfma_tflops": round(qk_flops / (per_launch["score_probs"][0] * 1e-3) / 1e12, 1),
@@ -230,7 +241,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg)
+        out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg, args.block)
     print(json.dumps(out))
 
 

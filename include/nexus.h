@@ -79,7 +79,8 @@ typedef struct nx_desc {
                                sizes the compaction grid only (any value is correct, a
                                close bound is fastest); 0 means max_tokens */
   int64_t kv_head_stride;   /* elements between KV heads in k/v; 0 means n_tokens * head_dim */
-  int64_t out_head_stride;  /* elements between KV heads in out_k/out_v; 0 means budget * head_dim */
+  int64_t out_head_stride;  /* elements between KV heads in out_k/out_v; 0 means budget * head_dim
+                               (budget * block * head_dim with blocks) */
   void* workspace;          /* device scratch, >= nx_evict_workspace_bytes(); zero-filled once
                                before first use and not modified by the caller afterwards */
   size_t workspace_bytes;
@@ -90,7 +91,15 @@ typedef struct nx_desc {
                                NX_TOPK (-1): the deterministic n -> infinity limit of
                                appendix 8.2, the B largest weights (key w);
                                anything else: NX_EINVAL */
-  int32_t reserved;         /* must be 0 */
+  int32_t block;            /* units of selection (section 2.1, Eq. 1): 0 or 1 = tokens; b = 2, 4,
+                               8, 16 or 32 = blocks of b consecutive tokens (the last block of a
+                               head may be shorter), scored by BlockSum_b of the attention rows.
+                               With b > 1 the budget, n_sink and n_recent count blocks, keep
+                               indices are block indices, weight / key arrays hold
+                               ceil(n_tokens / b) entries per head, and the compacted rows are
+                               the kept blocks' rows in ascending block order (out_head_stride
+                               >= budget * b rows; items with appended rows need n_tokens % b
+                               == 0).  Other values: NX_EUNSUPPORTED. */
 } nx_desc;
 
 #define NX_MAX_AVG 64

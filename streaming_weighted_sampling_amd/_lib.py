@@ -38,7 +38,7 @@ class NxDesc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("n_avg", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("block", ctypes.c_int32),
     ]
 
 

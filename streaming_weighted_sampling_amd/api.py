@@ -32,6 +32,15 @@ class NexusConfig:
     n_sink: int = 0
     n_recent: int = 0
     n_avg: int = 1            # [Nexus] Eq. 6 averaging count; TOPK (-1) = deterministic limit
+    block: int = 1            # [Nexus] Eq. 1 block size b: 1 = tokens, else 2..32 (power of 2)
+
+    def units(self, n_tokens):
+        """Selection units of a head: tokens, or ceil(n_tokens / block) blocks."""
+        return -(-n_tokens // self.block)
+
+    def kept_rows(self, n_tokens, budget):
+        """Rows of the kept units (at most budget whole blocks, a short last one shorter)."""
+        return min(min(budget, self.units(n_tokens)) * self.block, n_tokens)
 
     def desc(self, workspace=None, *, layer=0, step=0, seq_id=0, kv_head_stride=0,
              out_head_stride=0, max_out_rows=0, stream=None):
@@ -46,6 +55,7 @@ class NexusConfig:
         d.n_sink = self.n_sink
         d.n_recent = self.n_recent
         d.n_avg = self.n_avg
+        d.block = self.block
         d.layer = layer
         d.step = step
         d.seq_id = seq_id
@@ -104,7 +114,7 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
     if q.dtype != cfg.dtype or not q.is_contiguous() or \
             tuple(q.shape) != (cfg.n_q_heads, cfg.window, cfg.head_dim):
         raise ValueError("q must be a contiguous [n_q_heads, window, head_dim] tensor")
-    kept = min(budget, n_tokens)
+    kept = cfg.kept_rows(n_tokens, budget)
     if out_k is None:
         out_k = torch.empty(cfg.n_kv_heads, max(kept, 1), cfg.head_dim, dtype=cfg.dtype, device=k.device)
     if out_v is None:
@@ -123,10 +133,10 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
 
 
 def nx_nexus_weights(cfg, q, k, n_tokens, walk_iters, *, workspace, out_w=None, stream=None):
-    """Nexus weights w [H_kv, n_tokens] fp32."""
+    """Nexus weights w [H_kv, units] fp32 (units = n_tokens, or blocks)."""
     kst = _check_cache(cfg, k, "k")
     if out_w is None:
-        out_w = torch.empty(cfg.n_kv_heads, n_tokens, dtype=torch.float32, device=k.device)
+        out_w = torch.empty(cfg.n_kv_heads, cfg.units(n_tokens), dtype=torch.float32, device=k.device)
     d = cfg.desc(workspace, kv_head_stride=kst, stream=stream)
     check(load().nx_nexus_weights(ctypes.byref(d), _ptr(q), _ptr(k), n_tokens, walk_iters,
                                   _ptr(out_w)), "nx_nexus_weights")
@@ -150,7 +160,7 @@ def nx_reservoir_select(cfg, w, budget, seed, *, workspace, layer=0, step=0, seq
 def nx_kv_compact(cfg, k, v, keep, n_tokens, budget, *, workspace, out_k=None, out_v=None,
                   stream=None):
     kst = _check_cache(cfg, k, "k")
-    kept = min(budget, n_tokens)
+    kept = cfg.kept_rows(n_tokens, budget)
     if out_k is None:
         out_k = torch.empty(cfg.n_kv_heads, kept, cfg.head_dim, dtype=cfg.dtype, device=k.device)
     if out_v is None:

@@ -3,6 +3,7 @@
 //
 // [Nexus] = "Forget Without Compromise: Nexus Sampling for Streaming KV-Cache
 // Eviction Under Fixed Budgets" (academ.us article page).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -27,7 +28,8 @@ nx_status check_desc(const nx_desc* d) {
   if (d->window < 1 || d->n_sink < 0 || d->n_recent < 0) return NX_EINVAL;
   if (!std::isfinite(d->lambda) || !std::isfinite(d->eps_tie)) return NX_EINVAL;
   if (d->n_avg != NX_TOPK && (d->n_avg < 0 || d->n_avg > NX_MAX_AVG)) return NX_EINVAL;
-  if (d->reserved != 0) return NX_EINVAL;
+  if (d->block < 0) return NX_EINVAL;
+  if (d->block > 1 && (d->block > 32 || (d->block & (d->block - 1)) != 0)) return NX_EUNSUPPORTED;
   if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return NX_EUNSUPPORTED;
   return NX_OK;
@@ -61,6 +63,7 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->rows = int32_t(rows);
   g->rows_pad = int32_t(rows_pad);
   g->walk_rows = group * walk;
+  g->block = d->block > 1 ? d->block : 1;
   g->dtype = d->dtype;
   g->n_hu = int32_t(n_hu);
   g->max_tokens = max_tokens;
@@ -153,7 +156,8 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 // on to selection (not the weights-only export) with one draw per token.
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   hipError_t err = hipSuccess;
-  const bool fused = a.g.max_tokens <= kFusedMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
+  const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
+  const bool fused = max_units <= kFusedMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {
@@ -191,7 +195,8 @@ nx_unit single_unit(const nx_desc* d, const void* q, const void* k, const void* 
   u.out_k = out_k;
   u.out_v = out_v;
   u.kv_head_stride = d->kv_head_stride ? d->kv_head_stride : int64_t(n) * d->head_dim;
-  u.out_head_stride = d->out_head_stride ? d->out_head_stride : int64_t(budget) * d->head_dim;
+  u.out_head_stride = d->out_head_stride ? d->out_head_stride
+                                         : int64_t(budget) * (d->block > 1 ? d->block : 1) * d->head_dim;
   u.n_tokens = n;
   u.budget = budget;
   u.layer = d->layer;
@@ -221,7 +226,10 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   const nx_unit u = single_unit(desc, q_window, k_cache, v_cache, out_keep_idx, out_k, out_v,
                                 n_tokens, budget);
   const int64_t d = desc->head_dim, hk = desc->n_kv_heads;
-  const int32_t kept = budget < n_tokens ? budget : n_tokens;
+  const int32_t blk = desc->block > 1 ? desc->block : 1;
+  const int32_t units = (n_tokens + blk - 1) / blk;
+  const int32_t kept_units = budget < units ? budget : units;
+  const int32_t kept = int32_t(std::min<int64_t>(int64_t(kept_units) * blk, n_tokens));   // rows
   if (u.kv_head_stride < n_tokens * d || u.out_head_stride < kept * d) return NX_EINVAL;
   const int32_t esz = elem_size(desc->dtype);
   const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);
@@ -279,6 +287,7 @@ nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tok
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
+  g.block = 1;   // the given weights are the selection units
   if (!w || !out_keep_idx) return NX_EINVAL;
   if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
   // The scoring inputs are not used; q and k only need to be non-null.
@@ -303,7 +312,10 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
   const nx_unit u = single_unit(desc, k_cache, k_cache, v_cache, const_cast<int32_t*>(keep_idx),
                                 out_k, out_v, n_tokens, budget);
   const int64_t d = desc->head_dim, hk = desc->n_kv_heads;
-  const int32_t kept = budget < n_tokens ? budget : n_tokens;
+  const int32_t blk = desc->block > 1 ? desc->block : 1;
+  const int32_t units = (n_tokens + blk - 1) / blk;
+  const int32_t kept_units = budget < units ? budget : units;
+  const int32_t kept = int32_t(std::min<int64_t>(int64_t(kept_units) * blk, n_tokens));   // rows
   if (u.kv_head_stride < n_tokens * d || u.out_head_stride < kept * d) return NX_EINVAL;
   const int32_t esz = elem_size(desc->dtype);
   const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);

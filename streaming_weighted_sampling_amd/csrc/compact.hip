@@ -3,8 +3,9 @@
 // Streaming KV-Cache Eviction Under Fixed Budgets", academ.us article page,
 // section 2.1 streaming view).
 //
-// out[h, r, :] = cache[h, keep[h, r], :] for r < kept, as bit copies, then the
-// optional appended rows out[h, kept + i, :] = app[h, i, :].  Each workgroup
+// out[h, r, :] = cache[h, keep[h, r], :] for r < kept, as bit copies (with
+// blocks of b tokens, whole blocks: out[h, r] = cache[h, keep[h, r / b] * b
+// + r % b]), then the optional appended rows after the kept rows.  Each workgroup
 // moves kCompactRows rows of K and of V; every lane moves 16-B chunks, so a
 // 256-B row is one fully used 256-B segment read and written by 16 lanes.
 // Loads and stores go through buffer resources sized to the head's rows.
@@ -29,7 +30,12 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
   const int hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid || u.out_k == nullptr || u.out_v == nullptr || u.keep == nullptr) return;
-  const int rows = u.kept + u.n_append;
+  // Kept units are tokens (b = 1) or blocks of b tokens: output row r comes
+  // from kept unit r / b, row r % b of it; rows past a short last block are
+  // skipped.  Appended rows follow the kept rows.
+  const int b = a.g.block;
+  const int kept_rows = min(u.kept * b, u.n);
+  const int rows = kept_rows + u.n_append;
   const uint32_t src_bytes = uint32_t(u.n) * kRowBytes;
   const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
   const Buf kb(u.k, src_bytes), vb(u.v, src_bytes);
@@ -47,12 +53,13 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
       const int off = (c % kPerRow) * 16;
       src[i] = -1;
       app[i] = false;
-      if (r < u.kept) {
-        const int idx = u.keep[r];
-        if (idx >= 0 && idx < u.n) src[i] = idx * kRowBytes + off;
-        else bad = true;
+      if (r < kept_rows) {
+        const int idx = u.keep[r / b];
+        const int sr = idx * b + (r & (b - 1));
+        if (idx < 0 || idx >= u.nu) bad = true;
+        else if (sr < u.n) src[i] = sr * kRowBytes + off;
       } else if (r < rows) {
-        src[i] = (r - u.kept) * kRowBytes + off;
+        src[i] = (r - kept_rows) * kRowBytes + off;
         app[i] = true;
       }
     }

@@ -90,6 +90,7 @@ struct HeadUnit {
   const char* app_k;
   const char* app_v;
   int32_t n, budget, kept, n_append;
+  int32_t nu;          // selection units: ceil(n / block); kept = min(budget, nu) of them
   uint32_t layer, unit_id;
   int32_t h;
   bool valid;
@@ -112,7 +113,8 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   r.h = h;
   r.n = u.n_tokens;
   r.budget = u.budget;
-  r.kept = u.budget < u.n_tokens ? u.budget : u.n_tokens;
+  r.nu = (u.n_tokens + g.block - 1) / g.block;
+  r.kept = u.budget < r.nu ? u.budget : r.nu;
   r.n_append = u.n_append;
   r.layer = u.layer;
   r.unit_id = u.seq_id * uint32_t(g.h_kv) + uint32_t(h);
@@ -127,9 +129,12 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && u.budget >= 1 &&
             u.n_append >= 0 && a.n_sink + a.n_recent <= u.budget &&
             u.kv_head_stride >= int64_t(u.n_tokens) * d && u.q != nullptr && u.k != nullptr;
+  // Rows of the kept units (whole blocks; a short last block only shortens it).
+  const int64_t kept_rows = min(int64_t(r.kept) * g.block, int64_t(u.n_tokens));
   if (u.out_k || u.out_v)
-    ok = ok && u.out_head_stride >= int64_t(r.kept + u.n_append) * d &&
-         (int64_t(r.kept) + u.n_append) * d * esz <= INT32_MAX;
+    ok = ok && u.out_head_stride >= (kept_rows + u.n_append) * d &&
+         (kept_rows + u.n_append) * d * esz <= INT32_MAX;
+  if (g.block > 1 && u.n_append > 0) ok = ok && u.n_tokens % g.block == 0;
   if (u.n_append > 0) ok = ok && u.app_k != nullptr && u.app_v != nullptr;
   r.valid = ok;
   return r;

@@ -56,6 +56,7 @@ struct Geometry {
   int32_t n_tmax;        // score tiles per head unit at tok_per_block (for max_tokens)
   int32_t n_t1, n_t2;    // workspace tile slots per head unit (sized for kMinTokPerBlock)
   int32_t n_kc;          // reservoir_keys chunks per head unit
+  int32_t block;         // tokens per selection unit (1, or a block size up to 32)
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).

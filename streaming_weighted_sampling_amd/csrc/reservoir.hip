@@ -118,7 +118,7 @@ __device__ inline double token_key(const Args& a, const HeadUnit& u, int j, floa
     }
     key = m + log(sum) - log(double(a.n_avg));
   }
-  if (j < a.n_sink || j >= u.n - a.n_recent) key = INFINITY;
+  if (j < a.n_sink || j >= u.nu - a.n_recent) key = INFINITY;
   return key;
 }
 
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) return;
   const int j0 = chunk * kKeysPerBlock;
-  if (j0 >= u.n) return;
+  if (j0 >= u.nu) return;
   __shared__ float s_coef[kMaxWalk];
   __shared__ uint64_t s_or[kKeysThreads / 64], s_and[kKeysThreads / 64];
 
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
   const float* a_in = a.a + size_t(hu) * g.max_tokens;
   const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
   uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
-  const size_t ext = size_t(u.h) * u.n;   // row of head h in [h_kv, n] exports
-  const float ramp = u.n > 1 ? 1.f / float(u.n - 1) : 0.f;
+  const size_t ext = size_t(u.h) * u.nu;   // row of head h in [h_kv, n] exports
+  const float ramp = u.nu > 1 ? 1.f / float(u.nu - 1) : 0.f;
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   uint64_t v_or = 0, v_and = ~0ull;
   bool nonfinite = false;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int j = j0 + threadIdx.x + kKeysThreads * i;
-    in[i] = j < u.n;
+    in[i] = j < u.nu;
     const int jc = in[i] ? j : j0;   // a valid token for the lanes past the end
     if (a.w_in != nullptr) {
       w[i] = a.w_in[ext + jc];
@@ -308,7 +308,7 @@ __device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Vali
 // from (o, an), the radix passes, then the kept indices in ascending order.
 __device__ inline void select_global(const Args& a, const HeadUnit& u, const uint64_t* keys,
                                      uint64_t o, uint64_t an, SelCore& sh) {
-  const int n = u.n, tid = threadIdx.x;
+  const int n = u.nu, tid = threadIdx.x;
   if (tid == 0) sel_init(sh, o, an, n, u.budget);
   __syncthreads();
   const int slots = (n + kSelThreads - 1) / kSelThreads;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) 
   const int hu = blockIdx.x;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid || u.keep == nullptr) return;
-  const int n = u.n;
+  const int n = u.nu;
   if (u.budget >= n) {
     for (int j = threadIdx.x; j < n; j += kSelThreads) u.keep[j] = j;
     return;
@@ -489,7 +489,7 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
 // Whether a head unit's selection runs on estimate codes (no key export, a
 // keep array, and something to drop).
 __device__ inline bool uses_estimate(const Args& a, const HeadUnit& u) {
-  return a.keys_out == nullptr && u.keep != nullptr && u.budget < u.n;
+  return a.keys_out == nullptr && u.keep != nullptr && u.budget < u.nu;
 }
 
 // Estimate codes of kKeysPerBlock tokens of one head unit (many workgroups
@@ -501,12 +501,12 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) return;
   const int j0 = chunk * kKeysPerBlock;
-  if (j0 >= u.n) return;
+  if (j0 >= u.nu) return;
   __shared__ float s_coef[kMaxWalk];
   if (threadIdx.x < kMaxWalk)
     s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
   __syncthreads();
-  const int n = u.n;
+  const int n = u.nu;
   const size_t ext = size_t(u.h) * n;
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
                      a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   const int hu = blockIdx.x;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid) return;
-  const int n = u.n;
+  const int n = u.nu;
   __shared__ SelShared sh;
   SelCore& core = sh.core;
   const int tid = threadIdx.x;
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   if (tid < kMaxWalk) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
   __syncthreads();
 
-  const size_t ext = size_t(u.h) * u.n;   // row of head h in [h_kv, n] exports
+  const size_t ext = size_t(u.h) * u.nu;   // row of head h in [h_kv, n] exports
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
                      a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);

@@ -59,6 +59,30 @@ struct Geo {
 
 __device__ inline int out_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
 
+// Sum over aligned groups of b lanes (b a power of two up to 32, inside a
+// lane half), every lane of a group receiving the group's sum in a fixed
+// order: DPP lane moves inside a row of 16 (quad permutes for partners at
+// distance 1 and 2, then the half-row and row mirrors, which pair each lane
+// with the other quad / half of its row), and one cross-row permute for 32.
+__device__ inline float dpp_add(float x, int ctrl_sel) {
+  int v;
+  switch (ctrl_sel) {
+    case 0: v = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+    case 1: v = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+    case 2: v = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: v = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return x + __int_as_float(v);
+}
+__device__ inline float group_sum(float x, int b) {
+  if (b >= 2) x = dpp_add(x, 0);
+  if (b >= 4) x = dpp_add(x, 1);
+  if (b >= 8) x = dpp_add(x, 2);
+  if (b >= 16) x = dpp_add(x, 3);
+  if (b >= 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
 // Window row rho of a head unit -> (query head within the group, window slot).
 __device__ inline bool row_source(const Geometry& g, int rho, int& qh, int& wpos) {
   if (rho >= g.rows) return false;
@@ -430,14 +454,25 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 
   // P_t of token t0 + 32 s + nn (lanes of half 0): global and LDS; tokens past
   // the cache end enter the Gram as zero.
+  // With blocks (b > 1) the values of a block's b lanes are summed (BlockSum_b
+  // of Eq. 1); the block's first lane stores the sum at the block index and
+  // holds it in LDS, the other lanes hold 0, so the Gram sees block rows.
+  const int blk = g.block;
+  const bool lead = (nn & (blk - 1)) == 0;
   auto put_walk = [&](int s, const float (&pt)[kMaxT]) {
     const int tok = t0 + 32 * s + nn;
     const bool ok = tok < u.n;
 #pragma unroll
     for (int t = 0; t < kMaxT; ++t) {
       if (t < walk) {
-        if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
-        s_pt[s & 1][t][nn] = ok ? pt[t] : 0.f;
+        if (blk == 1) {
+          if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
+          s_pt[s & 1][t][nn] = ok ? pt[t] : 0.f;
+        } else {
+          const float v = group_sum(ok ? pt[t] : 0.f, blk);
+          if (lead && ok) p_out.stf(uint32_t((t * g.max_tokens + tok / blk) * 4), v);
+          s_pt[s & 1][t][nn] = lead ? v : 0.f;
+        }
       }
     }
   };
@@ -476,7 +511,12 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int r = 1; r < kWaves; ++r)
       if (r < row_roles) sum += s_a[s & 1][r][nn];
-    if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
+    if (blk == 1) {
+      if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
+    } else {
+      sum = group_sum(tok < u.n ? sum : 0.f, blk);
+      if (lead && tok < u.n) a_out.stf(uint32_t((tok / blk) * 4), sum);
+    }
   };
 
   sweep_tiles<T, D, GE::kSlotsProbs, 2>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {

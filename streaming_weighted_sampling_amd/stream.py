@@ -66,7 +66,7 @@ class StreamingCache:
     def step(self):
         """One eviction event: q, app_k and app_v must hold this event's window
         queries and the rows that arrive before the next event."""
-        kept = min(self.budget, self.n_tokens)
+        kept = self.cfg.kept_rows(self.n_tokens, self.budget)
         if kept + self.n_append > self.capacity:
             raise ValueError("capacity too small for budget + n_append")
         units = self._units_for(self.cur, self.n_tokens)

@@ -270,6 +270,73 @@ def test_averaged_priority_end_to_end(n_avg):
         assert gc.rows_equal(ov[h], d["v"][h], got)
 
 
+# ------------------------------------------------- block granularity (f2) --
+
+
+@pytest.mark.parametrize("block,n", [(32, 4096), (8, 4096), (2, 1000), (32, 4001), (16, 300)])
+def test_block_mode_end_to_end(block, n):
+    """Blocks of b tokens (Eq. 1's BlockSum_b): block weights against the oracle,
+    the kept blocks equal the oracle's selection on the GPU's weights, whole
+    kept blocks compacted (a short last block when b does not divide N)."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=block)
+    d = gen_layer(wl, device=DEV, n_tokens=n)
+    nu = cfg.units(n)
+    budget = max(1, round(nu / 5))
+    ws = _ws(cfg, n, 1, wl.walk_iters)
+    w_gpu = nx.nx_nexus_weights(cfg, d["q"], d["k"], n, wl.walk_iters, workspace=ws)
+    nx.nx_read_device_status(cfg, ws)
+    assert tuple(w_gpu.shape) == (wl.h_kv, nu)
+    keep, ok, ov = nx.nx_evict_step(cfg, d["q"], d["k"], d["v"], n, budget, wl.walk_iters, 5,
+                                    workspace=ws, layer=1, step=2)
+    nx.nx_read_device_status(cfg, ws)
+    qh, dt = gc.host(d["q"])
+    kh, _ = gc.host(d["k"])
+    vh, _ = gc.host(d["v"])
+    ref = nexus.evict_step(qh, kh, vh, budget, wl.walk_iters, 5, dtype=dt, layer=1, step=2,
+                           block=block)
+    _, on_gpu_w = nexus.select_from_weights(w_gpu.cpu().numpy(), budget, 5, layer=1, step=2)
+    for h in range(wl.h_kv):
+        gc.assert_weights_close(w_gpu[h].cpu().numpy(), ref["w"][h], f"block {block} head {h}")
+        got = gc.check_keep_valid(keep[h].cpu().numpy(), nu, budget)
+        np.testing.assert_array_equal(got, on_gpu_w[h])
+        assert gc.overlap_fraction(got, ref["keep"][h]) >= 1 - 1.0 / len(got)
+        rows = np.concatenate([np.arange(b * block, min(b * block + block, n)) for b in got])
+        assert gc.rows_equal(ok[h][:len(rows)], d["k"][h], rows)
+        assert gc.rows_equal(ov[h][:len(rows)], d["v"][h], rows)
+
+
+def test_block_mode_streaming_appends_after_whole_blocks():
+    """Four events of append-256 / evict with blocks of 32 on four layers."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=32)
+    L, n0, A, budget = 4, 4096, 256, 26          # 26 blocks = 832 rows kept
+    sc = StreamingCache(cfg, L, n0 + A, budget, A, wl.walk_iters, seed=4, device=DEV)
+    k0 = torch.randn(L, wl.h_kv, n0 + A, wl.head_dim, device=DEV).to(torch.bfloat16)
+    v0 = torch.randn_like(k0)
+    sc.load(k0, v0, n0 + A)
+    for step in range(4):
+        sc.q.copy_(torch.randn_like(sc.q))
+        sc.app_k.copy_(torch.randn_like(sc.app_k))
+        sc.app_v.copy_(torch.randn_like(sc.app_v))
+        kp, vp = (t.clone() for t in sc.live())
+        n_pre = sc.n_tokens
+        app_k, app_v = sc.app_k.clone(), sc.app_v.clone()
+        sc.step()
+        nx.nx_read_device_status(sc.cfg, sc.ws)
+        assert sc.n_tokens == budget * 32 + A
+        kl, vl = sc.live()
+        for l in range(L):
+            for h in range(wl.h_kv):
+                blocks = sc.keep[l, h].cpu().numpy()
+                gc.check_keep_valid(blocks, n_pre // 32, budget)
+                rows = np.concatenate([np.arange(b * 32, b * 32 + 32) for b in blocks])
+                assert gc.rows_equal(kl[l, h, :budget * 32], kp[l, h], rows)
+                assert gc.rows_equal(vl[l, h, :budget * 32], vp[l, h], rows)
+            assert torch.equal(kl[l, :, budget * 32:].view(torch.int16), app_k[l].view(torch.int16))
+
+
 # --------------------------------------------------------------- compaction --
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
