@@ -304,3 +304,40 @@ def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
                             n_recent)
         keeps.append(select_top(keys[h], budget))
     return keys, keeps
+
+
+# ------------------------------------------------- in-place compaction ----
+
+def inplace_layout(keep, n_tokens):
+    """Where each kept row lands when the cache is compacted in place.
+
+    [Nexus] section 2.1 continues with K_S, V_S; attention does not depend on
+    the order of the cached rows once positions are encoded in K, so only the
+    kept rows at or past position `kept` (= len(keep)) must move: the j-th of
+    them (ascending) fills the j-th evicted position below `kept`
+    (ascending).  Returns new_pos [len(keep)]: the new row of keep[i].
+    """
+    keep = np.asarray(keep, dtype=np.int64)
+    kept = len(keep)
+    stay = keep < kept
+    holes = np.setdiff1d(np.arange(kept), keep[stay])
+    movers = keep[~stay]
+    if len(holes) != len(movers):
+        raise AssertionError("holes and movers must pair up")
+    new_pos = keep.copy()
+    new_pos[~stay] = holes
+    return new_pos
+
+
+def compact_inplace(cache, keep, appended=None):
+    """The cache after in-place compaction of one head: cache [N, D] (a copy is
+    returned), keep ascending; appended rows, if any, go to kept, kept+1, ..."""
+    out = np.array(cache, copy=True)
+    keep = np.asarray(keep, dtype=np.int64)
+    kept = len(keep)
+    new_pos = inplace_layout(keep, cache.shape[0])
+    moved = new_pos != keep
+    out[new_pos[moved]] = np.asarray(cache)[keep[moved]]
+    if appended is not None and len(appended):
+        out[kept:kept + len(appended)] = appended
+    return out
