@@ -127,6 +127,55 @@ def cpu_baseline(wl, data, budget_s, n_avg=1, block=1):
                       f"{dt:.1f} s; BLAS threads {threads}, {os.cpu_count()} host CPUs visible"}
 
 
+def steady(wl, args):
+    """Streaming steady state: every event holds N = B + A rows per head, keeps
+    B and appends A new rows (queries and new rows synthetic, fixed)."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    dev = "cuda"
+    L, B, A = wl.n_layers, wl.budget, wl.stream_append
+    n = B + A
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16)
+    sc = StreamingCache(cfg, L, n, B, A, wl.walk_iters, seed=0, device=dev,
+                        inplace=args.compact == "inplace")
+    q32 = torch.empty(wl.h_q, wl.window, wl.head_dim, device=dev)
+    k32 = torch.empty(wl.h_kv, n, wl.head_dim, device=dev)
+    v32 = torch.empty(wl.h_kv, n, wl.head_dim, device=dev)
+    k0 = torch.empty(L, wl.h_kv, n, wl.head_dim, dtype=torch.bfloat16, device=dev)
+    v0 = torch.empty_like(k0)
+    for layer in range(L):
+        fill_layer_(wl, q32, k32, v32, layer=layer, n_tokens=n)
+        sc.q[layer].copy_(q32)
+        k0[layer].copy_(k32)
+        v0[layer].copy_(v32)
+    sc.load(k0, v0, n)
+    g = torch.Generator(device=dev).manual_seed(5)
+    sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g, device=dev).to(torch.bfloat16))
+    sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g, device=dev).to(torch.bfloat16))
+    for _ in range(args.warmup):
+        sc.step()
+    torch.cuda.synchronize()
+    nx.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        sc.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nx.profile_enable(False)
+    stages = nx.profile_read()
+    nx.nx_read_device_status(sc.cfg, sc.ws)
+    ms = (t1 - t0) * 1e3 / args.steps
+    units = L * wl.h_kv
+    print(json.dumps({
+        "metric": METRIC, "value": round(units * n / (ms * 1e-3), 1), "unit": "KV tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"llama3_8b_stream32 steady-state event N={n} -> {B} + {A} "
+                               f"appended, 32 layers x 8 KV heads", "compact": args.compact},
+        "stage_ms_per_launch": {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items() if v[1]},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +183,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--steady", action="store_true",
+                    help="time the streaming steady-state event (N = B + 256 -> B, 32 layers) "
+                         "through StreamingCache instead of the N = 32768 event")
+    ap.add_argument("--compact", choices=["copy", "inplace"], default="copy",
+                    help="with --steady: copy kept rows to the other buffer, or fill holes in place")
     ap.add_argument("--block", type=int, default=1,
                     help="selection unit of Eq. 1: 1 = tokens, else blocks of that many tokens")
     ap.add_argument("--n-avg", type=int, default=1,
@@ -161,6 +215,9 @@ def main():
         return
 
     wl = WORKLOADS["llama3_8b_stream32"]
+    if args.steady:
+        steady(wl, args)
+        return
     data = build_batch(wl, dev, args.block)
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
                          n_avg=args.n_avg, block=args.block)

@@ -100,7 +100,20 @@ typedef struct nx_desc {
                                the kept blocks' rows in ascending block order (out_head_stride
                                >= budget * b rows; items with appended rows need n_tokens % b
                                == 0).  Other values: NX_EUNSUPPORTED. */
+  int32_t compact;          /* NX_COMPACT_COPY (0): kept rows copied in ascending order to
+                               out_k / out_v.  NX_COMPACT_INPLACE (1): k / v themselves are
+                               compacted (section 2.1 continues with K_S, V_S; attention does
+                               not depend on row order once positions are in K): the kept
+                               rows at or past position kept move, the j-th of them
+                               (ascending) into the j-th evicted slot below kept, and the
+                               appended rows go to kept, kept + 1, ...; out_k / out_v must be
+                               NULL and kv_head_stride must hold kept + n_append rows; tokens
+                               only (block <= 1).  Other values: NX_EINVAL. */
+  int32_t reserved;         /* must be 0 */
 } nx_desc;
+
+#define NX_COMPACT_COPY 0
+#define NX_COMPACT_INPLACE 1
 
 #define NX_MAX_AVG 64
 #define NX_TOPK (-1)
@@ -157,7 +170,9 @@ size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t
  *                first, feed the walk; H = 0 gives plain direct attention
  *   seed         64-bit Philox key
  *   out_keep_idx [n_kv_heads, budget] int32, ascending; entries past `kept` untouched
- *   out_k, out_v [n_kv_heads][out_head_stride], must not overlap k_cache / v_cache
+ *   out_k, out_v [n_kv_heads][out_head_stride], must not overlap k_cache / v_cache;
+ *                NULL with desc->compact == NX_COMPACT_INPLACE, which compacts k_cache
+ *                and v_cache themselves (the caches are then written)
  * Errors: NX_EINVAL, NX_EALIAS, NX_EWORKSPACE, NX_EUNSUPPORTED, NX_EHIP.
  */
 nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,

@@ -7,7 +7,8 @@ the binding fails loudly when the library has not been built.
 
 from ._lib import (  # noqa: F401
     NX_OK, NX_EINVAL, NX_EALIAS, NX_EWORKSPACE, NX_EUNSUPPORTED, NX_ENONFINITE, NX_EHIP,
-    NX_BF16, NX_F32, NxDesc, NxUnit, NexusError, LIB_PATH, load, status_str,
+    NX_BF16, NX_F32, NX_COMPACT_COPY, NX_COMPACT_INPLACE, NxDesc, NxUnit, NexusError, LIB_PATH,
+    load, status_str,
 )
 from .api import (  # noqa: F401
     NexusConfig, TOPK, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,

@@ -13,6 +13,8 @@ NX_EWORKSPACE = -3
 NX_EUNSUPPORTED = -4
 NX_ENONFINITE = -5
 NX_EHIP = -6
+NX_COMPACT_COPY = 0
+NX_COMPACT_INPLACE = 1
 NX_BF16 = 0
 NX_F32 = 1
 
@@ -39,6 +41,8 @@ class NxDesc(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("n_avg", ctypes.c_int32),
         ("block", ctypes.c_int32),
+        ("compact", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

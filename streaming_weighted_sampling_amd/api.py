@@ -33,6 +33,7 @@ class NexusConfig:
     n_recent: int = 0
     n_avg: int = 1            # [Nexus] Eq. 6 averaging count; TOPK (-1) = deterministic limit
     block: int = 1            # [Nexus] Eq. 1 block size b: 1 = tokens, else 2..32 (power of 2)
+    compact: int = 0          # 0: copy kept rows to new buffers; 1: compact k / v in place
 
     def units(self, n_tokens):
         """Selection units of a head: tokens, or ceil(n_tokens / block) blocks."""
@@ -56,6 +57,7 @@ class NexusConfig:
         d.n_recent = self.n_recent
         d.n_avg = self.n_avg
         d.block = self.block
+        d.compact = self.compact
         d.layer = layer
         d.step = step
         d.seq_id = seq_id
@@ -115,13 +117,20 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
             tuple(q.shape) != (cfg.n_q_heads, cfg.window, cfg.head_dim):
         raise ValueError("q must be a contiguous [n_q_heads, window, head_dim] tensor")
     kept = cfg.kept_rows(n_tokens, budget)
-    if out_k is None:
-        out_k = torch.empty(cfg.n_kv_heads, max(kept, 1), cfg.head_dim, dtype=cfg.dtype, device=k.device)
-    if out_v is None:
-        out_v = torch.empty_like(out_k)
-    ost = _check_cache(cfg, out_k, "out_k")
-    if _check_cache(cfg, out_v, "out_v") != ost:
-        raise ValueError("out_k and out_v must share the head stride")
+    if cfg.compact:
+        # In place: k and v are compacted themselves (their first `kept` rows).
+        if out_k is not None or out_v is not None:
+            raise ValueError("in-place compaction takes no out_k / out_v")
+        ost = 0
+    else:
+        if out_k is None:
+            out_k = torch.empty(cfg.n_kv_heads, max(kept, 1), cfg.head_dim, dtype=cfg.dtype,
+                                device=k.device)
+        if out_v is None:
+            out_v = torch.empty_like(out_k)
+        ost = _check_cache(cfg, out_k, "out_k")
+        if _check_cache(cfg, out_v, "out_v") != ost:
+            raise ValueError("out_k and out_v must share the head stride")
     if keep is None:
         keep = torch.empty(cfg.n_kv_heads, budget, dtype=torch.int32, device=k.device)
     d = cfg.desc(workspace, layer=layer, step=step, seq_id=seq_id, kv_head_stride=kst,
@@ -129,6 +138,8 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
     check(load().nx_evict_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), n_tokens, budget,
                                walk_iters, seed, _ptr(keep), _ptr(out_k), _ptr(out_v)),
           "nx_evict_step")
+    if cfg.compact:
+        return keep, k, v
     return keep, out_k, out_v
 
 

@@ -29,6 +29,9 @@ nx_status check_desc(const nx_desc* d) {
   if (!std::isfinite(d->lambda) || !std::isfinite(d->eps_tie)) return NX_EINVAL;
   if (d->n_avg != NX_TOPK && (d->n_avg < 0 || d->n_avg > NX_MAX_AVG)) return NX_EINVAL;
   if (d->block < 0) return NX_EINVAL;
+  if (d->compact != NX_COMPACT_COPY && d->compact != NX_COMPACT_INPLACE) return NX_EINVAL;
+  if (d->reserved != 0) return NX_EINVAL;
+  if (d->compact == NX_COMPACT_INPLACE && d->block > 1) return NX_EUNSUPPORTED;
   if (d->block > 1 && (d->block > 32 || (d->block & (d->block - 1)) != 0)) return NX_EUNSUPPORTED;
   if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return NX_EUNSUPPORTED;
@@ -64,6 +67,7 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->rows_pad = int32_t(rows_pad);
   g->walk_rows = group * walk;
   g->block = d->block > 1 ? d->block : 1;
+  g->inplace = d->compact == NX_COMPACT_INPLACE;
   g->dtype = d->dtype;
   g->n_hu = int32_t(n_hu);
   g->max_tokens = max_tokens;
@@ -221,7 +225,9 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
-  if (!q_window || !k_cache || !v_cache || !out_keep_idx || !out_k || !out_v) return NX_EINVAL;
+  const bool inplace = desc->compact == NX_COMPACT_INPLACE;
+  if (!q_window || !k_cache || !v_cache || !out_keep_idx) return NX_EINVAL;
+  if (inplace ? (out_k || out_v) : (!out_k || !out_v)) return NX_EINVAL;
   if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
   const nx_unit u = single_unit(desc, q_window, k_cache, v_cache, out_keep_idx, out_k, out_v,
                                 n_tokens, budget);
@@ -235,13 +241,20 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);
   const Range rv = span(v_cache, hk, u.kv_head_stride, n_tokens * d, esz);
   const Range rq = span(q_window, 1, 0, int64_t(desc->n_q_heads) * desc->window * d, esz);
-  const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
-  const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
   const Range rkeep = span(out_keep_idx, 1, 0, hk * budget, 4);
-  for (Range o : {rok, rov, rkeep})
+  if (inplace) {
+    // k and v are compacted in place: only the keep array must stay apart.
     for (Range i : {rk, rv, rq})
-      if (overlap(o, i)) return NX_EALIAS;
-  if (overlap(rok, rov) || overlap(rok, rkeep) || overlap(rov, rkeep)) return NX_EALIAS;
+      if (overlap(rkeep, i)) return NX_EALIAS;
+    if (overlap(rk, rv)) return NX_EALIAS;
+  } else {
+    const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
+    const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
+    for (Range o : {rok, rov, rkeep})
+      for (Range i : {rk, rv, rq})
+        if (overlap(o, i)) return NX_EALIAS;
+    if (overlap(rok, rov) || overlap(rok, rkeep) || overlap(rov, rkeep)) return NX_EALIAS;
+  }
   g.max_out_rows = kept;
   Args a = base_args(desc, g, seed);
   if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
@@ -307,7 +320,9 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
-  if (!k_cache || !v_cache || !keep_idx || !out_k || !out_v) return NX_EINVAL;
+  const bool inplace = desc->compact == NX_COMPACT_INPLACE;
+  if (!k_cache || !v_cache || !keep_idx) return NX_EINVAL;
+  if (inplace ? (out_k || out_v) : (!out_k || !out_v)) return NX_EINVAL;
   if (budget < 1) return NX_EINVAL;
   const nx_unit u = single_unit(desc, k_cache, k_cache, v_cache, const_cast<int32_t*>(keep_idx),
                                 out_k, out_v, n_tokens, budget);
@@ -320,12 +335,16 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
   const int32_t esz = elem_size(desc->dtype);
   const Range rk = span(k_cache, hk, u.kv_head_stride, n_tokens * d, esz);
   const Range rv = span(v_cache, hk, u.kv_head_stride, n_tokens * d, esz);
-  const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
-  const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
-  for (Range o : {rok, rov})
-    for (Range i : {rk, rv})
-      if (overlap(o, i)) return NX_EALIAS;
-  if (overlap(rok, rov)) return NX_EALIAS;
+  if (inplace) {
+    if (overlap(rk, rv)) return NX_EALIAS;
+  } else {
+    const Range rok = span(out_k, hk, u.out_head_stride, kept * d, esz);
+    const Range rov = span(out_v, hk, u.out_head_stride, kept * d, esz);
+    for (Range o : {rok, rov})
+      for (Range i : {rk, rv})
+        if (overlap(o, i)) return NX_EALIAS;
+    if (overlap(rok, rov)) return NX_EALIAS;
+  }
   if (desc->workspace == nullptr || desc->workspace_bytes < 256) return NX_EWORKSPACE;
   g.max_out_rows = kept;
   Args a = base_args(desc, g, 0);

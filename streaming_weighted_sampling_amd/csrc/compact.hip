@@ -84,17 +84,132 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
   if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(a, kStatusBadItem);
 }
 
+// In-place compaction (hole filling) for streaming.  With kept rows in
+// ascending keep[0..kept), let c = #{keep[i] < kept}: rows keep[c..kept) are
+// the movers (kept rows at or past position kept) and the evicted positions
+// below kept are the holes, equally many.  The j-th mover goes to the j-th
+// hole; since keep[i] - i counts the holes before keep[i], the j-th hole is
+// j + i + 1 for the last i < c with keep[i] - i <= j (or j when none).
+// Sources (>= kept) and destinations (< kept) are disjoint; the appended rows
+// are written by a second kernel so that none overwrites a mover before it is
+// read.  Rows move as 16-B chunks, one kCompactRows block of movers per
+// workgroup.
+constexpr int kLdsKeep = 12288;   // keep entries staged in LDS for the searches (48 KB)
+
+// Moves the movers of one head unit; keep(i) reads keep entry i.  The two
+// callers pass a reader of the LDS copy or of the array in memory, each
+// naming its own address space, so that no LDS access goes through a generic
+// pointer (a flat access whose base register lies outside the LDS aperture
+// faults even when the immediate offset would bring it back inside).
+template <int kRowBytes, typename Keep>
+__device__ __forceinline__ bool fill_holes(const HeadUnit& u, Keep keep) {
+  constexpr int kPerRow = kRowBytes / 16;
+  constexpr int kRowsPerPass = kThreads / kPerRow;
+  const int kept = u.kept;
+  // c = #{keep[i] < kept}: the entries are ascending, so a binary search.
+  int lo = 0, hi = kept;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (keep(mid) < kept) lo = mid + 1; else hi = mid;
+  }
+  const int c = lo;
+  const int movers = kept - c;
+  // Sources lie below n, destinations below kept; the head holds
+  // max(n, kept + n_append) rows (both bounds are checked in head_unit).
+  const uint32_t head_bytes = uint32_t(max(u.n, kept + u.n_append)) * kRowBytes;
+  const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);
+  const int col = threadIdx.x % kPerRow;
+  bool bad = false;
+  for (int m0 = blockIdx.x * kCompactRows; m0 < movers; m0 += gridDim.x * kCompactRows) {
+    for (int r = threadIdx.x / kPerRow; r < kCompactRows; r += kRowsPerPass) {
+      const int j = m0 + r;
+      if (j >= movers) break;
+      const int src = keep(c + j);
+      // last i < c with keep[i] - i <= j
+      int l = 0, h = c;
+      while (l < h) {
+        const int mid = (l + h) >> 1;
+        if (keep(mid) - mid <= j) l = mid + 1; else h = mid;
+      }
+      const int hole = j + l;
+      if (src < kept || src >= u.n || hole >= kept) { bad = true; continue; }
+      const uint4 xk = kb.ld16(uint32_t(src * kRowBytes + 16 * col));
+      const uint4 xv = vb.ld16(uint32_t(src * kRowBytes + 16 * col));
+      kb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xk);
+      vb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xv);
+    }
+  }
+  return bad;
+}
+
+template <int kRowBytes>
+__global__ __launch_bounds__(kThreads) void kv_fill_holes_kernel(const Args a) {
+  __shared__ int32_t s_keep[kLdsKeep];
+  const int hu = blockIdx.y;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid || u.keep == nullptr) return;
+  const int kept = u.kept;
+  // Movers are kept rows at or past kept, so at most n - kept of them; the
+  // whole workgroup leaves together.
+  if (int(blockIdx.x) * kCompactRows >= u.n - kept) return;
+  bool bad;
+  if (kept <= kLdsKeep) {
+    // The searches read the keep array many times: stage it in LDS once.
+    for (int i = threadIdx.x; i < kept; i += kThreads) s_keep[i] = u.keep[i];
+    __syncthreads();
+    bad = fill_holes<kRowBytes>(u, [](int i) { return s_keep[i]; });
+  } else {
+    const int32_t* keep = u.keep;
+    bad = fill_holes<kRowBytes>(u, [keep](int i) { return keep[i]; });
+  }
+  if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(a, kStatusBadItem);
+}
+
+template <int kRowBytes>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
+  constexpr int kPerRow = kRowBytes / 16;
+  constexpr int kRowsPerPass = kThreads / kPerRow;
+  const int hu = blockIdx.y;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid || u.keep == nullptr || u.n_append == 0) return;
+  const uint32_t head_bytes = uint32_t(u.kept + u.n_append) * kRowBytes;
+  const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
+  const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);
+  const Buf kab(u.app_k, app_bytes), vab(u.app_v, app_bytes);
+  const int col = threadIdx.x % kPerRow;
+  for (int r0 = blockIdx.x * kCompactRows; r0 < u.n_append; r0 += gridDim.x * kCompactRows) {
+    for (int r = threadIdx.x / kPerRow; r < kCompactRows && r0 + r < u.n_append; r += kRowsPerPass) {
+      const uint32_t off = uint32_t((r0 + r) * kRowBytes + 16 * col);
+      const uint4 xk = kab.ld16(off);
+      const uint4 xv = vab.ld16(off);
+      kb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xk);
+      vb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xv);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_kv_compact(const Args& a, hipStream_t s) {
   const int max_rows = a.g.max_out_rows > 0 ? a.g.max_out_rows : a.g.max_tokens;
   const dim3 grid((max_rows + kCompactRows - 1) / kCompactRows, a.g.n_hu);
   const int row_bytes = a.g.head_dim * (a.g.dtype == NX_BF16 ? 2 : 4);
-  switch (row_bytes) {
-    case 128: hipLaunchKernelGGL(kv_compact_kernel<128>, grid, dim3(kThreads), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(kv_compact_kernel<256>, grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(kv_compact_kernel<512>, grid, dim3(kThreads), 0, s, a); break;
+#define NX_LAUNCH(K, GRID)                                                                    \
+  switch (row_bytes) {                                                                        \
+    case 128: hipLaunchKernelGGL(K<128>, GRID, dim3(kThreads), 0, s, a); break;               \
+    case 256: hipLaunchKernelGGL(K<256>, GRID, dim3(kThreads), 0, s, a); break;               \
+    default: hipLaunchKernelGGL(K<512>, GRID, dim3(kThreads), 0, s, a); break;                \
   }
+  if (a.g.inplace) {
+    // Movers are at most the kept rows; the appended rows are max_out_rows - kept.
+    NX_LAUNCH(kv_fill_holes_kernel, grid)
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    NX_LAUNCH(kv_append_kernel, grid)
+  } else {
+    NX_LAUNCH(kv_compact_kernel, grid)
+  }
+#undef NX_LAUNCH
   return hipGetLastError();
 }
 

@@ -135,6 +135,10 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
     ok = ok && u.out_head_stride >= (kept_rows + u.n_append) * d &&
          (kept_rows + u.n_append) * d * esz <= INT32_MAX;
   if (g.block > 1 && u.n_append > 0) ok = ok && u.n_tokens % g.block == 0;
+  if (g.inplace)   // k / v are compacted in place and must hold the appended rows too
+    ok = ok && u.out_k == nullptr && u.out_v == nullptr && u.v != nullptr &&
+         u.kv_head_stride >= (kept_rows + u.n_append) * d &&
+         (kept_rows + u.n_append) * d * esz <= INT32_MAX;
   if (u.n_append > 0) ok = ok && u.app_k != nullptr && u.app_v != nullptr;
   r.valid = ok;
   return r;

@@ -57,6 +57,7 @@ struct Geometry {
   int32_t n_t1, n_t2;    // workspace tile slots per head unit (sized for kMinTokPerBlock)
   int32_t n_kc;          // reservoir_keys chunks per head unit
   int32_t block;         // tokens per selection unit (1, or a block size up to 32)
+  int32_t inplace;       // 1: compaction rearranges k / v in place (hole filling)
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).

@@ -11,26 +11,36 @@ each resident row once and writes the next cache once.  Marshalling only:
 every byte of the path moves inside libnexus.so.
 """
 
+from dataclasses import replace
+
 import torch
 
 from .api import NexusConfig, make_units, new_workspace, nx_evict_batch
 
 
 class StreamingCache:
-    """Ping-pong K/V capacity buffers for `n_layers` layers of one sequence.
+    """K/V capacity buffers for `n_layers` layers of one sequence.
 
     Layout of each buffer: [n_layers, n_kv_heads, capacity, head_dim].
-    `capacity` must hold max(initial tokens, budget + n_append).
+    `capacity` must hold max(initial tokens, budget + n_append).  With
+    inplace=False two buffers ping-pong and the kept rows stay in cache
+    order; with inplace=True one buffer is compacted in place (hole filling:
+    only the kept rows past the kept count move, then the new rows follow), so
+    an event writes about n_append rows per head instead of budget.
     """
 
     def __init__(self, cfg: NexusConfig, n_layers, capacity, budget, n_append, walk_iters,
-                 seed=0, seq_id=0, device="cuda"):
+                 seed=0, seq_id=0, device="cuda", inplace=False):
+        if inplace:
+            cfg = replace(cfg, compact=1)
+        self.inplace = inplace
         self.cfg, self.n_layers, self.capacity = cfg, n_layers, capacity
         self.budget, self.n_append, self.walk_iters = budget, n_append, walk_iters
         self.seed, self.seq_id, self.device = seed, seq_id, device
         shape = (n_layers, cfg.n_kv_heads, capacity, cfg.head_dim)
-        self.k = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(2)]
-        self.v = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(2)]
+        nbuf = 1 if inplace else 2
+        self.k = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(nbuf)]
+        self.v = [torch.zeros(shape, dtype=cfg.dtype, device=device) for _ in range(nbuf)]
         self.q = torch.zeros(n_layers, cfg.n_q_heads, cfg.window, cfg.head_dim, dtype=cfg.dtype,
                              device=device)
         self.app_k = torch.zeros(n_layers, cfg.n_kv_heads, n_append, cfg.head_dim,
@@ -52,10 +62,13 @@ class StreamingCache:
     def _units_for(self, src, n_tokens):
         key = (src, n_tokens)
         if key not in self._units:
-            dst = 1 - src
+            dst = src if self.inplace else 1 - src
             rows = self.capacity * self.cfg.head_dim
+            out_k = None if self.inplace else self.k[dst]
+            out_v = None if self.inplace else self.v[dst]
             items = [dict(q=self.q[l], k=self.k[src][l], v=self.v[src][l], keep=self.keep[l],
-                          out_k=self.k[dst][l], out_v=self.v[dst][l], app_k=self.app_k[l],
+                          out_k=None if out_k is None else out_k[l],
+                          out_v=None if out_v is None else out_v[l], app_k=self.app_k[l],
                           app_v=self.app_v[l], kv_head_stride=rows, out_head_stride=rows,
                           n_tokens=n_tokens, budget=self.budget, n_append=self.n_append,
                           layer=l, seq_id=self.seq_id)
@@ -72,7 +85,8 @@ class StreamingCache:
         units = self._units_for(self.cur, self.n_tokens)
         nx_evict_batch(self.cfg, units, self.n_layers, self.n_tokens, self.walk_iters, self.seed,
                        workspace=self.ws, step=self.step_no, max_out_rows=kept + self.n_append)
-        self.cur = 1 - self.cur
+        if not self.inplace:
+            self.cur = 1 - self.cur
         self.n_tokens = kept + self.n_append
         self.step_no += 1
 

@@ -337,6 +337,84 @@ def test_block_mode_streaming_appends_after_whole_blocks():
             assert torch.equal(kl[l, :, budget * 32:].view(torch.int16), app_k[l].view(torch.int16))
 
 
+# ------------------------------------------- in-place compaction (f4) --
+
+
+def test_inplace_step_matches_copy_and_oracle_layout():
+    """Same kept set as the copy mode; the caches afterwards equal the oracle's
+    hole-filling layout of the original rows (movers from beyond kept)."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    d = gen_layer(wl, device=DEV)
+    n, B = wl.n_tokens, wl.budget
+    cfg_copy = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window)
+    cfg_in = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, compact=nx.NX_COMPACT_INPLACE)
+    ws = _ws(cfg_copy, n, 1, wl.walk_iters)
+    keep_c, ok, ov = nx.nx_evict_step(cfg_copy, d["q"], d["k"], d["v"], n, B, wl.walk_iters, 3,
+                                      workspace=ws, layer=2, step=1)
+    k_in, v_in = d["k"].clone(), d["v"].clone()
+    keep_i, k_out, v_out = nx.nx_evict_step(cfg_in, d["q"], k_in, v_in, n, B, wl.walk_iters, 3,
+                                            workspace=ws, layer=2, step=1)
+    nx.nx_read_device_status(cfg_in, ws)
+    assert k_out.data_ptr() == k_in.data_ptr()
+    assert torch.equal(keep_c, keep_i)
+    kh = d["k"].view(torch.int16).cpu().numpy()
+    vh = d["v"].view(torch.int16).cpu().numpy()
+    for h in range(wl.h_kv):
+        keep = keep_i[h].cpu().numpy()
+        exp_k = nexus.compact_inplace(kh[h], keep)
+        exp_v = nexus.compact_inplace(vh[h], keep)
+        np.testing.assert_array_equal(k_in[h].view(torch.int16).cpu().numpy()[:B], exp_k[:B])
+        np.testing.assert_array_equal(v_in[h].view(torch.int16).cpu().numpy()[:B], exp_v[:B])
+        # the same rows as the copy mode, permuted
+        pos = nexus.inplace_layout(keep, n)
+        np.testing.assert_array_equal(exp_k[pos], ok[h].view(torch.int16).cpu().numpy())
+
+
+def test_inplace_streaming_events_match_oracle():
+    """Six append-256 / evict events, in place, on two layers: every event's
+    cache equals the oracle's hole filling of the pre-event cache with the GPU's
+    keep, and the keep matches the oracle's selection on the GPU's weights."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window)
+    L, A, B = 2, 256, 819
+    n0 = 2048
+    sc = StreamingCache(cfg, L, n0, B, A, wl.walk_iters, seed=8, device=DEV, inplace=True)
+    k0 = torch.randn(L, wl.h_kv, n0, wl.head_dim, device=DEV).to(torch.bfloat16)
+    v0 = torch.randn_like(k0)
+    sc.load(k0, v0, n0)
+    g = torch.Generator(device="cpu").manual_seed(17)
+    for step in range(6):
+        sc.q.copy_(torch.randn(sc.q.shape, generator=g).to(torch.bfloat16))
+        sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g).to(torch.bfloat16))
+        sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g).to(torch.bfloat16))
+        kp, vp = (t.clone() for t in sc.live())
+        n_pre = sc.n_tokens
+        sc.step()
+        nx.nx_read_device_status(sc.cfg, sc.ws)
+        assert sc.n_tokens == B + A
+        kl, vl = sc.live()
+        for l in range(L):
+            keep = sc.keep[l].cpu().numpy()
+            q = sc.q[l]
+            ws1 = _ws(cfg, n_pre, 1, wl.walk_iters)
+            w_gpu = nx.nx_nexus_weights(cfg, q, kp[l], n_pre, wl.walk_iters,
+                                        workspace=ws1).cpu().numpy()
+            _, on_gpu_w = nexus.select_from_weights(w_gpu, B, 8, layer=l, step=step)
+            for h in range(wl.h_kv):
+                # nx_nexus_weights tiles the pre-event cache differently from the batched
+                # call (fp32 sums in another order), so allow a boundary flip.
+                assert gc.overlap_fraction(keep[h], on_gpu_w[h]) >= 1 - 2.0 / B
+                exp_k = nexus.compact_inplace(kp[l, h].view(torch.int16).cpu().numpy(), keep[h],
+                                              sc.app_k[l, h].view(torch.int16).cpu().numpy())
+                np.testing.assert_array_equal(kl[l, h].view(torch.int16).cpu().numpy(),
+                                              exp_k[:B + A])
+                exp_v = nexus.compact_inplace(vp[l, h].view(torch.int16).cpu().numpy(), keep[h],
+                                              sc.app_v[l, h].view(torch.int16).cpu().numpy())
+                np.testing.assert_array_equal(vl[l, h].view(torch.int16).cpu().numpy(),
+                                              exp_v[:B + A])
+
+
 # --------------------------------------------------------------- compaction --
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])
