@@ -176,6 +176,39 @@ def steady(wl, args):
     }))
 
 
+def survival_bench(args):
+    """The survival stream: the same queries and arriving rows under each
+    selection policy; reports the Nexus policy's event rate and every policy's
+    survival of the tracked classes at a few event counts."""
+    from streaming_weighted_sampling_amd.survival import POLICIES, run_survival
+    from workloads import SURVIVAL, survival_event, survival_initial
+    spec = SURVIVAL
+    dev = "cuda"
+    initial = survival_initial(spec, device=dev)
+    curves, ms = {}, {}
+    for policy in POLICIES:
+        r = run_survival(spec, policy, initial, lambda e: survival_event(spec, e, device=dev),
+                         device=dev)
+        at = [e for e in (1, 10, 50, 100, 200, 300, 400) if e <= spec.events]
+        curves[policy] = {f"{off:+.1f}": [round(float(r.survival[e, c]), 5) for e in at]
+                          for c, off in enumerate(spec.offsets)}
+        ms[policy] = r.ms_per_event
+    units = spec.n_streams * spec.h_kv
+    print(json.dumps({
+        "metric": "survival-stream eviction events/sec (16 streams x 8 KV heads), 1 MI355X",
+        "value": round(1e3 / ms["nexus"], 1), "unit": "events/s", "n_gpus": 1,
+        "steps": spec.events, "warmup": 0, "ms_per_step": round(ms["nexus"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"survival_stream {spec.n_streams} streams x {spec.h_kv} KV heads, "
+                               f"N = {spec.n0} -> {spec.budget} + {spec.append}, "
+                               f"{spec.events} events", "head_units": units},
+        "ms_per_event": {p: round(v, 4) for p, v in ms.items()},
+        "survival_at_events": at,
+        "survival": curves,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +219,8 @@ def main():
     ap.add_argument("--steady", action="store_true",
                     help="time the streaming steady-state event (N = B + 256 -> B, 32 layers) "
                          "through StreamingCache instead of the N = 32768 event")
+    ap.add_argument("--survival", action="store_true",
+                    help="run the survival stream (400 events) under every selection policy")
     ap.add_argument("--compact", choices=["copy", "inplace"], default="copy",
                     help="with --steady: copy kept rows to the other buffer, or fill holes in place")
     ap.add_argument("--block", type=int, default=1,
@@ -215,6 +250,9 @@ def main():
         return
 
     wl = WORKLOADS["llama3_8b_stream32"]
+    if args.survival:
+        survival_bench(args)
+        return
     if args.steady:
         steady(wl, args)
         return

@@ -7,5 +7,6 @@ and the HIP-side tests / benchmark import.
 
 from .synth import (  # noqa: F401
     WORKLOADS, Workload, budget_for, gen_layer, gen_model, gen_stream_rows,
-    gen_stream_queries, ragged_lengths, bf16_bits, fill_layer_,
+    gen_stream_queries, ragged_lengths, bf16_bits, fill_layer_, SurvivalSpec, SURVIVAL,
+    survival_initial, survival_event,
 )

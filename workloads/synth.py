@@ -249,3 +249,97 @@ def gen_stream_queries(wl, *, layer, step, device="cpu"):
 def bf16_bits(t):
     """Raw bit patterns of a bf16 tensor as a numpy uint16 array (host copy)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- survival ----
+
+@dataclass(frozen=True)
+class SurvivalSpec:
+    """A long streaming run with tracked tokens ([Nexus] section 3; the check its
+    summary proposes: survival of low-direct-attention tokens over hundreds of
+    eviction events, Nexus against top-K on the same stream).
+
+    Every stream is one Llama-3-8B-shaped layer (GQA 32:8, head_dim 128, bf16)
+    that starts with budget + append resident tokens and then runs `events`
+    append-then-evict events.  All window queries of KV head h carry a common
+    component sqrt(D) * mu_h along a seeded unit direction mu_h, so every key
+    has a persistent logit offset k . mu_h (N(0, 1) for ordinary keys).  The
+    tracked tokens of class c have that offset set to exactly offsets[c];
+    per_class of them per class and KV head sit at seeded positions of the
+    initial cache.
+    """
+    name: str = "survival_stream"
+    index: int = 6
+    n_streams: int = 16
+    h_q: int = 32
+    h_kv: int = 8
+    head_dim: int = 128
+    window: int = 32
+    walk_iters: int = 3
+    dtype: str = "bf16"
+    budget: int = 2048
+    append: int = 256
+    events: int = 400
+    offsets: tuple = (-1.0, -0.5, 0.0, 0.5, 1.0)
+    per_class: int = 32
+
+    @property
+    def group(self):
+        return self.h_q // self.h_kv
+
+    @property
+    def n0(self):
+        return self.budget + self.append
+
+
+SURVIVAL = SurvivalSpec()
+
+
+def _survival_dirs(spec, device):
+    """mu [S, H_kv, D]: the seeded unit directions of every stream and KV head."""
+    g = _gen(device, spec.index, 0x5A, 0)
+    mu = torch.randn(spec.n_streams, spec.h_kv, spec.head_dim, generator=g, device=device)
+    return mu / mu.norm(dim=-1, keepdim=True)
+
+
+def survival_initial(spec, device="cpu"):
+    """Initial caches and class labels of a survival run.
+
+    Returns k, v [S, H_kv, n0, D] (spec dtype) and cls [S, H_kv, n0] int64:
+    the tracked class of each initial token, -1 for ordinary tokens.
+    """
+    S, H, D, n0 = spec.n_streams, spec.h_kv, spec.head_dim, spec.n0
+    n_cls = len(spec.offsets)
+    if n_cls * spec.per_class > n0:
+        raise ValueError("more tracked tokens than initial tokens")
+    mu = _survival_dirs(spec, device)
+    g = _gen(device, spec.index, 0x5B, 0)
+    k = torch.randn(S, H, n0, D, generator=g, device=device)
+    v = torch.randn(S, H, n0, D, generator=g, device=device)
+    cls = torch.full((S, H, n0), -1, dtype=torch.int64, device=device)
+    off = torch.tensor(spec.offsets, dtype=torch.float32, device=device)
+    for s in range(S):
+        for h in range(H):
+            pos = torch.randperm(n0, generator=g, device=device)[:n_cls * spec.per_class]
+            c = torch.arange(n_cls * spec.per_class, device=device) // spec.per_class
+            m = mu[s, h]
+            kt = k[s, h, pos]
+            kt = kt - (kt @ m)[:, None] * m[None, :] + off[c][:, None] * m[None, :]
+            k[s, h, pos] = kt
+            cls[s, h, pos] = c
+    dt = _torch_dtype(spec)
+    return k.to(dt), v.to(dt), cls
+
+
+def survival_event(spec, step, device="cpu"):
+    """Inputs of event `step`: window queries q [S, H_q, W, D] and the rows that
+    arrive after it, app_k and app_v [S, H_kv, append, D] (N(0, 1))."""
+    S, D, G = spec.n_streams, spec.head_dim, spec.group
+    mu = _survival_dirs(spec, device)
+    g = _gen(device, spec.index, 0x5C, step)
+    q = torch.randn(S, spec.h_q, spec.window, D, generator=g, device=device)
+    q += math.sqrt(D) * mu.repeat_interleave(G, dim=1)[:, :, None, :]
+    app_k = torch.randn(S, spec.h_kv, spec.append, D, generator=g, device=device)
+    app_v = torch.randn(S, spec.h_kv, spec.append, D, generator=g, device=device)
+    dt = _torch_dtype(spec)
+    return q.to(dt), app_k.to(dt), app_v.to(dt)
