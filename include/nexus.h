@@ -229,13 +229,17 @@ nx_status nx_read_device_status(const nx_desc* desc);
 const char* nx_status_str(nx_status status);
 
 /*
- * Per-stage timing with HIP events recorded on desc->stream around every
- * kernel launch of later calls (process-wide; not thread-safe).
- * nx_profile_enable(1) clears and starts, nx_profile_enable(0) stops.
+ * Per-stage timing with HIP events recorded on desc->stream around the
+ * kernel launches of later calls (process-wide; not thread-safe).
+ * nx_profile_enable(mask) with mask != 0 clears the records and starts
+ * recording around the stages whose bit (1 << stage index) is set in mask
+ * (-1: every stage); nx_profile_enable(0) stops.  Each recorded launch adds
+ * two event records to the stream, so a timed loop that needs one kernel's
+ * duration should record that stage only.
  * nx_profile_read waits for the recorded events and fills, per stage index,
  * the summed milliseconds and the launch count; returns the number of stages.
  */
-nx_status nx_profile_enable(int32_t enable);
+nx_status nx_profile_enable(int32_t stage_mask);
 int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_stages);
 const char* nx_stage_name(int32_t stage);
 

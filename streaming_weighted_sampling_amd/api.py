@@ -215,8 +215,23 @@ def nx_read_device_status(cfg, workspace, stream=None):
     check(load().nx_read_device_status(ctypes.byref(d)), "device status")
 
 
-def profile_enable(on):
-    load().nx_profile_enable(1 if on else 0)
+def profile_enable(on=True, stages=None):
+    """Start (clearing earlier records) or stop per-stage HIP-event timing.
+
+    stages: names of the stages to time (None: every stage)."""
+    lib = load()
+    if not on:
+        mask = 0
+    elif stages is None:
+        mask = -1
+    else:
+        names = [lib.nx_stage_name(i).decode() for i in range(32)]
+        mask = 0
+        for st in stages:
+            if st not in names:
+                raise ValueError(f"unknown stage {st!r}")
+            mask |= 1 << names.index(st)
+    lib.nx_profile_enable(mask)
 
 
 def profile_read():

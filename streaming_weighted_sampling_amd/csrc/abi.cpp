@@ -128,7 +128,7 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // ---- profiling (process-wide) ----
 struct Profiler {
   std::mutex mu;
-  bool on = false;
+  uint32_t mask = 0;   // bit i: record events around stage i
   struct Rec { int stage; hipEvent_t e0, e1; };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
@@ -144,7 +144,7 @@ Profiler& prof() { static Profiler p; return p; }
 template <typename F>
 hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
   Profiler& p = prof();
-  if (!p.on) return launch();
+  if (!((p.mask >> stage) & 1u)) return launch();
   std::lock_guard<std::mutex> lock(p.mu);
   hipEvent_t e0 = p.get(), e1 = p.get();
   if (e0) (void)hipEventRecord(e0, s);
@@ -383,14 +383,14 @@ const char* nx_status_str(nx_status s) {
   }
 }
 
-nx_status nx_profile_enable(int32_t enable) {
+nx_status nx_profile_enable(int32_t stage_mask) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lock(p.mu);
-  if (enable) {
+  if (stage_mask) {
     for (auto& r : p.recs) { p.pool.push_back(r.e0); p.pool.push_back(r.e1); }
     p.recs.clear();
   }
-  p.on = enable != 0;
+  p.mask = uint32_t(stage_mask);
   return NX_OK;
 }
 
