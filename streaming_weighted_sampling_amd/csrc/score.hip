@@ -367,9 +367,10 @@ __device__ inline void combine_unit(const Args& a, int hu) {
 
 // Walk modes of pass 2 (template parameter, chosen on the host).
 constexpr int kWalkNone = 0;    // H = 0
-constexpr int kWalkFast4 = 1;   // G = 4, G*H <= 32: P_t from register group sums
-constexpr int kWalkFast8 = 2;   // G = 8, G*H <= 32
+constexpr int kWalkFast4 = 1;   // G = 4, H <= 4: P_t from register group sums
+constexpr int kWalkFast8 = 2;   // G = 8, H <= 4
 constexpr int kWalkLds = 3;     // any other shape: walk rows through LDS
+constexpr int kWalkFast4Deep = 4;   // G = 4, 4 < H <= 8
 
 // Pass 2 on one (head unit, tile) item.
 //
@@ -399,11 +400,14 @@ constexpr int probs_smem_bytes() {
          int(sizeof(float)) * 2 * 32 * ((kWalk == kWalkLds ? kMaxWalkRows : 0) + kMaxWalk + kWaves);
 }
 
-template <typename T, int D, int MPW, int kWalk>
+// kBlocks: the call selects blocks of b > 1 tokens (b = 1 kernels carry no
+// block-sum code, which keeps them within 128 VGPRs).
+template <typename T, int D, int MPW, int kWalk, bool kBlocks>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   constexpr bool kHasWalk = kWalk != kWalkNone;
-  constexpr int kMaxT = kWalk == kWalkFast8 ? 4 : kMaxWalk;   // deepest walk of this mode
+  constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep;
+  constexpr int kMaxT = kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4 : kMaxWalk;   // deepest walk
   constexpr int kHalfWaves = 2 * kWaves;
   constexpr int kPairsPerLane = (kMaxT * (kMaxT + 1) / 2 + kHalfWaves - 1) / kHalfWaves;
   auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(smem + GE::kSlotsProbs * GE::kTileBytes);
@@ -457,7 +461,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   // With blocks (b > 1) the values of a block's b lanes are summed (BlockSum_b
   // of Eq. 1); the block's first lane stores the sum at the block index and
   // holds it in LDS, the other lanes hold 0, so the Gram sees block rows.
-  const int blk = g.block;
+  const int blk = kBlocks ? g.block : 1;
   const bool lead = (nn & (blk - 1)) == 0;
   auto put_walk = [&](int s, const float (&pt)[kMaxT]) {
     const int tok = t0 + 32 * s + nn;
@@ -491,26 +495,51 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     }
     put_walk(s, pt);
   };
-  auto gram_step = [&](int s) {
+  // The Gram step is split into its LDS reads (issued before the K fragment
+  // reads of the next sub-tile) and its accumulation (after that sub-tile's
+  // MFMA chain has been issued), so that neither waits on the critical path.
+  // Every half-wave runs kcap iterations (uniform); pairs past n_pairs read
+  // in-bounds rows and are not accumulated.
+  const int kcap = (n_pairs + kHalfWaves - 1) / kHalfWaves;
+  auto gram_load = [&](int s, float (&gx)[kPairsPerLane], float (&gy)[kPairsPerLane]) {
     const float* sp = &s_pt[s & 1][0][nn];
 #pragma unroll
     for (int k = 0; k < kPairsPerLane; ++k) {
-      if (pg + kHalfWaves * k < n_pairs) {
+      if (k < kcap) {
         const uint32_t t = (pairs >> (6 * k + 3)) & 7, t2 = (pairs >> (6 * k)) & 7;
-        const float x = sp[32 * t];
-        const float y = t2 == t ? 1.f : sp[32 * t2];
-        gacc[k] = fmaf(x, y, gacc[k]);
+        gx[k] = sp[32 * t];
+        gy[k] = sp[32 * t2];
       }
     }
   };
-  // a_j of sub-tile s: M-tile-ordered sum of the partials (role 1, half 0).
-  auto a_final = [&](int s) {
-    if (role != 1 || hh != 0) return;
+  auto gram_add = [&](const float (&gx)[kPairsPerLane], const float (&gy)[kPairsPerLane]) {
+#pragma unroll
+    for (int k = 0; k < kPairsPerLane; ++k) {
+      if (k < kcap) {
+        const uint32_t t = (pairs >> (6 * k + 3)) & 7, t2 = (pairs >> (6 * k)) & 7;
+        const float f = fmaf(gx[k], t2 == t ? 1.f : gy[k], gacc[k]);
+        gacc[k] = pg + kHalfWaves * k < n_pairs ? f : gacc[k];
+      }
+    }
+  };
+  auto gram_step = [&](int s) {
+    float gx[kPairsPerLane], gy[kPairsPerLane];
+    gram_load(s, gx, gy);
+    gram_add(gx, gy);
+  };
+  // a_j of sub-tile s: M-tile-ordered sum of the partials (role 1, half 0),
+  // likewise split into the reads and the sum and store.
+  auto a_load = [&](int s, float (&la)[kWaves]) {
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r) la[r] = s_a[s & 1][r][nn];
+  };
+  auto a_store = [&](int s, const float (&la)[kWaves]) {
+    if (hh != 0) return;
     const int tok = t0 + 32 * s + nn;
-    float sum = s_a[s & 1][0][nn];
+    float sum = la[0];
 #pragma unroll
     for (int r = 1; r < kWaves; ++r)
-      if (r < row_roles) sum += s_a[s & 1][r][nn];
+      if (r < row_roles) sum += la[r];
     if (blk == 1) {
       if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
     } else {
@@ -518,14 +547,27 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       if (lead && tok < u.n) a_out.stf(uint32_t((tok / blk) * 4), sum);
     }
   };
+  auto a_final = [&](int s) {
+    if (role != 1) return;
+    float la[kWaves];
+    a_load(s, la);
+    a_store(s, la);
+  };
 
   sweep_tiles<T, D, GE::kSlotsProbs, 2>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
-    // Lagged work on slots the previous barrier made visible.
-    if (st > 0) {
-      a_final(st - 1);
-      if constexpr (kWalk == kWalkFast4 || kWalk == kWalkFast8) {
-        gram_step(st - 1);
-      } else if constexpr (kWalk == kWalkLds) {
+    // Lagged work on slots the previous barrier made visible: the LDS reads
+    // now, ahead of the K fragment reads; the sums after the MFMA issue.
+    // (The LDS walk mode keeps its lagged work in one piece, ahead of the
+    // fragment reads: splitting it costs it occupancy.)
+    constexpr bool kSplitLag = kWalk != kWalkLds;
+    const bool lag = st > 0;
+    float la[kWaves], gx[kPairsPerLane], gy[kPairsPerLane];
+    if (lag) {
+      if constexpr (kSplitLag) {
+        if (role == 1) a_load(st - 1, la);
+        if constexpr (kFastWalk) gram_load(st - 1, gx, gy);
+      } else {
+        a_final(st - 1);
         walk_lds(st - 1);
         if (st > 1) gram_step(st - 2);
       }
@@ -536,22 +578,33 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
       const int mt = role + kWaves * i;
+      auto consume_lag = [&] {
+        if constexpr (kSplitLag) {
+          if (role == 1) a_store(st - 1, la);
+          if constexpr (kFastWalk) gram_add(gx, gy);
+        }
+      };
+      if (mt >= n_mt && i == 0 && lag) consume_lag();
       if (mt < n_mt) {
         const floatx16_t acc = mfma_tile<T, D>(qf[i], kf);
+        if (i == 0 && lag) consume_lag();
         float e[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          e[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
-          tp += e[v];
-        }
-        if constexpr (kWalk == kWalkFast4 || kWalk == kWalkFast8) {
+        for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(fmaf(acc[v], c, -bt[i][v]));
+        // Sums of the 4-row groups 8q + 4*half .. +3, then of the lane's 16
+        // rows, as a tree (no chain of 16 dependent adds).
+        float sq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sq[q] = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
+        tp += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+        if constexpr (kFastWalk) {
           if (i == 0 && role == 0) {
             // Group sums S over rows 8q + 4*half .. +3; after the swap every
             // lane holds S for q' = 2q (half 0) and q' = 2q + 1 (half 1).
             float grp[8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float sg = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
+              const float sg = sq[q];
               const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sg),
                                                                __float_as_uint(sg), false, false);
               grp[2 * q] = __uint_as_float(sw[0]);
@@ -561,7 +614,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
               float pt[kMaxT];
 #pragma unroll
               for (int t = 0; t < kMaxT; ++t)
-                pt[t] = wf * (kWalk == kWalkFast4 ? grp[t] : grp[2 * t] + grp[2 * t + 1]);
+                pt[t] = wf * (kWalk != kWalkFast8 ? grp[t] : grp[2 * t] + grp[2 * t + 1]);
               put_walk(st, pt);
             }
           }
@@ -623,18 +676,19 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 }
 
 // Pass 2: one workgroup per (tile, head unit).
-template <typename T, int D, int MPW, int kWalk>
+template <typename T, int D, int MPW, int kWalk, bool kBlocks>
 __global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
   __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk>()];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
-  if (u.valid) probs_item<T, D, MPW, kWalk>(a, u, hu, tile, smem);
+  if (u.valid) probs_item<T, D, MPW, kWalk, kBlocks>(a, u, hu, tile, smem);
 }
 
 int walk_mode(const Geometry& g) {
   if (g.walk == 0) return kWalkNone;
-  if (g.walk_rows <= 32 && g.group == 4) return kWalkFast4;
-  if (g.walk_rows <= 32 && g.group == 8) return kWalkFast8;
+  if (g.walk <= 4 && g.group == 4) return kWalkFast4;
+  if (g.walk <= 4 && g.group == 8) return kWalkFast8;
+  if (g.walk_rows <= 32 && g.group == 4) return kWalkFast4Deep;
   return kWalkLds;
 }
 
@@ -644,23 +698,32 @@ int mtiles_per_wave(const Geometry& g) {
   return per <= 1 ? 1 : per <= 2 ? 2 : 4;
 }
 
+template <int MPW, typename T, int D, bool kBlocks>
+void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
+  switch (walk_mode(a.g)) {
+    case kWalkNone:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkNone, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      break;
+    case kWalkFast4:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      break;
+    case kWalkFast8:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast8, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      break;
+    case kWalkFast4Deep:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4Deep, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkLds, kBlocks>), grid, dim3(kThreads), 0, s, a);
+  }
+}
+
 template <bool kProbs, int MPW, typename T, int D>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   const dim3 grid(a.g.n_tmax, a.g.n_hu);
   if constexpr (kProbs) {
-    switch (walk_mode(a.g)) {
-      case kWalkNone:
-        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkNone>), grid, dim3(kThreads), 0, s, a);
-        break;
-      case kWalkFast4:
-        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4>), grid, dim3(kThreads), 0, s, a);
-        break;
-      case kWalkFast8:
-        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast8>), grid, dim3(kThreads), 0, s, a);
-        break;
-      default:
-        hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkLds>), grid, dim3(kThreads), 0, s, a);
-    }
+    if (a.g.block > 1) launch_probs<MPW, T, D, true>(a, grid, s);
+    else launch_probs<MPW, T, D, false>(a, grid, s);
   } else {
     hipLaunchKernelGGL((score_stats_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
   }
