@@ -241,7 +241,8 @@ def unit_uniforms(n_tokens, unit_id, layer, step, seed):
 
 def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
                step=0, seq_id=0, lam=LAMBDA_DEFAULT, eps=EPS_TIE_DEFAULT,
-               n_sink=0, n_recent=0, heads=None, n_avg=1, block=1):
+               n_sink=0, n_recent=0, heads=None, n_avg=1, block=1, head_budgets=None,
+               ada_floor=None, head_cap=None):
     """One eviction event for one (sequence, layer): every KV head.
 
     [Nexus] section 2.1 (streaming view): keep `budget` of the N resident
@@ -253,7 +254,11 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
     units scored, sampled and kept are blocks of b tokens (section 2.1); then
     budget, n_sink and n_recent count blocks, keep holds block indices, and
     out_k / out_v are the rows of the kept blocks in ascending block order.
-    Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v.
+    Per-head budgets (appendix 10): head_budgets gives head h's kept count;
+    ada_floor = f (not None) computes them with ada_head_budgets from the
+    weights of all heads (capacity head_cap, default budget).
+    Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v,
+    and "budgets" (the per-head kept counts used).
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -270,26 +275,35 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
         raise ValueError("block must be >= 1")
     g = h_q // h_kv
     heads = range(h_kv) if heads is None else heads
-    out = {"w": {}, "keys": {}, "keep": {}, "out_k": {}, "out_v": {}}
-    for h in heads:
+    out = {"w": {}, "keys": {}, "keep": {}, "out_k": {}, "out_v": {}, "budgets": {}}
+    weights = {}
+    for h in (range(h_kv) if ada_floor is not None else heads):
         q_grp = as_f64(q[h * g:(h + 1) * g], dtype)
-        kh = as_f64(k[h], dtype)
-        sc = head_weights(q_grp, kh, walk_iters, lam, eps, block)
-        nu = sc["w"].shape[-1]
-        keys = head_keys(sc["w"], nu, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
+        weights[h] = head_weights(q_grp, as_f64(k[h], dtype), walk_iters, lam, eps, block)["w"]
+    if ada_floor is not None:
+        head_budgets = ada_head_budgets(np.stack([weights[h] for h in range(h_kv)]), budget,
+                                        ada_floor, budget if head_cap is None else head_cap)
+    for h in heads:
+        w = weights[h]
+        nu = w.shape[-1]
+        b_h = budget if head_budgets is None else int(head_budgets[h])
+        if n_sink + n_recent > b_h:
+            raise ValueError("forced slots exceed the head's budget")
+        keys = head_keys(w, nu, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
                          n_recent)
-        keep = select_top(keys, budget)
+        keep = select_top(keys, b_h)
         rows = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in keep])
-        out["w"][h] = sc["w"]
+        out["w"][h] = w
         out["keys"][h] = keys
         out["keep"][h] = keep
+        out["budgets"][h] = b_h
         out["out_k"][h] = k[h][rows]
         out["out_v"][h] = v[h][rows]
     return out
 
 
 def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
-                        n_sink=0, n_recent=0, n_avg=1):
+                        n_sink=0, n_recent=0, n_avg=1, head_budgets=None):
     """Reservoir selection on given weights w: [H_kv, N] (any precision).
 
     The oracle run on someone else's scores: same Philox stream, fp64 keys,
@@ -302,8 +316,43 @@ def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
     for h in range(h_kv):
         keys[h] = head_keys(w[h], n, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
                             n_recent)
-        keeps.append(select_top(keys[h], budget))
+        keeps.append(select_top(keys[h], budget if head_budgets is None else
+                                int(head_budgets[h])))
     return keys, keeps
+
+
+# ------------------------------------------------- per-head budgets ----
+
+def ada_head_budgets(w, budget, floor, cap=None):
+    """Per-head budgets of one item: [Nexus] appendix 10 layers the
+    head-adaptive allocation of Ada-KV (its reference [12]) on a score: a fixed
+    budget for the layer, redistributed over its heads.  The pages give only
+    that aim; this is the allocation of Ada-KV itself, a top-K over the
+    scores of all heads together, on the Nexus weights, with a per-head floor:
+
+      Bbar = min(budget, N), f = min(floor, Bbar), K = H (Bbar - f);
+      order all (head h, unit j) by weight, largest first (weights <= 0 all
+      count as 0), equal weights: the smaller head first;
+      c_h = how many of the first K belong to head h;
+      B_h = min(f + c_h, cap, N)   (cap: the per-head capacity, default budget).
+
+    w: [H, N] weights of the item's KV heads (any precision).  Returns int64 [H].
+    """
+    w = np.asarray(w, dtype=np.float64)
+    h_kv, n = w.shape
+    if budget < 1 or floor < 0:
+        raise ValueError("budget must be >= 1 and floor >= 0")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite Nexus weight")
+    cap = budget if cap is None else cap
+    bbar = min(budget, n)
+    f = min(floor, bbar)
+    k = h_kv * (bbar - f)
+    val = np.where(w > 0, w, 0.0).ravel()
+    head = np.repeat(np.arange(h_kv), n)
+    order = np.lexsort((head, -val))          # weight descending, then head ascending
+    counts = np.bincount(head[order[:k]], minlength=h_kv)
+    return np.minimum(np.minimum(f + counts, cap), n).astype(np.int64)
 
 
 # ------------------------------------------------- in-place compaction ----
