@@ -75,10 +75,13 @@ def budget_units(wl, block):
     return wl.budget if block == 1 else max(1, round(wl.budget / block))
 
 
-def build_batch(wl, device, block=1):
+def build_batch(wl, device, block=1, head_cap=0):
+    """The headline batch; head_cap > 0 sizes keep and output rows for per-head
+    budgets of up to head_cap units (head_budget arrays included)."""
     L, H, N, D = wl.n_layers, wl.h_kv, wl.n_tokens, wl.head_dim
     B = budget_units(wl, block)
-    R = min(B * block, N)            # kept rows per head
+    C = head_cap if head_cap > 0 else B
+    R = min(C * block, N)            # kept rows per head (capacity)
     q = torch.empty(L, wl.h_q, wl.window, D, dtype=torch.bfloat16, device=device)
     k = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
     v = torch.empty(L, H, N, D, dtype=torch.bfloat16, device=device)
@@ -91,15 +94,17 @@ def build_batch(wl, device, block=1):
         k[layer].copy_(k32)
         v[layer].copy_(v32)
     del q32, k32, v32
-    keep = torch.empty(L, H, B, dtype=torch.int32, device=device)
+    keep = torch.empty(L, H, C, dtype=torch.int32, device=device)
     out_k = torch.empty(L, H, R, D, dtype=torch.bfloat16, device=device)
     out_v = torch.empty_like(out_k)
+    head_budget = torch.zeros(L, H, dtype=torch.int32, device=device)
     items = [dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=out_k[l], out_v=out_v[l],
-                  kv_head_stride=N * D, out_head_stride=R * D, n_tokens=N, budget=B, layer=l)
+                  kv_head_stride=N * D, out_head_stride=R * D, n_tokens=N, budget=B, layer=l,
+                  head_cap=head_cap, head_budget=head_budget[l] if head_cap > 0 else None)
              for l in range(L)]
     units = nx.make_units(items, device=device)
     return dict(q=q, k=k, v=v, keep=keep, out_k=out_k, out_v=out_v, units=units, budget=B,
-                rows=R)
+                rows=R, head_budget=head_budget)
 
 
 def cpu_baseline(wl, data, budget_s, n_avg=1, block=1):
@@ -221,6 +226,9 @@ def main():
                          "through StreamingCache instead of the N = 32768 event")
     ap.add_argument("--survival", action="store_true",
                     help="run the survival stream (400 events) under every selection policy")
+    ap.add_argument("--heads", choices=["uniform", "alloc"], default="uniform",
+                    help="per-head budgets: uniform B, or allocated over the heads of each "
+                         "layer (floor B/5, capacity 2B)")
     ap.add_argument("--compact", choices=["copy", "inplace"], default="copy",
                     help="with --steady: copy kept rows to the other buffer, or fill holes in place")
     ap.add_argument("--block", type=int, default=1,
@@ -256,9 +264,13 @@ def main():
     if args.steady:
         steady(wl, args)
         return
-    data = build_batch(wl, dev, args.block)
+    heads = args.heads == "alloc"
+    cap = 2 * budget_units(wl, args.block) if heads else 0
+    data = build_batch(wl, dev, args.block, head_cap=cap)
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
-                         n_avg=args.n_avg, block=args.block)
+                         n_avg=args.n_avg, block=args.block,
+                         head_alloc=nx.NX_HEADS_ALLOC if heads else nx.NX_HEADS_UNIFORM,
+                         head_floor=data["budget"] // 5 if heads else 0)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -288,7 +300,8 @@ def main():
     # sweep; per kept row 4*d*e bytes (K and V read and written) plus a 4-byte index.
     d, e = wl.head_dim, 2
     k_bytes = tokens * d * e
-    compact_bytes = units * (data["rows"] * 4 * d * e + data["budget"] * 4)
+    kept_rows = min(data["budget"] * args.block, wl.n_tokens)   # per head on average
+    compact_bytes = units * (kept_rows * 4 * d * e + data["budget"] * 4)
     qk_flops = tokens * 2 * wl.group * wl.window * d
     # (algorithmic amount per launch, unit, peak, bound) of the stages that move the bulk.
     work = {
@@ -334,7 +347,7 @@ def main():
                                "heads, GQA 32:8, head_dim 128, W=32, H=3, B=6554)",
                    "layers": wl.n_layers, "kv_heads": wl.h_kv, "n_tokens": wl.n_tokens,
                    "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters,
-                   "n_avg": args.n_avg, "block": args.block,
+                   "n_avg": args.n_avg, "block": args.block, "heads": args.heads,
                    "budget_units": data["budget"]},
         "step_latency_ms": round(ms_per_step, 4),
         "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},

@@ -109,11 +109,37 @@ typedef struct nx_desc {
                                appended rows go to kept, kept + 1, ...; out_k / out_v must be
                                NULL and kv_head_stride must hold kept + n_append rows; tokens
                                only (block <= 1).  Other values: NX_EINVAL. */
+  int32_t head_alloc;       /* per-head budgets (appendix 10: a layer budget shared unevenly by
+                               the heads), nx_evict_batch and nx_head_budgets only:
+                               NX_HEADS_UNIFORM (0): every head keeps min(budget, units).
+                               NX_HEADS_GIVEN (1): head h of an item keeps
+                               min(head_budget[h], units) units, 1 <= head_budget[h] <= cap.
+                               NX_HEADS_ALLOC (2): the library writes head_budget[h] =
+                               min(f + c_h, cap, units), f = min(head_floor, Bbar),
+                               Bbar = min(budget, units), c_h = the number of head h's units
+                               among the n_kv_heads * (Bbar - f) largest Nexus weights of all
+                               heads of the item (weights <= 0 count as 0; equal weights: the
+                               lower head first), the head-adaptive rule of Ada-KV that
+                               appendix 10 cites; then every head keeps its allocation.
+                               With 1 or 2: cap = the item's head_cap (0: budget), keep rows
+                               hold cap entries (entries past a head's kept count are set to
+                               -1), out_head_stride >= cap rows (cap * block with blocks),
+                               n_append must be 0, and head_budget must be non-NULL.  A
+                               violation on the device marks the item bad.  Other values:
+                               NX_EINVAL; nx_evict_step, nx_reservoir_select and
+                               nx_kv_compact need 0. */
+  int32_t head_floor;       /* NX_HEADS_ALLOC: per-head floor f >= 0 (units); an allocation
+                               below n_sink + n_recent marks the item bad */
   int32_t reserved;         /* must be 0 */
 } nx_desc;
 
 #define NX_COMPACT_COPY 0
 #define NX_COMPACT_INPLACE 1
+
+#define NX_HEADS_UNIFORM 0
+#define NX_HEADS_GIVEN 1
+#define NX_HEADS_ALLOC 2
+#define NX_MAX_ALLOC_HEADS 256   /* n_kv_heads limit of NX_HEADS_ALLOC */
 
 #define NX_MAX_AVG 64
 #define NX_TOPK (-1)
@@ -145,7 +171,9 @@ typedef struct nx_unit {
   int32_t n_append;
   uint32_t layer;
   uint32_t seq_id;
-  uint32_t reserved;
+  int32_t head_cap;         /* per-head capacity with desc->head_alloc != 0 (0: budget) */
+  int32_t* head_budget;     /* [n_kv_heads] int32 device array with desc->head_alloc != 0:
+                               read (NX_HEADS_GIVEN) or written (NX_HEADS_ALLOC); else ignored */
 } nx_unit;
 
 /*
@@ -209,6 +237,17 @@ nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void
 nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tokens,
                               int32_t budget, uint64_t seed, int32_t* out_keep_idx,
                               double* out_keys);
+
+/*
+ * Per-head allocation only (desc->head_alloc == NX_HEADS_ALLOC, appendix 10) on
+ * given weights w [n_kv_heads, n_tokens] fp32 of one item: writes
+ * out_head_budget [n_kv_heads] int32 (device) by the rule under nx_desc.head_alloc
+ * with layer budget `budget` per head and capacity head_cap (0: budget).
+ * n_kv_heads <= NX_MAX_ALLOC_HEADS.  Errors: NX_EINVAL, NX_EWORKSPACE,
+ * NX_EUNSUPPORTED, NX_EHIP.
+ */
+nx_status nx_head_budgets(const nx_desc* desc, const float* w, int32_t n_tokens, int32_t budget,
+                          int32_t head_cap, int32_t* out_head_budget);
 
 /*
  * Compaction stage only (section 2.1: continue with K_S, V_S): bit copies

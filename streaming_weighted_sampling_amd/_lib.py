@@ -15,6 +15,10 @@ NX_ENONFINITE = -5
 NX_EHIP = -6
 NX_COMPACT_COPY = 0
 NX_COMPACT_INPLACE = 1
+NX_HEADS_UNIFORM = 0
+NX_HEADS_GIVEN = 1
+NX_HEADS_ALLOC = 2
+NX_MAX_ALLOC_HEADS = 256
 NX_BF16 = 0
 NX_F32 = 1
 
@@ -42,6 +46,8 @@ class NxDesc(ctypes.Structure):
         ("n_avg", ctypes.c_int32),
         ("block", ctypes.c_int32),
         ("compact", ctypes.c_int32),
+        ("head_alloc", ctypes.c_int32),
+        ("head_floor", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -63,7 +69,8 @@ class NxUnit(ctypes.Structure):
         ("n_append", ctypes.c_int32),
         ("layer", ctypes.c_uint32),
         ("seq_id", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("head_cap", ctypes.c_int32),
+        ("head_budget", ctypes.c_void_p),
     ]
 
 
@@ -79,6 +86,7 @@ SIGNATURES = {
     "nx_nexus_weights": (_I32, [_P(NxDesc), _VP, _VP, _I32, _I32, _VP]),
     "nx_reservoir_select": (_I32, [_P(NxDesc), _VP, _I32, _I32, ctypes.c_uint64, _VP, _VP]),
     "nx_kv_compact": (_I32, [_P(NxDesc), _VP, _VP, _VP, _I32, _I32, _VP, _VP]),
+    "nx_head_budgets": (_I32, [_P(NxDesc), _VP, _I32, _I32, _I32, _VP]),
     "nx_read_device_status": (_I32, [_P(NxDesc)]),
     "nx_status_str": (ctypes.c_char_p, [_I32]),
     "nx_profile_enable": (_I32, [_I32]),

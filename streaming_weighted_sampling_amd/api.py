@@ -34,6 +34,8 @@ class NexusConfig:
     n_avg: int = 1            # [Nexus] Eq. 6 averaging count; TOPK (-1) = deterministic limit
     block: int = 1            # [Nexus] Eq. 1 block size b: 1 = tokens, else 2..32 (power of 2)
     compact: int = 0          # 0: copy kept rows to new buffers; 1: compact k / v in place
+    head_alloc: int = 0       # appendix 10 per-head budgets: 0 uniform, 1 given, 2 allocated
+    head_floor: int = 0       # per-head floor of the allocation (head_alloc = 2)
 
     def units(self, n_tokens):
         """Selection units of a head: tokens, or ceil(n_tokens / block) blocks."""
@@ -58,6 +60,8 @@ class NexusConfig:
         d.n_avg = self.n_avg
         d.block = self.block
         d.compact = self.compact
+        d.head_alloc = self.head_alloc
+        d.head_floor = self.head_floor
         d.layer = layer
         d.step = step
         d.seq_id = seq_id
@@ -168,6 +172,19 @@ def nx_reservoir_select(cfg, w, budget, seed, *, workspace, layer=0, step=0, seq
     return keep, keys
 
 
+def nx_head_budgets(cfg, w, budget, *, workspace, head_cap=0, out=None, stream=None):
+    """Per-head budgets allocated on given weights w [H_kv, N] fp32 of one item
+    (cfg.head_alloc must be 2); returns int32 [H_kv] on w's device."""
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 2:
+        raise ValueError("w must be a contiguous [n_kv_heads, n_tokens] float32 tensor")
+    if out is None:
+        out = torch.empty(cfg.n_kv_heads, dtype=torch.int32, device=w.device)
+    d = cfg.desc(workspace, stream=stream)
+    check(load().nx_head_budgets(ctypes.byref(d), _ptr(w), w.shape[1], budget, head_cap,
+                                 _ptr(out)), "nx_head_budgets")
+    return out
+
+
 def nx_kv_compact(cfg, k, v, keep, n_tokens, budget, *, workspace, out_k=None, out_v=None,
                   stream=None):
     kst = _check_cache(cfg, k, "k")
@@ -198,6 +215,8 @@ def make_units(items, device="cuda"):
         rec.n_append = it.get("n_append", 0)
         rec.layer = it.get("layer", 0)
         rec.seq_id = it.get("seq_id", 0)
+        rec.head_cap = it.get("head_cap", 0)
+        rec.head_budget = _ptr(it.get("head_budget"))
     host = torch.frombuffer(bytearray(arr), dtype=torch.uint8)
     return host.to(device)
 

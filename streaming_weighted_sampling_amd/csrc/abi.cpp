@@ -31,6 +31,8 @@ nx_status check_desc(const nx_desc* d) {
   if (d->block < 0) return NX_EINVAL;
   if (d->compact != NX_COMPACT_COPY && d->compact != NX_COMPACT_INPLACE) return NX_EINVAL;
   if (d->reserved != 0) return NX_EINVAL;
+  if (d->head_alloc < NX_HEADS_UNIFORM || d->head_alloc > NX_HEADS_ALLOC || d->head_floor < 0)
+    return NX_EINVAL;
   if (d->compact == NX_COMPACT_INPLACE && d->block > 1) return NX_EUNSUPPORTED;
   if (d->block > 1 && (d->block > 32 || (d->block & (d->block - 1)) != 0)) return NX_EUNSUPPORTED;
   if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
@@ -68,6 +70,11 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->walk_rows = group * walk;
   g->block = d->block > 1 ? d->block : 1;
   g->inplace = d->compact == NX_COMPACT_INPLACE;
+  g->head_alloc = d->head_alloc;
+  // The allocation selects over all heads' units of an item at once.
+  if (d->head_alloc == NX_HEADS_ALLOC &&
+      (d->n_kv_heads > NX_MAX_ALLOC_HEADS || int64_t(d->n_kv_heads) * max_tokens >= (int64_t(1) << 31)))
+    return NX_EUNSUPPORTED;
   g->dtype = d->dtype;
   g->n_hu = int32_t(n_hu);
   g->max_tokens = max_tokens;
@@ -98,6 +105,7 @@ nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
   a->coef = reinterpret_cast<float*>(base + L.coef);
   a->keys = reinterpret_cast<uint64_t*>(base + L.keys);
   a->selp = reinterpret_cast<uint64_t*>(base + L.selp);
+  a->ahist = reinterpret_cast<uint32_t*>(base + L.ahist);
   return NX_OK;
 }
 
@@ -113,6 +121,7 @@ Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
   a.step = d->step;
   a.seed = seed;
   a.n_avg = d->n_avg == 0 ? 1 : d->n_avg;
+  a.head_floor = d->head_floor;
   return a;
 }
 
@@ -163,6 +172,9 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
   const bool fused = max_units <= kFusedMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
+  // The stages from the keys on read the per-head budgets of this call.
+  Args live = a;
+  live.heads_live = 1;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {
       case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
@@ -170,18 +182,24 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
       case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
       case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
       case kStageReservoirKeys:
+        // Per-head budgets are settled before any stage that reads them.
+        if (a.g.head_alloc != NX_HEADS_UNIFORM && !a.stop_after_weights) {
+          err = run_stage(kStageHeadBudget, s, [&] { return launch_head_budget(a, s); });
+          if (err != hipSuccess) break;
+        }
         if (fused)
-          err = run_stage(kStageEstimateKeys, s, [&] { return launch_estimate_keys(a, s); });
+          err = run_stage(kStageEstimateKeys, s, [&] { return launch_estimate_keys(live, s); });
         else
-          err = run_stage(st, s, [&] { return launch_reservoir_keys(a, s); });
+          err = run_stage(st, s, [&] { return launch_reservoir_keys(live, s); });
         break;
       case kStageTopbSelect:
         if (fused)
-          err = run_stage(kStageSampleSelect, s, [&] { return launch_sample_select(a, s); });
+          err = run_stage(kStageSampleSelect, s, [&] { return launch_sample_select(live, s); });
         else
-          err = run_stage(st, s, [&] { return launch_topb_select(a, s); });
+          err = run_stage(st, s, [&] { return launch_topb_select(live, s); });
         break;
-      case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(a, s); }); break;
+      case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(live, s); }); break;
+      case kStageHeadBudget: err = run_stage(st, s, [&] { return launch_head_budget(a, s); }); break;
       default: break;
     }
   }
@@ -225,6 +243,7 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
+  if (desc->head_alloc != NX_HEADS_UNIFORM) return NX_EINVAL;   // batch calls only
   const bool inplace = desc->compact == NX_COMPACT_INPLACE;
   if (!q_window || !k_cache || !v_cache || !out_keep_idx) return NX_EINVAL;
   if (inplace ? (out_k || out_v) : (!out_k || !out_v)) return NX_EINVAL;
@@ -281,6 +300,7 @@ nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
+  g.head_alloc = NX_HEADS_UNIFORM;   // weights do not depend on the budgets
   if (!q_window || !k_cache || !out_w) return NX_EINVAL;
   nx_unit u = single_unit(desc, q_window, k_cache, nullptr, nullptr, nullptr, nullptr, n_tokens,
                           n_tokens);
@@ -300,6 +320,7 @@ nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tok
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
+  if (desc->head_alloc != NX_HEADS_UNIFORM) return NX_EINVAL;   // batch calls only
   g.block = 1;   // the given weights are the selection units
   if (!w || !out_keep_idx) return NX_EINVAL;
   if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
@@ -314,12 +335,34 @@ nx_status nx_reservoir_select(const nx_desc* desc, const float* w, int32_t n_tok
   return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageReservoirKeys, kStageTopbSelect);
 }
 
+nx_status nx_head_budgets(const nx_desc* desc, const float* w, int32_t n_tokens, int32_t budget,
+                          int32_t head_cap, int32_t* out_head_budget) {
+  Geometry g{};
+  nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
+  if (st != NX_OK) return st;
+  g.block = 1;   // the given weights are the selection units
+  if (desc->head_alloc != NX_HEADS_ALLOC) return NX_EINVAL;
+  if (!w || !out_head_budget || budget < 1 || head_cap < 0) return NX_EINVAL;
+  if (desc->n_sink + desc->n_recent > (head_cap > 0 ? head_cap : budget)) return NX_EINVAL;
+  // The scoring inputs are not used; q and k only need to be non-null.
+  nx_unit u = single_unit(desc, w, w, nullptr, nullptr, nullptr, nullptr, n_tokens, budget);
+  u.kv_head_stride = int64_t(n_tokens) * desc->head_dim;
+  u.head_cap = head_cap;
+  u.head_budget = out_head_budget;
+  Args a = base_args(desc, g, 0);
+  if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
+  a.single = u;
+  a.w_in = w;
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageHeadBudget, kStageHeadBudget);
+}
+
 nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_cache,
                         const int32_t* keep_idx, int32_t n_tokens, int32_t budget, void* out_k,
                         void* out_v) {
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, 0, &g);
   if (st != NX_OK) return st;
+  if (desc->head_alloc != NX_HEADS_UNIFORM) return NX_EINVAL;   // batch calls only
   const bool inplace = desc->compact == NX_COMPACT_INPLACE;
   if (!k_cache || !v_cache || !keep_idx) return NX_EINVAL;
   if (inplace ? (out_k || out_v) : (!out_k || !out_v)) return NX_EINVAL;
@@ -416,7 +459,8 @@ int32_t nx_profile_read(float* stage_ms, int32_t* stage_launches, int32_t max_st
 const char* nx_stage_name(int32_t stage) {
   static const char* names[kNumStages] = {"score_stats", "score_combine",  "score_probs",
                                           "walk_coef",   "reservoir_keys", "topb_select",
-                                          "kv_compact",  "sample_select", "estimate_keys"};
+                                          "kv_compact",  "sample_select", "estimate_keys",
+                                          "head_budget"};
   return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
 }
 

@@ -91,6 +91,7 @@ struct HeadUnit {
   const char* app_v;
   int32_t n, budget, kept, n_append;
   int32_t nu;          // selection units: ceil(n / block); kept = min(budget, nu) of them
+  int32_t cap;         // keep row length: budget, or the per-head capacity
   uint32_t layer, unit_id;
   int32_t h;
   bool valid;
@@ -112,25 +113,35 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   HeadUnit r;
   r.h = h;
   r.n = u.n_tokens;
-  r.budget = u.budget;
+  // Per-head budgets: keep rows of `cap` entries; the head's own budget (given
+  // ones at every stage, allocated ones once this call's allocation is in
+  // place; before that, the capacity).
+  const bool per_head = g.head_alloc != NX_HEADS_UNIFORM;
+  const bool budgets_in = a.heads_live || g.head_alloc == NX_HEADS_GIVEN;
+  r.cap = per_head && u.head_cap > 0 ? u.head_cap : u.budget;
+  r.budget = !per_head ? u.budget
+             : (budgets_in && u.head_budget != nullptr) ? u.head_budget[h] : r.cap;
   r.nu = (u.n_tokens + g.block - 1) / g.block;
-  r.kept = u.budget < r.nu ? u.budget : r.nu;
+  r.kept = r.budget < r.nu ? r.budget : r.nu;
   r.n_append = u.n_append;
   r.layer = u.layer;
   r.unit_id = u.seq_id * uint32_t(g.h_kv) + uint32_t(h);
   r.q = static_cast<const char*>(u.q) + int64_t(h) * g.group * g.window * d * esz;
   r.k = static_cast<const char*>(u.k) + int64_t(h) * u.kv_head_stride * esz;
   r.v = u.v ? static_cast<const char*>(u.v) + int64_t(h) * u.kv_head_stride * esz : nullptr;
-  r.keep = u.keep ? u.keep + int64_t(h) * u.budget : nullptr;
+  r.keep = u.keep ? u.keep + int64_t(h) * r.cap : nullptr;
   r.out_k = u.out_k ? static_cast<char*>(u.out_k) + int64_t(h) * u.out_head_stride * esz : nullptr;
   r.out_v = u.out_v ? static_cast<char*>(u.out_v) + int64_t(h) * u.out_head_stride * esz : nullptr;
   r.app_k = u.app_k ? static_cast<const char*>(u.app_k) + int64_t(h) * u.n_append * d * esz : nullptr;
   r.app_v = u.app_v ? static_cast<const char*>(u.app_v) + int64_t(h) * u.n_append * d * esz : nullptr;
   bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && u.budget >= 1 &&
-            u.n_append >= 0 && a.n_sink + a.n_recent <= u.budget &&
+            u.n_append >= 0 && r.budget >= 1 && r.budget <= r.cap &&
+            (a.n_sink + a.n_recent <= r.budget || r.budget >= r.nu) &&
             u.kv_head_stride >= int64_t(u.n_tokens) * d && u.q != nullptr && u.k != nullptr;
-  // Rows of the kept units (whole blocks; a short last block only shortens it).
-  const int64_t kept_rows = min(int64_t(r.kept) * g.block, int64_t(u.n_tokens));
+  if (per_head) ok = ok && u.head_cap >= 0 && u.n_append == 0 && u.head_budget != nullptr;
+  // Rows of the kept units (whole blocks; a short last block only shortens it),
+  // at most the capacity's.
+  const int64_t kept_rows = min(int64_t(min(r.cap, r.nu)) * g.block, int64_t(u.n_tokens));
   if (u.out_k || u.out_v)
     ok = ok && u.out_head_stride >= (kept_rows + u.n_append) * d &&
          (kept_rows + u.n_append) * d * esz <= INT32_MAX;

@@ -12,6 +12,7 @@
 //   reservoir_keys Nexus weight, Philox uniform, fp64 key
 //   topb_select    radix select of the budget largest keys, ascending indices
 //   kv_compact     gather of the kept K/V rows (+ optional appended rows)
+// and, with per-head budgets, head_budget (before the keys).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +32,8 @@ constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
 constexpr int kFusedPer = 32;        // tokens per lane of the fused keys + select kernel
 constexpr int kFusedMaxTokens = 1024 * kFusedPer;   // largest n it handles
+constexpr int kAllocBins = 4096;     // per-item histogram of bits 30..19 of the weight codes
+constexpr int kAllocShift = 19;
 
 enum Stage {
   kStageScoreStats = 0,
@@ -42,6 +45,7 @@ enum Stage {
   kStageKvCompact,
   kStageSampleSelect,   // select on estimate codes in registers (n <= kFusedMaxTokens)
   kStageEstimateKeys,   // estimate codes of the keys (n <= kFusedMaxTokens)
+  kStageHeadBudget,     // per-head budgets (before the keys; NX_HEADS_GIVEN / _ALLOC)
   kNumStages
 };
 
@@ -58,11 +62,12 @@ struct Geometry {
   int32_t n_kc;          // reservoir_keys chunks per head unit
   int32_t block;         // tokens per selection unit (1, or a block size up to 32)
   int32_t inplace;       // 1: compaction rearranges k / v in place (hole filling)
+  int32_t head_alloc;    // NX_HEADS_UNIFORM / _GIVEN / _ALLOC
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
-  size_t status, part1, beta, a, p, gram, coef, keys, selp, total;
+  size_t status, part1, beta, a, p, gram, coef, keys, selp, ahist, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -80,6 +85,9 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.coef = off;   off = align256(off + hu * kMaxWalk * sizeof(float));
   L.keys = off;   off = align256(off + hu * nm * sizeof(uint64_t));
   L.selp = off;   off = align256(off + hu * g.n_kc * 2 * sizeof(uint64_t));
+  // per-item histogram of the per-head allocation (left zeroed by every call)
+  L.ahist = off;
+  if (g.head_alloc == NX_HEADS_ALLOC) off = align256(off + (hu / g.h_kv) * kAllocBins * sizeof(uint32_t));
   L.total = off;
   return L;
 }
@@ -108,11 +116,14 @@ struct Args {
   float* coef;     // [n_hu][kMaxWalk]: gamma_t / ||C||_1
   uint64_t* keys;  // [n_hu][max_tokens], order-preserving bits of the fp64 key
   uint64_t* selp;  // [n_hu][n_kc][2]: OR and AND of the chunk's keys
+  uint32_t* ahist; // [n_items][kAllocBins]: allocation histogram (zero between calls)
   // stage-only extras
   const float* w_in;    // reservoir-only mode: weights [h_kv][n] (row stride n)
   float* w_out;         // optional weight export [h_kv][n]
   double* keys_out;     // optional key export [h_kv][n]
   int32_t stop_after_weights;  // 1: reservoir_keys writes w_out and stops
+  int32_t head_floor;   // NX_HEADS_ALLOC floor
+  int32_t heads_live;   // 1: the items' head_budget arrays hold this call's budgets
 };
 
 hipError_t launch_score_stats(const Args& a, hipStream_t s);
@@ -124,5 +135,6 @@ hipError_t launch_topb_select(const Args& a, hipStream_t s);
 hipError_t launch_sample_select(const Args& a, hipStream_t s);
 hipError_t launch_estimate_keys(const Args& a, hipStream_t s);
 hipError_t launch_kv_compact(const Args& a, hipStream_t s);
+hipError_t launch_head_budget(const Args& a, hipStream_t s);
 
 }  // namespace nx

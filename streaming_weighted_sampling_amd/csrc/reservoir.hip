@@ -751,6 +751,329 @@ hipError_t launch_reservoir_keys(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- per-head budgets ([Nexus] appendix 10) ----------------------------
+//
+// NX_HEADS_ALLOC: an item's heads share the layer budget H * Bbar; each head
+// keeps f + c_h units, c_h = its share of the H * (Bbar - f) largest weights
+// over all heads of the item (the head-adaptive allocation of the cited
+// Ada-KV), capped by the capacity and the head's units.
+
+// Weight codes of one head unit's units for the allocation: the bits of w
+// for finite w > 0 (positive floats order as their bit patterns), else 0;
+// uint32 at the start of the head unit's key array (this call's keys are
+// written there only afterwards).  Each workgroup also adds its codes to the
+// item's histogram of code bits 30..19 (LDS first, then one global atomic
+// per non-empty bin).
+__global__ __launch_bounds__(kKeysThreads) void head_codes_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.y, chunk = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int j0 = chunk * kKeysPerBlock;
+  if (j0 >= u.nu) return;
+  __shared__ float s_coef[kMaxWalk];
+  __shared__ uint32_t s_hist[kAllocBins];
+  for (int b = threadIdx.x; b < kAllocBins; b += kKeysThreads) s_hist[b] = 0u;
+  if (threadIdx.x < kMaxWalk)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
+  __syncthreads();
+  const int n = u.nu;
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + size_t(u.h) * n : nullptr,
+                     a.a + size_t(hu) * g.max_tokens, a.p + size_t(hu) * g.walk * g.max_tokens,
+                     n > 1 ? 1.f / float(n - 1) : 0.f};
+  uint32_t* codes = reinterpret_cast<uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
+  constexpr int kPer = kKeysPerBlock / kKeysThreads;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    if (j < n) {
+      const float w = ws(a, s_coef, j);
+      const uint32_t c = (w > 0.f && w < INFINITY) ? __float_as_uint(w) : 0u;
+      codes[j] = c;
+      atomicAdd(&s_hist[c >> kAllocShift], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = a.ahist + size_t(hu / g.h_kv) * kAllocBins;
+  for (int b = threadIdx.x; b < kAllocBins; b += kKeysThreads)
+    if (s_hist[b] != 0u) atomicAdd(&gh[b], s_hist[b]);
+}
+
+// One workgroup per item: sets the heads' keep rows to -1 (the selection
+// then writes the kept entries) and, for NX_HEADS_ALLOC, finds how many of
+// the K largest codes over all H * units codes of the item each head holds:
+//   1. the item's histogram of code bits 30..19 (then cleared for the next
+//      call) gives the bin b* holding the K-th largest code;
+//   2. one pass over the codes counts each head's codes above b* and copies
+//      the codes in b* (low 19 bits and head) into LDS;
+//   3. the radix passes of SelCore select among those candidates;
+//   4. the threshold class's remaining places go to the heads in ascending
+//      order, and the budgets are written.
+// If the candidates overflow LDS or the counts disagree with the histogram
+// (a histogram left over from an interrupted call), the radix passes run
+// over all codes of the item instead.
+constexpr int kAllocCand = 8192;
+
+__global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int item = blockIdx.x, H = g.h_kv, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const nx_unit it = load_item(a, item);
+  const HeadUnit u0 = head_unit(a, item * H);
+  if (!u0.valid) return;
+  const int cap = u0.cap, nu = u0.nu;
+  if (it.keep != nullptr)
+    for (int64_t i = tid; i < int64_t(H) * cap; i += kSelThreads) it.keep[i] = -1;
+  if (g.head_alloc != NX_HEADS_ALLOC) return;
+  __shared__ SelCore sh;
+  __shared__ int s_gt[NX_MAX_ALLOC_HEADS], s_eq[NX_MAX_ALLOC_HEADS];
+  __shared__ uint32_t s_hist[kAllocBins];
+  __shared__ uint32_t s_cand[kAllocCand];
+  __shared__ uint32_t s_wsum[kSelWaves];
+  __shared__ int s_bstar, s_krem, s_ncand, s_above, s_fallback;
+  const int bbar = min(it.budget, nu);
+  const int f = min(a.head_floor, bbar);
+  const int total = H * nu;               // < 2^31 (checked on the host)
+  const int k = H * (bbar - f);
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens);
+  const size_t hstride = 2 * size_t(g.max_tokens);   // uint32 per head unit's key array
+  uint32_t* gh = a.ahist + size_t(item) * kAllocBins;
+  for (int h = tid; h < H; h += kSelThreads) {
+    s_gt[h] = 0;
+    s_eq[h] = 0;
+  }
+  // 1. Histogram into LDS; the global copy is cleared for the next call.
+  for (int b = tid; b < kAllocBins; b += kSelThreads) {
+    s_hist[b] = gh[b];
+    gh[b] = 0u;
+  }
+  if (tid == 0) {
+    s_ncand = 0;
+    s_fallback = 0;
+    s_bstar = -1;
+  }
+  __syncthreads();
+  bool all = true;   // every code of the threshold class is taken
+  int need = 0;
+  if (k > 0 && k < total) {
+    // Thread t owns bins 4t .. 4t+3; suffix sums over the threads (highest
+    // bins first) locate the bin of the k-th largest code.
+    static_assert(kAllocBins == 4 * kSelThreads, "bin split");
+    const uint32_t h0 = s_hist[4 * tid], h1 = s_hist[4 * tid + 1], h2 = s_hist[4 * tid + 2],
+                   h3 = s_hist[4 * tid + 3];
+    const uint32_t own = h0 + h1 + h2 + h3;
+    uint32_t suf = own;   // inclusive suffix sum inside the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t v = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += v;
+    }
+    if (lane == 0) s_wsum[wave] = suf;
+    __syncthreads();
+    uint32_t higher = suf - own;
+    for (int w = wave + 1; w < kSelWaves; ++w) higher += s_wsum[w];
+    const uint32_t kk = uint32_t(k);
+    if (higher < kk && kk <= higher + own) {
+      const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
+      const int b = kk <= c3 ? 3 : kk <= c2 ? 2 : kk <= c1 ? 1 : 0;
+      const uint32_t acc = b == 3 ? higher : b == 2 ? c3 : b == 1 ? c2 : c1;
+      s_bstar = 4 * tid + b;
+      s_krem = int(kk - acc);
+      s_above = int(acc);
+    }
+    __syncthreads();
+    const int bstar = s_bstar;
+    if (bstar < 0) {
+      if (tid == 0) s_fallback = 1;   // the histogram does not hold the item's codes
+    } else {
+      // 2. Counts above b* per head; the codes of b* into LDS.
+      // Codes are read as pairs (8-byte loads, 16 in flight per thread); a
+      // head unit's key array holds 2 * max_tokens >= units + 1 of them.
+      constexpr int kLoads = 16;
+      const int n2 = (nu + 1) / 2;
+      for (int h = 0; h < H; ++h) {
+        const uint2* ch2 = reinterpret_cast<const uint2*>(base + size_t(h) * hstride);
+        int gt = 0;
+        auto consider = [&](uint32_t c) {
+          const int bin = int(c >> kAllocShift);
+          gt += bin > bstar;
+          if (bin == bstar) {
+            const int slot = atomicAdd(&s_ncand, 1);
+            if (slot < kAllocCand)
+              s_cand[slot] = (uint32_t(h) << kAllocShift) | (c & ((1u << kAllocShift) - 1u));
+          }
+        };
+        for (int p0 = tid; p0 < n2; p0 += kSelThreads * kLoads) {
+          uint2 v[kLoads];
+#pragma unroll
+          for (int r = 0; r < kLoads; ++r) {
+            const int pr = p0 + r * kSelThreads;
+            v[r] = pr < n2 ? ch2[pr] : make_uint2(0u, 0u);
+          }
+#pragma unroll
+          for (int r = 0; r < kLoads; ++r) {
+            const int pr = p0 + r * kSelThreads;
+            if (pr < n2) {
+              consider(v[r].x);
+              if (2 * pr + 1 < nu) consider(v[r].y);
+            }
+          }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off, 64);
+        if (lane == 0 && gt != 0) atomicAdd(&s_gt[h], gt);
+      }
+    }
+    __syncthreads();
+    if (!s_fallback) {
+      int above = 0;
+      for (int h = 0; h < H; ++h) above += s_gt[h];
+      if (s_ncand > kAllocCand || uint32_t(s_ncand) != s_hist[bstar] || above != s_above)
+        s_fallback = 1;   // (every thread reads the same values; the write agrees)
+    }
+    __syncthreads();
+    const int ncand = s_ncand;
+    const bool fallback = s_fallback != 0;
+    __syncthreads();
+    if (!fallback) {
+      // 3. The s_krem-th largest low part among the candidates.
+      constexpr uint64_t kHigh = ~uint64_t((1u << kAllocShift) - 1u);
+      constexpr uint32_t kLow = (1u << kAllocShift) - 1u;
+      uint32_t o = 0u, an = ~0u;
+      for (int i = tid; i < ncand; i += kSelThreads) {
+        o |= s_cand[i] & kLow;
+        an &= s_cand[i] & kLow;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        o |= __shfl_xor(o, off, 64);
+        an &= __shfl_xor(an, off, 64);
+      }
+      if (lane == 0) {
+        sh.red_or[wave] = o;
+        sh.red_and[wave] = an;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t oo = 0, aa = ~0ull;
+        for (int w = 0; w < kSelWaves; ++w) {
+          oo |= sh.red_or[w];
+          aa &= sh.red_and[w];
+        }
+        sel_init(sh, oo | kHigh, (aa & kLow) | kHigh, ncand, s_krem);
+      }
+      __syncthreads();
+      const int slots = (ncand + kSelThreads - 1) / kSelThreads;
+      sel_passes(sh, slots, [&](int i) { return uint64_t(s_cand[tid + kSelThreads * i] & kLow) | kHigh; },
+                 [&](int i) { return tid + kSelThreads * i < ncand; });
+      const uint64_t prefix = sh.prefix, mask = sh.mask;
+      for (int i = tid; i < ncand; i += kSelThreads) {
+        const uint64_t c = (uint64_t(s_cand[i] & kLow) | kHigh) & mask;
+        const int h = int(s_cand[i] >> kAllocShift);
+        if (c > prefix) atomicAdd(&s_gt[h], 1);
+        else if (c == prefix) atomicAdd(&s_eq[h], 1);
+      }
+      __syncthreads();
+      need = sh.need;
+      all = sh.eq == sh.need;
+    } else {
+      // Radix passes over all codes of the item.
+      for (int h = tid; h < H; h += kSelThreads) {
+        s_gt[h] = 0;
+        s_eq[h] = 0;
+      }
+      auto code_at = [&](int idx) -> uint64_t {
+        const int h = idx / nu;
+        return uint64_t(base[size_t(h) * hstride + (idx - h * nu)]) | 0xFFFFFFFF00000000ull;
+      };
+      uint32_t o = 0u, an = ~0u;
+      for (int idx = tid; idx < total; idx += kSelThreads) {
+        const uint32_t c = uint32_t(code_at(idx));
+        o |= c;
+        an &= c;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        o |= __shfl_xor(o, off, 64);
+        an &= __shfl_xor(an, off, 64);
+      }
+      if (lane == 0) {
+        sh.red_or[wave] = o;
+        sh.red_and[wave] = an;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint64_t oo = 0, aa = ~0ull;
+        for (int w = 0; w < kSelWaves; ++w) {
+          oo |= sh.red_or[w];
+          aa &= sh.red_and[w];
+        }
+        sel_init(sh, oo | 0xFFFFFFFF00000000ull, aa | 0xFFFFFFFF00000000ull, total, k);
+      }
+      __syncthreads();
+      const int slots = (total + kSelThreads - 1) / kSelThreads;
+      sel_passes(sh, slots, [&](int i) { return code_at(tid + kSelThreads * i); },
+                 [&](int i) { return tid + kSelThreads * i < total; });
+      const uint64_t prefix = sh.prefix, mask = sh.mask;
+      int cur = -1, gt = 0, eq = 0;
+      for (int idx = tid; idx < total; idx += kSelThreads) {
+        const int h = idx / nu;
+        if (h != cur) {
+          if (cur >= 0) {
+            atomicAdd(&s_gt[cur], gt);
+            atomicAdd(&s_eq[cur], eq);
+          }
+          cur = h;
+          gt = eq = 0;
+        }
+        const uint64_t c = code_at(idx) & mask;
+        gt += c > prefix;
+        eq += c == prefix;
+      }
+      if (cur >= 0) {
+        atomicAdd(&s_gt[cur], gt);
+        atomicAdd(&s_eq[cur], eq);
+      }
+      __syncthreads();
+      need = sh.need;
+      all = sh.eq == sh.need;
+    }
+    if (!sh.done) {   // unreachable with consistent inputs
+      if (tid == 0) raise_status(a, kStatusBadItem);
+      return;
+    }
+  }
+  // 4. Budgets.
+  if (tid == 0) {
+    for (int h = 0; h < H; ++h) {
+      int ch;
+      if (k == 0) {
+        ch = 0;
+      } else if (k >= total) {
+        ch = nu;
+      } else {
+        const int take = all ? s_eq[h] : min(s_eq[h], need);
+        if (!all) need -= take;
+        ch = s_gt[h] + take;
+      }
+      const int bh = min(min(f + ch, cap), nu);
+      it.head_budget[h] = bh;
+      // A budget that cannot hold the forced slots makes the head invalid for
+      // the stages that follow: report it.
+      if (bh < a.n_sink + a.n_recent && bh < nu) raise_status(a, kStatusBadItem);
+    }
+  }
+}
+
+hipError_t launch_head_budget(const Args& a, hipStream_t s) {
+  if (a.g.head_alloc == NX_HEADS_ALLOC) {
+    hipLaunchKernelGGL(head_codes_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(head_alloc_kernel, dim3(a.g.n_hu / a.g.h_kv), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
   hipLaunchKernelGGL(estimate_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
   return hipGetLastError();

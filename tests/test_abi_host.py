@@ -52,7 +52,8 @@ int main(void) {
   printf("nx_desc %zu\nnx_unit %zu\n", sizeof(nx_desc), sizeof(nx_unit));
   F(nx_desc, max_out_rows); F(nx_desc, kv_head_stride); F(nx_desc, workspace);
   F(nx_desc, stream); F(nx_desc, n_avg); F(nx_unit, app_v); F(nx_unit, kv_head_stride); F(nx_unit, n_tokens);
-  F(nx_unit, seq_id);
+  F(nx_unit, seq_id); F(nx_unit, head_cap); F(nx_unit, head_budget);
+  F(nx_desc, head_alloc); F(nx_desc, head_floor); F(nx_desc, reserved);
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -71,6 +72,11 @@ int main(void) {
     assert int(out["nx_unit.kv_head_stride"]) == NxUnit.kv_head_stride.offset
     assert int(out["nx_unit.n_tokens"]) == NxUnit.n_tokens.offset
     assert int(out["nx_unit.seq_id"]) == NxUnit.seq_id.offset
+    assert int(out["nx_unit.head_cap"]) == NxUnit.head_cap.offset
+    assert int(out["nx_unit.head_budget"]) == NxUnit.head_budget.offset
+    assert int(out["nx_desc.head_alloc"]) == NxDesc.head_alloc.offset
+    assert int(out["nx_desc.head_floor"]) == NxDesc.head_floor.offset
+    assert int(out["nx_desc.reserved"]) == NxDesc.reserved.offset
 
 
 def _desc(**kw):
@@ -91,7 +97,8 @@ def test_status_strings(lib):
     assert lib.nx_stage_name(6) == b"kv_compact"
     assert lib.nx_stage_name(7) == b"sample_select"
     assert lib.nx_stage_name(8) == b"estimate_keys"
-    assert lib.nx_stage_name(9) == b"unknown"
+    assert lib.nx_stage_name(9) == b"head_budget"
+    assert lib.nx_stage_name(10) == b"unknown"
 
 
 def test_workspace_query(lib):
@@ -157,3 +164,18 @@ def test_stage_entry_points_validate(lib):
     assert lib.nx_evict_batch(ctypes.byref(d), FAKE, 32, 32768, 3, 0) == _lib.NX_EWORKSPACE
     assert lib.nx_evict_batch(ctypes.byref(d), FAKE, 9000, 4096, 3, 0) == _lib.NX_EUNSUPPORTED
     assert lib.nx_read_device_status(None) == _lib.NX_EINVAL
+    # per-head budgets: batch calls and nx_head_budgets only
+    for mode in (_lib.NX_HEADS_GIVEN, _lib.NX_HEADS_ALLOC):
+        assert _step(lib, _desc(head_alloc=mode)) == _lib.NX_EINVAL
+        assert lib.nx_reservoir_select(ctypes.byref(_desc(head_alloc=mode)), FAKE, 4096, 10, 0,
+                                       FAKE, None) == _lib.NX_EINVAL
+    assert _step(lib, _desc(head_alloc=3)) == _lib.NX_EINVAL
+    assert _step(lib, _desc(head_floor=-1)) == _lib.NX_EINVAL
+    alloc = _desc(head_alloc=_lib.NX_HEADS_ALLOC)
+    assert lib.nx_head_budgets(ctypes.byref(_desc()), FAKE, 4096, 10, 0, FAKE) == _lib.NX_EINVAL
+    assert lib.nx_head_budgets(ctypes.byref(alloc), None, 4096, 10, 0, FAKE) == _lib.NX_EINVAL
+    assert lib.nx_head_budgets(ctypes.byref(alloc), FAKE, 4096, 0, 0, FAKE) == _lib.NX_EINVAL
+    assert lib.nx_head_budgets(ctypes.byref(alloc), FAKE, 4096, 10, 0, FAKE) == _lib.NX_EWORKSPACE
+    wide = _desc(head_alloc=_lib.NX_HEADS_ALLOC, n_q_heads=512, n_kv_heads=512)
+    assert lib.nx_head_budgets(ctypes.byref(wide), FAKE, 4096, 10, 0, FAKE) == \
+        _lib.NX_EUNSUPPORTED
