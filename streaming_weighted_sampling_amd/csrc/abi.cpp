@@ -181,17 +181,30 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
       case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
       case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
       case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
-      case kStageReservoirKeys:
-        // Per-head budgets are settled before any stage that reads them.
-        if (a.g.head_alloc != NX_HEADS_UNIFORM && !a.stop_after_weights) {
-          err = run_stage(kStageHeadBudget, s, [&] { return launch_head_budget(a, s); });
+      case kStageReservoirKeys: {
+        // Per-head budgets are settled before any stage that reads them.  On
+        // the fused path with allocated budgets the estimate pass runs first
+        // (it does not read the budgets) and also writes the weight codes.
+        const bool heads = a.g.head_alloc != NX_HEADS_UNIFORM && !a.stop_after_weights;
+        const bool est_first = heads && fused && a.g.head_alloc == NX_HEADS_ALLOC;
+        Args pre = a;
+        pre.est_wcodes = est_first ? 1 : 0;
+        pre.wcode_off = est_first ? a.g.max_tokens : 0;
+        if (est_first) {
+          err = run_stage(kStageEstimateKeys, s, [&] { return launch_estimate_keys(pre, s); });
           if (err != hipSuccess) break;
         }
+        if (heads) {
+          err = run_stage(kStageHeadBudget, s, [&] { return launch_head_budget(pre, s); });
+          if (err != hipSuccess) break;
+        }
+        if (est_first) break;
         if (fused)
           err = run_stage(kStageEstimateKeys, s, [&] { return launch_estimate_keys(live, s); });
         else
           err = run_stage(st, s, [&] { return launch_reservoir_keys(live, s); });
         break;
+      }
       case kStageTopbSelect:
         if (fused)
           err = run_stage(kStageSampleSelect, s, [&] { return launch_sample_select(live, s); });

@@ -124,6 +124,8 @@ struct Args {
   int32_t stop_after_weights;  // 1: reservoir_keys writes w_out and stops
   int32_t head_floor;   // NX_HEADS_ALLOC floor
   int32_t heads_live;   // 1: the items' head_budget arrays hold this call's budgets
+  int32_t est_wcodes;   // 1: estimate_keys also writes the allocation's weight codes
+  int32_t wcode_off;    // uint32 offset of the weight codes in a head unit's key array
 };
 
 hipError_t launch_score_stats(const Args& a, hipStream_t s);

@@ -488,8 +488,11 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
 
 // Whether a head unit's selection runs on estimate codes (no key export, a
 // keep array, and something to drop).
+// (With allocated per-head budgets the estimate pass runs before the budgets
+// exist, so every head unit gets its codes.)
 __device__ inline bool uses_estimate(const Args& a, const HeadUnit& u) {
-  return a.keys_out == nullptr && u.keep != nullptr && u.budget < u.nu;
+  return a.keys_out == nullptr && u.keep != nullptr &&
+         (u.budget < u.nu || a.g.head_alloc == NX_HEADS_ALLOC);
 }
 
 // Estimate codes of kKeysPerBlock tokens of one head unit (many workgroups
@@ -532,6 +535,27 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
         codes[j] = estimate_code(x.x, x.y, w[i], j < a.n_sink || j >= n - a.n_recent);
       }
     }
+  }
+  if (a.est_wcodes) {
+    // Allocated per-head budgets: the weight codes (after the estimate codes)
+    // and the item's histogram, as in head_codes_kernel.
+    __shared__ uint32_t s_hist[kAllocBins];
+    for (int b = threadIdx.x; b < kAllocBins; b += kKeysThreads) s_hist[b] = 0u;
+    __syncthreads();
+    uint32_t* wc = codes + a.wcode_off;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = j0 + threadIdx.x + kKeysThreads * i;
+      if (j < n) {
+        const uint32_t c = (w[i] > 0.f && w[i] < INFINITY) ? __float_as_uint(w[i]) : 0u;
+        wc[j] = c;
+        atomicAdd(&s_hist[c >> kAllocShift], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t* gh = a.ahist + size_t(hu / g.h_kv) * kAllocBins;
+    for (int b = threadIdx.x; b < kAllocBins; b += kKeysThreads)
+      if (s_hist[b] != 0u) atomicAdd(&gh[b], s_hist[b]);
   }
   if (__syncthreads_or(nonfinite) && threadIdx.x == 0) raise_status(a, kStatusNonFinite);
 }
@@ -834,7 +858,8 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
   const int f = min(a.head_floor, bbar);
   const int total = H * nu;               // < 2^31 (checked on the host)
   const int k = H * (bbar - f);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens);
+  const uint32_t* base =
+      reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens) + a.wcode_off;
   const size_t hstride = 2 * size_t(g.max_tokens);   // uint32 per head unit's key array
   uint32_t* gh = a.ahist + size_t(item) * kAllocBins;
   for (int h = tid; h < H; h += kSelThreads) {
@@ -886,12 +911,15 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
       if (tid == 0) s_fallback = 1;   // the histogram does not hold the item's codes
     } else {
       // 2. Counts above b* per head; the codes of b* into LDS.
-      // Codes are read as pairs (8-byte loads, 16 in flight per thread); a
-      // head unit's key array holds 2 * max_tokens >= units + 1 of them.
+      // Codes are read as pairs (8-byte loads, 16 in flight per thread) when
+      // they start on an 8-byte boundary (wcode_off even; the key array
+      // then holds the pair that ends past the last code), else one by one.
       constexpr int kLoads = 16;
-      const int n2 = (nu + 1) / 2;
+      const bool pairs = (a.wcode_off & 1) == 0;
+      const int n2 = pairs ? (nu + 1) / 2 : nu;
       for (int h = 0; h < H; ++h) {
-        const uint2* ch2 = reinterpret_cast<const uint2*>(base + size_t(h) * hstride);
+        const uint32_t* ch = base + size_t(h) * hstride;
+        const uint2* ch2 = reinterpret_cast<const uint2*>(ch);
         int gt = 0;
         auto consider = [&](uint32_t c) {
           const int bin = int(c >> kAllocShift);
@@ -907,14 +935,14 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
 #pragma unroll
           for (int r = 0; r < kLoads; ++r) {
             const int pr = p0 + r * kSelThreads;
-            v[r] = pr < n2 ? ch2[pr] : make_uint2(0u, 0u);
+            v[r] = pr >= n2 ? make_uint2(0u, 0u) : pairs ? ch2[pr] : make_uint2(ch[pr], 0u);
           }
 #pragma unroll
           for (int r = 0; r < kLoads; ++r) {
             const int pr = p0 + r * kSelThreads;
             if (pr < n2) {
               consider(v[r].x);
-              if (2 * pr + 1 < nu) consider(v[r].y);
+              if (pairs && 2 * pr + 1 < nu) consider(v[r].y);
             }
           }
         }
@@ -1065,7 +1093,7 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
 }
 
 hipError_t launch_head_budget(const Args& a, hipStream_t s) {
-  if (a.g.head_alloc == NX_HEADS_ALLOC) {
+  if (a.g.head_alloc == NX_HEADS_ALLOC && !a.est_wcodes) {
     hipLaunchKernelGGL(head_codes_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
