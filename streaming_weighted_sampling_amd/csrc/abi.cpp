@@ -106,6 +106,8 @@ nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
   a->keys = reinterpret_cast<uint64_t*>(base + L.keys);
   a->selp = reinterpret_cast<uint64_t*>(base + L.selp);
   a->ahist = reinterpret_cast<uint32_t*>(base + L.ahist);
+  a->acand = reinterpret_cast<uint32_t*>(base + L.acand);
+  a->acnt = reinterpret_cast<int32_t*>(base + L.acnt);
   return NX_OK;
 }
 

@@ -34,6 +34,7 @@ constexpr int kFusedPer = 32;        // tokens per lane of the fused keys + sele
 constexpr int kFusedMaxTokens = 1024 * kFusedPer;   // largest n it handles
 constexpr int kAllocBins = 4096;     // per-item histogram of bits 30..19 of the weight codes
 constexpr int kAllocShift = 19;
+constexpr int kAllocCand = 8192;     // boundary-bin codes held per item (and per head unit)
 
 enum Stage {
   kStageScoreStats = 0,
@@ -67,7 +68,7 @@ struct Geometry {
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
-  size_t status, part1, beta, a, p, gram, coef, keys, selp, ahist, total;
+  size_t status, part1, beta, a, p, gram, coef, keys, selp, ahist, acand, acnt, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -88,6 +89,11 @@ inline WsLayout ws_layout(const Geometry& g) {
   // per-item histogram of the per-head allocation (left zeroed by every call)
   L.ahist = off;
   if (g.head_alloc == NX_HEADS_ALLOC) off = align256(off + (hu / g.h_kv) * kAllocBins * sizeof(uint32_t));
+  // per head unit: its boundary-bin codes and (count above, candidate count)
+  L.acand = off;
+  if (g.head_alloc == NX_HEADS_ALLOC) off = align256(off + hu * kAllocCand * sizeof(uint32_t));
+  L.acnt = off;
+  if (g.head_alloc == NX_HEADS_ALLOC) off = align256(off + hu * 2 * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -117,6 +123,8 @@ struct Args {
   uint64_t* keys;  // [n_hu][max_tokens], order-preserving bits of the fp64 key
   uint64_t* selp;  // [n_hu][n_kc][2]: OR and AND of the chunk's keys
   uint32_t* ahist; // [n_items][kAllocBins]: allocation histogram (zero between calls)
+  uint32_t* acand; // [n_hu][kAllocCand]: boundary-bin codes of each head unit
+  int32_t* acnt;   // [n_hu][2]: codes above the boundary bin, codes in it
   // stage-only extras
   const float* w_in;    // reservoir-only mode: weights [h_kv][n] (row stride n)
   float* w_out;         // optional weight export [h_kv][n]

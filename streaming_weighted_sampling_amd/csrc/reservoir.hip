@@ -823,21 +823,138 @@ __global__ __launch_bounds__(kKeysThreads) void head_codes_kernel(const Args a) 
     if (s_hist[b] != 0u) atomicAdd(&gh[b], s_hist[b]);
 }
 
-// One workgroup per item: sets the heads' keep rows to -1 (the selection
-// then writes the kept entries) and, for NX_HEADS_ALLOC, finds how many of
-// the K largest codes over all H * units codes of the item each head holds:
-//   1. the item's histogram of code bits 30..19 (then cleared for the next
-//      call) gives the bin b* holding the K-th largest code;
-//   2. one pass over the codes counts each head's codes above b* and copies
-//      the codes in b* (low 19 bits and head) into LDS;
-//   3. the radix passes of SelCore select among those candidates;
-//   4. the threshold class's remaining places go to the heads in ascending
-//      order, and the budgets are written.
-// If the candidates overflow LDS or the counts disagree with the histogram
-// (a histogram left over from an interrupted call), the radix passes run
-// over all codes of the item instead.
-constexpr int kAllocCand = 8192;
+// Allocation sizes of one item: Bbar = min(budget, units), f = min(floor,
+// Bbar), k = H (Bbar - f) codes to take out of total = H * units.
+struct AllocSizes {
+  int f, k, total;
+};
+__device__ inline AllocSizes alloc_sizes(const Args& a, const nx_unit& it, int nu) {
+  const int bbar = min(it.budget, nu);
+  const int f = min(a.head_floor, bbar);
+  return {f, a.g.h_kv * (bbar - f), a.g.h_kv * nu};   // total < 2^31 (checked on the host)
+}
 
+// The bin of the item's histogram (in LDS) that holds the k-th largest code.
+// Thread t owns bins 4t .. 4t+3; suffix sums over the threads, highest bins
+// first.  Sets *s_bstar (-1 if the histogram holds fewer than k codes),
+// *s_krem (codes still needed from that bin) and *s_above (codes above it).
+__device__ inline void alloc_boundary(const uint32_t* s_hist, int k, uint32_t* s_wsum,
+                                      int* s_bstar, int* s_krem, int* s_above) {
+  static_assert(kAllocBins == 4 * kSelThreads, "bin split");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) *s_bstar = -1;
+  const uint32_t h0 = s_hist[4 * tid], h1 = s_hist[4 * tid + 1], h2 = s_hist[4 * tid + 2],
+                 h3 = s_hist[4 * tid + 3];
+  const uint32_t own = h0 + h1 + h2 + h3;
+  uint32_t suf = own;   // inclusive suffix sum inside the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += v;
+  }
+  if (lane == 0) s_wsum[wave] = suf;
+  __syncthreads();
+  uint32_t higher = suf - own;
+  for (int w = wave + 1; w < kSelWaves; ++w) higher += s_wsum[w];
+  const uint32_t kk = uint32_t(k);
+  if (higher < kk && kk <= higher + own) {
+    const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
+    const int b = kk <= c3 ? 3 : kk <= c2 ? 2 : kk <= c1 ? 1 : 0;
+    const uint32_t acc = b == 3 ? higher : b == 2 ? c3 : b == 1 ? c2 : c1;
+    *s_bstar = 4 * tid + b;
+    *s_krem = int(kk - acc);
+    *s_above = int(acc);
+  }
+  __syncthreads();
+}
+
+// One workgroup per head unit (NX_HEADS_ALLOC): from the item's histogram,
+// the boundary bin b*; then one pass over this head's codes counts those
+// above b* and copies those in b* (low 19 bits and the head) to the head
+// unit's candidate area.  Writes (count above, candidate count); a count over
+// kAllocCand means the candidates did not fit.
+__global__ __launch_bounds__(kSelThreads) void head_count_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.x, H = g.h_kv, tid = threadIdx.x, lane = tid & 63;
+  const int item = hu / H, h = hu - item * H;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const nx_unit it = load_item(a, item);
+  const int nu = u.nu;
+  const AllocSizes z = alloc_sizes(a, it, nu);
+  if (!(z.k > 0 && z.k < z.total)) return;
+  __shared__ uint32_t s_hist[kAllocBins];
+  __shared__ uint32_t s_wsum[kSelWaves];
+  __shared__ int s_bstar, s_krem, s_above, s_n, s_gt;
+  const uint32_t* gh = a.ahist + size_t(item) * kAllocBins;
+  for (int b = tid; b < kAllocBins; b += kSelThreads) s_hist[b] = gh[b];
+  if (tid == 0) {
+    s_n = 0;
+    s_gt = 0;
+  }
+  __syncthreads();
+  alloc_boundary(s_hist, z.k, s_wsum, &s_bstar, &s_krem, &s_above);
+  const int bstar = s_bstar;
+  int* cnt = a.acnt + 2 * size_t(hu);
+  if (bstar < 0) {   // the histogram does not hold the item's codes
+    if (tid == 0) {
+      cnt[0] = -1;
+      cnt[1] = -1;
+    }
+    return;
+  }
+  const uint32_t* ch = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens) + a.wcode_off;
+  uint32_t* cand = a.acand + size_t(hu) * kAllocCand;
+  // Codes are read as pairs (8-byte loads, 16 in flight per thread) when
+  // they start on an 8-byte boundary (wcode_off even; the key array then
+  // holds the pair that ends past the last code), else one by one.
+  constexpr int kLoads = 16;
+  const bool pairs = (a.wcode_off & 1) == 0;
+  const int n2 = pairs ? (nu + 1) / 2 : nu;
+  const uint2* ch2 = reinterpret_cast<const uint2*>(ch);
+  int gt = 0;
+  auto consider = [&](uint32_t c) {
+    const int bin = int(c >> kAllocShift);
+    gt += bin > bstar;
+    if (bin == bstar) {
+      const int slot = atomicAdd(&s_n, 1);
+      if (slot < kAllocCand) cand[slot] = (uint32_t(h) << kAllocShift) | (c & ((1u << kAllocShift) - 1u));
+    }
+  };
+  for (int p0 = tid; p0 < n2; p0 += kSelThreads * kLoads) {
+    uint2 v[kLoads];
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int pr = p0 + r * kSelThreads;
+      v[r] = pr >= n2 ? make_uint2(0u, 0u) : pairs ? ch2[pr] : make_uint2(ch[pr], 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+      const int pr = p0 + r * kSelThreads;
+      if (pr < n2) {
+        consider(v[r].x);
+        if (pairs && 2 * pr + 1 < nu) consider(v[r].y);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off, 64);
+  if (lane == 0 && gt != 0) atomicAdd(&s_gt, gt);
+  __syncthreads();
+  if (tid == 0) {
+    cnt[0] = s_gt;
+    cnt[1] = s_n;
+  }
+}
+
+// One workgroup per item: sets the heads' keep rows to -1 (the selection
+// then writes the kept entries) and, for NX_HEADS_ALLOC, turns the heads'
+// counts into budgets: the boundary bin again from the histogram (cleared
+// here for the next call), the heads' candidates gathered into LDS, the
+// radix passes of SelCore among them, the threshold class's remaining places
+// to the heads in ascending order.  If the candidates overflow or the counts
+// disagree with the histogram (one left over from an interrupted call), the
+// radix passes run over all codes of the item instead.
 __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
   const Geometry& g = a.g;
   const int item = blockIdx.x, H = g.h_kv, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -849,15 +966,13 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
     for (int64_t i = tid; i < int64_t(H) * cap; i += kSelThreads) it.keep[i] = -1;
   if (g.head_alloc != NX_HEADS_ALLOC) return;
   __shared__ SelCore sh;
-  __shared__ int s_gt[NX_MAX_ALLOC_HEADS], s_eq[NX_MAX_ALLOC_HEADS];
+  __shared__ int s_gt[NX_MAX_ALLOC_HEADS], s_eq[NX_MAX_ALLOC_HEADS], s_off[NX_MAX_ALLOC_HEADS];
   __shared__ uint32_t s_hist[kAllocBins];
   __shared__ uint32_t s_cand[kAllocCand];
   __shared__ uint32_t s_wsum[kSelWaves];
-  __shared__ int s_bstar, s_krem, s_ncand, s_above, s_fallback;
-  const int bbar = min(it.budget, nu);
-  const int f = min(a.head_floor, bbar);
-  const int total = H * nu;               // < 2^31 (checked on the host)
-  const int k = H * (bbar - f);
+  __shared__ int s_bstar, s_krem, s_above, s_ncand, s_fallback;
+  const AllocSizes z = alloc_sizes(a, it, nu);
+  const int f = z.f, k = z.k, total = z.total;
   const uint32_t* base =
       reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens) + a.wcode_off;
   const size_t hstride = 2 * size_t(g.max_tokens);   // uint32 per head unit's key array
@@ -866,104 +981,45 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
     s_gt[h] = 0;
     s_eq[h] = 0;
   }
-  // 1. Histogram into LDS; the global copy is cleared for the next call.
+  // The histogram into LDS; the global copy is cleared for the next call.
   for (int b = tid; b < kAllocBins; b += kSelThreads) {
     s_hist[b] = gh[b];
     gh[b] = 0u;
-  }
-  if (tid == 0) {
-    s_ncand = 0;
-    s_fallback = 0;
-    s_bstar = -1;
   }
   __syncthreads();
   bool all = true;   // every code of the threshold class is taken
   int need = 0;
   if (k > 0 && k < total) {
-    // Thread t owns bins 4t .. 4t+3; suffix sums over the threads (highest
-    // bins first) locate the bin of the k-th largest code.
-    static_assert(kAllocBins == 4 * kSelThreads, "bin split");
-    const uint32_t h0 = s_hist[4 * tid], h1 = s_hist[4 * tid + 1], h2 = s_hist[4 * tid + 2],
-                   h3 = s_hist[4 * tid + 3];
-    const uint32_t own = h0 + h1 + h2 + h3;
-    uint32_t suf = own;   // inclusive suffix sum inside the wave
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += v;
-    }
-    if (lane == 0) s_wsum[wave] = suf;
-    __syncthreads();
-    uint32_t higher = suf - own;
-    for (int w = wave + 1; w < kSelWaves; ++w) higher += s_wsum[w];
-    const uint32_t kk = uint32_t(k);
-    if (higher < kk && kk <= higher + own) {
-      const uint32_t c3 = higher + h3, c2 = c3 + h2, c1 = c2 + h1;
-      const int b = kk <= c3 ? 3 : kk <= c2 ? 2 : kk <= c1 ? 1 : 0;
-      const uint32_t acc = b == 3 ? higher : b == 2 ? c3 : b == 1 ? c2 : c1;
-      s_bstar = 4 * tid + b;
-      s_krem = int(kk - acc);
-      s_above = int(acc);
-    }
-    __syncthreads();
-    const int bstar = s_bstar;
-    if (bstar < 0) {
-      if (tid == 0) s_fallback = 1;   // the histogram does not hold the item's codes
-    } else {
-      // 2. Counts above b* per head; the codes of b* into LDS.
-      // Codes are read as pairs (8-byte loads, 16 in flight per thread) when
-      // they start on an 8-byte boundary (wcode_off even; the key array
-      // then holds the pair that ends past the last code), else one by one.
-      constexpr int kLoads = 16;
-      const bool pairs = (a.wcode_off & 1) == 0;
-      const int n2 = pairs ? (nu + 1) / 2 : nu;
-      for (int h = 0; h < H; ++h) {
-        const uint32_t* ch = base + size_t(h) * hstride;
-        const uint2* ch2 = reinterpret_cast<const uint2*>(ch);
-        int gt = 0;
-        auto consider = [&](uint32_t c) {
-          const int bin = int(c >> kAllocShift);
-          gt += bin > bstar;
-          if (bin == bstar) {
-            const int slot = atomicAdd(&s_ncand, 1);
-            if (slot < kAllocCand)
-              s_cand[slot] = (uint32_t(h) << kAllocShift) | (c & ((1u << kAllocShift) - 1u));
-          }
-        };
-        for (int p0 = tid; p0 < n2; p0 += kSelThreads * kLoads) {
-          uint2 v[kLoads];
-#pragma unroll
-          for (int r = 0; r < kLoads; ++r) {
-            const int pr = p0 + r * kSelThreads;
-            v[r] = pr >= n2 ? make_uint2(0u, 0u) : pairs ? ch2[pr] : make_uint2(ch[pr], 0u);
-          }
-#pragma unroll
-          for (int r = 0; r < kLoads; ++r) {
-            const int pr = p0 + r * kSelThreads;
-            if (pr < n2) {
-              consider(v[r].x);
-              if (pairs && 2 * pr + 1 < nu) consider(v[r].y);
-            }
-          }
+    alloc_boundary(s_hist, k, s_wsum, &s_bstar, &s_krem, &s_above);
+    if (tid == 0) {
+      // The heads' counts, checked against the histogram.
+      int fb = s_bstar < 0, above = 0, nc = 0;
+      for (int h = 0; h < H && !fb; ++h) {
+        const int* cnt = a.acnt + 2 * (size_t(item) * H + h);
+        if (cnt[0] < 0 || cnt[1] < 0 || cnt[1] > kAllocCand) {
+          fb = 1;
+          break;
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) gt += __shfl_xor(gt, off, 64);
-        if (lane == 0 && gt != 0) atomicAdd(&s_gt[h], gt);
+        s_gt[h] = cnt[0];
+        s_off[h] = nc;
+        above += cnt[0];
+        nc += cnt[1];
       }
+      if (!fb && (nc > kAllocCand || uint32_t(nc) != s_hist[s_bstar] || above != s_above)) fb = 1;
+      s_fallback = fb;
+      s_ncand = fb ? 0 : nc;
     }
     __syncthreads();
-    if (!s_fallback) {
-      int above = 0;
-      for (int h = 0; h < H; ++h) above += s_gt[h];
-      if (s_ncand > kAllocCand || uint32_t(s_ncand) != s_hist[bstar] || above != s_above)
-        s_fallback = 1;   // (every thread reads the same values; the write agrees)
-    }
-    __syncthreads();
-    const int ncand = s_ncand;
     const bool fallback = s_fallback != 0;
-    __syncthreads();
     if (!fallback) {
-      // 3. The s_krem-th largest low part among the candidates.
+      // Gather the candidates, then the s_krem-th largest low part among them.
+      const int ncand = s_ncand;
+      for (int h = 0; h < H; ++h) {
+        const int nh = a.acnt[2 * (size_t(item) * H + h) + 1];
+        const uint32_t* src = a.acand + (size_t(item) * H + h) * kAllocCand;
+        for (int i = tid; i < nh; i += kSelThreads) s_cand[s_off[h] + i] = src[i];
+      }
+      __syncthreads();
       constexpr uint64_t kHigh = ~uint64_t((1u << kAllocShift) - 1u);
       constexpr uint32_t kLow = (1u << kAllocShift) - 1u;
       uint32_t o = 0u, an = ~0u;
@@ -1070,7 +1126,7 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
       return;
     }
   }
-  // 4. Budgets.
+  // Budgets.
   if (tid == 0) {
     for (int h = 0; h < H; ++h) {
       int ch;
@@ -1095,6 +1151,11 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
 hipError_t launch_head_budget(const Args& a, hipStream_t s) {
   if (a.g.head_alloc == NX_HEADS_ALLOC && !a.est_wcodes) {
     hipLaunchKernelGGL(head_codes_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.g.head_alloc == NX_HEADS_ALLOC) {
+    hipLaunchKernelGGL(head_count_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
