@@ -158,11 +158,16 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     if (a.w_in != nullptr) {
       w[i] = a.w_in[ext + jc];
     } else {
+      // The same arithmetic as token_weight, loads first.
+      float pv[kMaxWalk];
+#pragma unroll
+      for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < g.walk ? p_in[size_t(t) * g.max_tokens + jc] : 0.f;
+      const float aj = a_in[jc];
       float cj = 0.f;
 #pragma unroll
       for (int t = 0; t < kMaxWalk; ++t)
-        if (t < g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * g.max_tokens + jc], cj);
-      w[i] = a_in[jc] + a.lambda * cj + a.eps_tie * (float(jc) * ramp);
+        if (t < g.walk) cj = fmaf(s_coef[t], pv[t], cj);
+      w[i] = aj + a.lambda * cj + a.eps_tie * (float(jc) * ramp);
     }
   }
 #pragma unroll
@@ -406,13 +411,19 @@ struct SelShared {
   int round_cnt[kFusedPer * kSelWaves];
 };
 
+// (All loads are issued before the first use, so one memory round trip
+// serves the direct score and every walk row.)
 __device__ __attribute__((always_inline)) inline float token_weight(
     const Args& a, const float* s_coef, const float* a_in, const float* p_in, float ramp, int j) {
+  float pv[kMaxWalk];
+#pragma unroll
+  for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < a.g.walk ? p_in[size_t(t) * a.g.max_tokens + j] : 0.f;
+  const float aj = a_in[j];
   float cj = 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxWalk; ++t)
-    if (t < a.g.walk) cj = fmaf(s_coef[t], p_in[size_t(t) * a.g.max_tokens + j], cj);
-  return a_in[j] + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+    if (t < a.g.walk) cj = fmaf(s_coef[t], pv[t], cj);
+  return aj + a.lambda * cj + a.eps_tie * (float(j) * ramp);
 }
 
 // Weight of token j of this head unit (given weights, or a + lambda c~ + ramp).
