@@ -235,6 +235,9 @@ def main():
                     help="selection unit of Eq. 1: 1 = tokens, else blocks of that many tokens")
     ap.add_argument("--n-avg", type=int, default=1,
                     help="priority averaging count of Eq. 6 (1: A-Res key; -1: top-B by weight)")
+    ap.add_argument("--score", choices=["two-sweeps", "one-read"], default="two-sweeps",
+                    help="score pass: two sweeps over K (default), or K read once with "
+                         "in-kernel per-unit barriers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1-GiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -270,7 +273,8 @@ def main():
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
                          n_avg=args.n_avg, block=args.block,
                          head_alloc=nx.NX_HEADS_ALLOC if heads else nx.NX_HEADS_UNIFORM,
-                         head_floor=data["budget"] // 5 if heads else 0)
+                         head_floor=data["budget"] // 5 if heads else 0,
+                         score_mode=nx.SCORE_ONE_READ if args.score == "one-read" else nx.SCORE_TWO_SWEEPS)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -305,10 +309,14 @@ def main():
     qk_flops = tokens * 2 * wl.group * wl.window * d
     # (algorithmic amount per launch, unit, peak, bound) of the stages that move the bulk.
     work = {
+        "score_fused": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
         "score_stats": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
         "score_probs": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
         "kv_compact": (compact_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
     }
+    score_stages = [s for s in ("score_fused", "score_stats", "score_combine", "score_probs")
+                    if s in per_launch]
+    one_read = "score_fused" in per_launch
     dominant = max((s for s in per_launch if s in work), key=lambda s: per_launch[s][0])
 
     # Timed region: HIP events around the dominant kernel only, on the stream
@@ -336,7 +344,8 @@ def main():
                 "kernel": dominant, "algorithmic_bytes": int(amount * 1e9),
                 "kernel_ms_per_launch": round(dom_ms_per_launch, 4), "launches_timed": dom_cnt,
                 "traffic_source": None if traffic is None else traffic["source"]}
-    score_ms = per_launch["score_stats"][0] + per_launch["score_probs"][0]
+    score_ms = sum(per_launch[s][0] for s in score_stages)
+    qk_stage = "score_fused" if one_read else "score_probs"
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
@@ -348,16 +357,17 @@ def main():
                    "layers": wl.n_layers, "kv_heads": wl.h_kv, "n_tokens": wl.n_tokens,
                    "budget": wl.budget, "window": wl.window, "walk_iters": wl.walk_iters,
                    "n_avg": args.n_avg, "block": args.block, "heads": args.heads,
-                   "budget_units": data["budget"]},
+                   "budget_units": data["budget"],
+                   "score": "one_read" if one_read else "two_sweeps"},
         "step_latency_ms": round(ms_per_step, 4),
         "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},
         "stage_ms_note": "per-stage times from a pass with events around every stage, "
                          "outside the timed region",
-        "score_probs_mfma_tflops": round(qk_flops / (per_launch["score_probs"][0] * 1e-3) / 1e12, 1),
+        f"{qk_stage}_mfma_tflops": round(qk_flops / (per_launch[qk_stage][0] * 1e-3) / 1e12, 1),
         "stage_gbs": {
-            "score_stats_k_read": round(k_bytes / (per_launch["score_stats"][0] * 1e-3) / 1e9, 1),
-            "score_probs_k_read": round(k_bytes / (per_launch["score_probs"][0] * 1e-3) / 1e9, 1),
-            "score_k_once_over_both_sweeps": round(k_bytes / (score_ms * 1e-3) / 1e9, 1),
+            **{f"{s}_k_read": round(k_bytes / (per_launch[s][0] * 1e-3) / 1e9, 1)
+               for s in ("score_fused", "score_stats", "score_probs") if s in per_launch},
+            "score_k_once_over_all_score_stages": round(k_bytes / (score_ms * 1e-3) / 1e9, 1),
             "kv_compact": round(compact_bytes / (per_launch["kv_compact"][0] * 1e-3) / 1e9, 1),
             "step_algorithmic": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         },

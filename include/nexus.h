@@ -130,8 +130,22 @@ typedef struct nx_desc {
                                nx_kv_compact need 0. */
   int32_t head_floor;       /* NX_HEADS_ALLOC: per-head floor f >= 0 (units); an allocation
                                below n_sink + n_recent marks the item bad */
-  int32_t reserved;         /* must be 0 */
+  int32_t score_mode;       /* how K is read for Eq. 1's softmax normaliser:
+                               NX_SCORE_TWO_SWEEPS (0): a statistics sweep, then a
+                               probabilities sweep (the faster path on MI355X);
+                               NX_SCORE_ONE_READ (1): K read once; the logits of each
+                               256-token tile stay in registers while the tiles of a head
+                               unit meet at two device-scope barriers inside one cooperative
+                               launch.  Needs bf16, head_dim 128, G * W <= 128, block <= 1,
+                               and walk_iters 0, or G = 4 and walk_iters <= 8, or G = 8 and
+                               walk_iters <= 4; else NX_EUNSUPPORTED.  Same weights up to
+                               fp32 rounding order.  A barrier that gives up is reported as
+                               NX_EHIP by nx_read_device_status().
+                               Other values: NX_EINVAL */
 } nx_desc;
+
+#define NX_SCORE_TWO_SWEEPS 0
+#define NX_SCORE_ONE_READ 1
 
 #define NX_COMPACT_COPY 0
 #define NX_COMPACT_INPLACE 1
@@ -260,7 +274,8 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
 
 /*
  * Waits for desc->stream, reads and clears the workspace status word.
- * Returns NX_OK, NX_ENONFINITE, NX_EINVAL (a bad batch item) or NX_EHIP.
+ * Returns NX_OK, NX_ENONFINITE, NX_EINVAL (a bad batch item) or NX_EHIP (a HIP
+ * call failed, or a single-read scoring barrier timed out).
  */
 nx_status nx_read_device_status(const nx_desc* desc);
 

@@ -13,6 +13,8 @@ NX_EWORKSPACE = -3
 NX_EUNSUPPORTED = -4
 NX_ENONFINITE = -5
 NX_EHIP = -6
+NX_SCORE_TWO_SWEEPS = 0
+NX_SCORE_ONE_READ = 1
 NX_COMPACT_COPY = 0
 NX_COMPACT_INPLACE = 1
 NX_HEADS_UNIFORM = 0
@@ -48,7 +50,7 @@ class NxDesc(ctypes.Structure):
         ("compact", ctypes.c_int32),
         ("head_alloc", ctypes.c_int32),
         ("head_floor", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("score_mode", ctypes.c_int32),
     ]
 
 

@@ -17,6 +17,8 @@ _DTYPES = {torch.bfloat16: NX_BF16, torch.float32: NX_F32}
 
 
 TOPK = -1                     # n_avg value of the deterministic top-B-by-weight limit
+SCORE_TWO_SWEEPS = 0          # score_mode: statistics sweep, then probabilities sweep
+SCORE_ONE_READ = 1            # score_mode: K read once (NX_EUNSUPPORTED where it cannot)
 
 
 @dataclass
@@ -36,6 +38,7 @@ class NexusConfig:
     compact: int = 0          # 0: copy kept rows to new buffers; 1: compact k / v in place
     head_alloc: int = 0       # appendix 10 per-head budgets: 0 uniform, 1 given, 2 allocated
     head_floor: int = 0       # per-head floor of the allocation (head_alloc = 2)
+    score_mode: int = 0       # 0: two sweeps over K, 1: K read once (in-kernel barriers)
 
     def units(self, n_tokens):
         """Selection units of a head: tokens, or ceil(n_tokens / block) blocks."""
@@ -62,6 +65,7 @@ class NexusConfig:
         d.compact = self.compact
         d.head_alloc = self.head_alloc
         d.head_floor = self.head_floor
+        d.score_mode = self.score_mode
         d.layer = layer
         d.step = step
         d.seq_id = seq_id

@@ -30,7 +30,7 @@ nx_status check_desc(const nx_desc* d) {
   if (d->n_avg != NX_TOPK && (d->n_avg < 0 || d->n_avg > NX_MAX_AVG)) return NX_EINVAL;
   if (d->block < 0) return NX_EINVAL;
   if (d->compact != NX_COMPACT_COPY && d->compact != NX_COMPACT_INPLACE) return NX_EINVAL;
-  if (d->reserved != 0) return NX_EINVAL;
+  if (d->score_mode != NX_SCORE_TWO_SWEEPS && d->score_mode != NX_SCORE_ONE_READ) return NX_EINVAL;
   if (d->head_alloc < NX_HEADS_UNIFORM || d->head_alloc > NX_HEADS_ALLOC || d->head_floor < 0)
     return NX_EINVAL;
   if (d->compact == NX_COMPACT_INPLACE && d->block > 1) return NX_EUNSUPPORTED;
@@ -89,6 +89,13 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->tok_per_block = tpb;
   g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
+  // One read of K (score_fused) on request, where the shape and the device allow it.
+  if (d->score_mode == NX_SCORE_ONE_READ) {
+    if (!score_fused_fits(*g)) return NX_EUNSUPPORTED;
+    g->fused = 1;
+    g->tok_per_block = kMinTokPerBlock;
+    g->n_tmax = (max_tokens + kMinTokPerBlock - 1) / kMinTokPerBlock;
+  }
   return NX_OK;
 }
 
@@ -97,6 +104,7 @@ nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
   if (d->workspace == nullptr || d->workspace_bytes < L.total) return NX_EWORKSPACE;
   char* base = static_cast<char*>(d->workspace);
   a->status = reinterpret_cast<uint32_t*>(base + L.status);
+  a->sync = reinterpret_cast<uint32_t*>(base + L.sync);
   a->part1 = reinterpret_cast<float*>(base + L.part1);
   a->beta = reinterpret_cast<float*>(base + L.beta);
   a->a = reinterpret_cast<float*>(base + L.a);
@@ -179,9 +187,16 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   live.heads_live = 1;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {
-      case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
-      case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
-      case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
+      case kStageScoreStats:
+        if (a.g.fused) err = run_stage(kStageScoreFused, s, [&] { return launch_score_fused(a, s); });
+        else err = run_stage(st, s, [&] { return launch_score_stats(a, s); });
+        break;
+      case kStageScoreCombine:
+        if (!a.g.fused) err = run_stage(st, s, [&] { return launch_score_combine(a, s); });
+        break;
+      case kStageScoreProbs:
+        if (!a.g.fused) err = run_stage(st, s, [&] { return launch_score_probs(a, s); });
+        break;
       case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
       case kStageReservoirKeys: {
         // Per-head budgets are settled before any stage that reads them.  On
@@ -423,6 +438,7 @@ nx_status nx_read_device_status(const nx_desc* desc) {
     if (hipMemcpy(desc->workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
       return NX_EHIP;
   }
+  if (word & kStatusSyncTimeout) return NX_EHIP;
   if (word & kStatusNonFinite) return NX_ENONFINITE;
   if (word & kStatusBadItem) return NX_EINVAL;
   return NX_OK;
@@ -475,7 +491,7 @@ const char* nx_stage_name(int32_t stage) {
   static const char* names[kNumStages] = {"score_stats", "score_combine",  "score_probs",
                                           "walk_coef",   "reservoir_keys", "topb_select",
                                           "kv_compact",  "sample_select", "estimate_keys",
-                                          "head_budget"};
+                                          "head_budget", "score_fused"};
   return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
 }
 

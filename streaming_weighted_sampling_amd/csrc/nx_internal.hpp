@@ -47,6 +47,7 @@ enum Stage {
   kStageSampleSelect,   // select on estimate codes in registers (n <= kFusedMaxTokens)
   kStageEstimateKeys,   // estimate codes of the keys (n <= kFusedMaxTokens)
   kStageHeadBudget,     // per-head budgets (before the keys; NX_HEADS_GIVEN / _ALLOC)
+  kStageScoreFused,     // single-read scoring in place of stats, combine and probs
   kNumStages
 };
 
@@ -64,11 +65,12 @@ struct Geometry {
   int32_t block;         // tokens per selection unit (1, or a block size up to 32)
   int32_t inplace;       // 1: compaction rearranges k / v in place (hole filling)
   int32_t head_alloc;    // NX_HEADS_UNIFORM / _GIVEN / _ALLOC
+  int32_t fused;         // 1: one score_fused launch replaces the two sweeps (tok_per_block 256)
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
-  size_t status, part1, beta, a, p, gram, coef, keys, selp, ahist, acand, acnt, total;
+  size_t status, sync, part1, beta, a, p, gram, coef, keys, selp, ahist, acand, acnt, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -78,6 +80,7 @@ inline WsLayout ws_layout(const Geometry& g) {
   size_t off = 0;
   const size_t hu = size_t(g.n_hu), nm = size_t(g.max_tokens);
   L.status = off; off = align256(off + 256);
+  L.sync = off;   off = align256(off + hu * 2 * sizeof(uint32_t));
   L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
   L.a = off;      off = align256(off + hu * nm * sizeof(float));
@@ -101,6 +104,7 @@ inline WsLayout ws_layout(const Geometry& g) {
 // Device status bits (OR-ed into the workspace status word).
 constexpr uint32_t kStatusNonFinite = 1u;
 constexpr uint32_t kStatusBadItem = 2u;
+constexpr uint32_t kStatusSyncTimeout = 4u;   // a per-unit barrier of score_fused gave up
 
 // Kernel argument block, passed by value to every stage.
 struct Args {
@@ -114,6 +118,7 @@ struct Args {
   uint64_t seed;
   // workspace
   uint32_t* status;
+  uint32_t* sync;  // [n_hu][2]: arrival counters of score_fused's two per-unit barriers
   float* part1;    // [n_hu][n_t1][rows_pad][2]: (max, sum) in log2 units
   float* beta;     // [n_hu][rows_pad]
   float* a;        // [n_hu][max_tokens]: direct score
@@ -139,6 +144,8 @@ struct Args {
 hipError_t launch_score_stats(const Args& a, hipStream_t s);
 hipError_t launch_score_combine(const Args& a, hipStream_t s);
 hipError_t launch_score_probs(const Args& a, hipStream_t s);
+hipError_t launch_score_fused(const Args& a, hipStream_t s);
+bool score_fused_fits(const Geometry& g);   // shape and device allow score_fused
 hipError_t launch_walk_coef(const Args& a, hipStream_t s);
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
 hipError_t launch_topb_select(const Args& a, hipStream_t s);

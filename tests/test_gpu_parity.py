@@ -470,10 +470,15 @@ def _synthetic(h_q, h_kv, d, W, dtype, n, seed):
     return q.to(dtype), k.to(dtype)
 
 
+@pytest.mark.parametrize("mode", [nx.SCORE_TWO_SWEEPS, nx.SCORE_ONE_READ], ids=["two_sweeps", "one_read"])
 @pytest.mark.parametrize("case", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
-def test_nexus_weights_match_oracle(case):
+def test_nexus_weights_match_oracle(case, mode):
     name, h_q, h_kv, d, W, dtype, n, walk = case
-    cfg = _cfg(h_q, h_kv, d, W, dtype)
+    one_read_fits = (dtype == torch.bfloat16 and d == 128 and h_q // h_kv * W <= 128 and
+                     (walk == 0 or (h_q // h_kv == 4 and walk <= 8) or (h_q // h_kv == 8 and walk <= 4)))
+    if mode == nx.SCORE_ONE_READ and not one_read_fits:
+        pytest.skip("shape outside the single-read kernel (NX_EUNSUPPORTED, checked on the host)")
+    cfg = _cfg(h_q, h_kv, d, W, dtype, score_mode=mode)
     ws = _ws(cfg, n, walk=walk)
     q, k = _synthetic(h_q, h_kv, d, W, dtype, n, seed=zlib.crc32(name.encode()))
     w = nx.nx_nexus_weights(cfg, q, k, n, walk, workspace=ws)
@@ -481,6 +486,60 @@ def test_nexus_weights_match_oracle(case):
     ref = gc.oracle_weights(q, k, n, walk, h_q // h_kv)
     for h in range(h_kv):
         gc.assert_weights_close(w[h].cpu().numpy(), ref[h], f"{name} head {h}")
+
+
+# Shapes of the single-read path (bf16, D = 128, G*W <= 128): padded M-tiles,
+# the G = 8 walk, 32 walk rows, no walk, tile edges, one token.
+ONE_READ_CASES = [
+    # name, h_q, h_kv, W, N, walk
+    ("rows64", 16, 4, 16, 3000, 3),
+    ("rows32_g4", 8, 2, 8, 1111, 2),
+    ("g8_h4", 32, 4, 16, 2500, 4),
+    ("g4_h8", 32, 8, 32, 1300, 8),
+    ("h0", 32, 8, 32, 700, 0),
+    ("tile_edge_257", 32, 8, 32, 257, 3),
+    ("one_tile_256", 32, 8, 32, 256, 3),
+    ("one_token", 32, 8, 32, 1, 3),
+    ("llama_8k", 32, 8, 32, 8192, 3),
+]
+
+
+@pytest.mark.parametrize("case", ONE_READ_CASES, ids=[c[0] for c in ONE_READ_CASES])
+def test_one_read_scoring_matches_oracle_and_two_sweeps(case):
+    """K read once (score_fused) against the oracle, and against the two-sweep
+    path on the same inputs (both fp32 over the same bf16 values)."""
+    name, h_q, h_kv, W, n, walk = case
+    q, k = _synthetic(h_q, h_kv, 128, W, torch.bfloat16, n, seed=zlib.crc32(name.encode()) + 7)
+    out = {}
+    for mode in (nx.SCORE_ONE_READ, nx.SCORE_TWO_SWEEPS):
+        cfg = _cfg(h_q, h_kv, 128, W, score_mode=mode)
+        ws = _ws(cfg, n, walk=walk)
+        out[mode] = nx.nx_nexus_weights(cfg, q, k, n, walk, workspace=ws).cpu().numpy()
+        nx.nx_read_device_status(cfg, ws)
+    ref = gc.oracle_weights(q, k, n, walk, h_q // h_kv)
+    for h in range(h_kv):
+        gc.assert_weights_close(out[nx.SCORE_ONE_READ][h], ref[h], f"{name} head {h}")
+        np.testing.assert_allclose(out[nx.SCORE_ONE_READ][h], out[nx.SCORE_TWO_SWEEPS][h],
+                                   rtol=2e-5, atol=1e-30)
+
+
+def test_one_read_many_items_per_workgroup():
+    """64 KV heads x 20 tiles (ragged tail) = 1280 (head unit, tile) items, more
+    than the grid's resident workgroups: every workgroup walks several items,
+    each time under a different head unit's barriers."""
+    h_q, h_kv, W, n, walk = 256, 64, 32, 5000, 3
+    q, k = _synthetic(h_q, h_kv, 128, W, torch.bfloat16, n, seed=901)
+    out = {}
+    for mode in (nx.SCORE_ONE_READ, nx.SCORE_TWO_SWEEPS):
+        cfg = _cfg(h_q, h_kv, 128, W, score_mode=mode)
+        ws = _ws(cfg, n, walk=walk)
+        out[mode] = nx.nx_nexus_weights(cfg, q, k, n, walk, workspace=ws).cpu().numpy()
+        nx.nx_read_device_status(cfg, ws)
+    np.testing.assert_allclose(out[nx.SCORE_ONE_READ], out[nx.SCORE_TWO_SWEEPS], rtol=2e-5, atol=1e-30)
+    heads = [0, 1, 31, 62, 63]
+    ref = gc.oracle_weights(q, k, n, walk, h_q // h_kv, heads=heads)
+    for h in heads:
+        gc.assert_weights_close(out[nx.SCORE_ONE_READ][h], ref[h], f"head {h}")
 
 
 def test_workload_weights_match_oracle():
@@ -500,14 +559,16 @@ def test_workload_weights_match_oracle():
 
 # -------------------------------------------------------------- end to end --
 
-def _end_to_end(wl_name, n=None, budget=None, walk=None, seed=0, layer=0, step=0, sink=0, recent=0):
+def _end_to_end(wl_name, n=None, budget=None, walk=None, seed=0, layer=0, step=0, sink=0, recent=0,
+                score_mode=0):
     wl = WORKLOADS[wl_name]
     n = wl.n_tokens if n is None else n
     budget = wl.budget if budget is None else budget
     walk = wl.walk_iters if walk is None else walk
     dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     x = gen_layer(wl, device=DEV, n_tokens=n)
-    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, dtype, n_sink=sink, n_recent=recent)
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, dtype, n_sink=sink, n_recent=recent,
+               score_mode=score_mode)
     ws = _ws(cfg, n, walk=walk)
     keep, ok, ov = nx.nx_evict_step(cfg, x["q"], x["k"], x["v"], n, budget, walk, seed,
                                     workspace=ws, layer=layer, step=step)
@@ -542,6 +603,11 @@ def test_evict_step_llama_layer():
     _end_to_end("llama3_8b_layer", layer=3, step=11, seed=42)
 
 
+def test_evict_step_llama_layer_one_read():
+    _end_to_end("llama3_8b_layer", layer=3, step=11, seed=42, score_mode=nx.SCORE_ONE_READ)
+    _end_to_end("llama3_8b_layer", n=2000, budget=400, sink=4, recent=16, score_mode=nx.SCORE_ONE_READ)
+
+
 def test_evict_step_forced_slots_and_edges():
     _end_to_end("llama3_8b_layer", n=2000, budget=400, sink=4, recent=16)
     _end_to_end("llama3_8b_layer", n=300, budget=300)       # B == N keeps all
@@ -570,9 +636,11 @@ def test_nonfinite_input_sets_device_status():
     nx.nx_read_device_status(cfg, ws)       # the status word was cleared
 
 
-def test_stats_overflow_fallback():
-    """Logits far above the first tile's max take the exact fallback sweep."""
-    cfg = _cfg(4, 1, 128, 4)
+@pytest.mark.parametrize("mode", [nx.SCORE_TWO_SWEEPS, nx.SCORE_ONE_READ], ids=["two_sweeps", "one_read"])
+def test_stats_overflow_fallback(mode):
+    """Logits far above the first tile's max take the exact fallback sweep of the
+    two-sweep path; the single-read path takes each tile's exact max."""
+    cfg = _cfg(4, 1, 128, 4, score_mode=mode)
     n = 600
     ws = _ws(cfg, n)
     q = torch.zeros(4, 4, 128, device=DEV)
