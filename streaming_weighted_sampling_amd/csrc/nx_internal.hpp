@@ -1,17 +1,23 @@
 // Internal interface between the C ABI (abi.cpp) and the HIP kernels.
 //
-// One eviction event runs seven kernel stages over "head units" (one head
+// One eviction event runs these kernel stages over "head units" (one head
 // unit = one KV head of one (sequence, layer) item):
 //   score_stats    window logits Q K^T / sqrt(D) with bf16/fp32 MFMA; per tile
 //                  and window row the max and the sum of exponentials
 //   score_combine  merge the tile statistics of every window row
 //   score_probs    logits again, probabilities averaged over the GQA group:
 //                  direct score a, the H walk rows, and their Gram partials
+//   (score_fused   on request, the three above with one read of K: per-unit
+//                  barriers inside a cooperative grid)
 //   walk_coef      reduce the Gram partials, run the walk recurrence, store
 //                  the per-row coefficients gamma_t / ||C||_1
-//   reservoir_keys Nexus weight, Philox uniform, fp64 key
-//   topb_select    radix select of the budget largest keys, ascending indices
-//   kv_compact     gather of the kept K/V rows (+ optional appended rows)
+//   estimate_keys + sample_select (head units of up to kFusedMaxTokens units,
+//                  one draw per token): fp32 estimates of the keys, radix
+//                  select in registers, exact fp64 keys near the boundary
+//   reservoir_keys + topb_select (otherwise): Nexus weight, Philox uniform,
+//                  fp64 key; radix select of the budget largest keys
+//   kv_compact     gather of the kept K/V rows (+ optional appended rows), or
+//                  kv_fill_holes + kv_append for in-place compaction
 // and, with per-head budgets, head_budget (before the keys).
 #pragma once
 
