@@ -372,6 +372,10 @@ def main():
             "step_algorithmic": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
         },
         "roofline": roofline,
+        # The whole step against HBM: one K read plus the compaction's K/V traffic.
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": int(k_bytes + compact_bytes),
+                          "ms_at_peak": round((k_bytes + compact_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                          "frac": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg, args.block)
