@@ -214,6 +214,99 @@ def survival_bench(args):
     }))
 
 
+def other_workload(args):
+    """One eviction event of the ragged batch or of the 70B-shaped share, timed
+    like the headline (HIP events around the dominant kernel, wall clock for the
+    step) and reported against its own bound: HBM for the ragged batch, bf16
+    MFMA for the 70B share (G*W = 512 query rows per K byte).  No CPU baseline."""
+    from workloads import budget_for, gen_model, ragged_lengths
+    dev = "cuda"
+    wl = WORKLOADS[args.workload]
+    D, Hk, L = wl.head_dim, wl.h_kv, wl.n_layers
+    lens = ragged_lengths(wl) if args.workload == "ragged16_zipf" else [wl.n_tokens]
+    items, keep_bufs = [], []
+    tokens = kept_rows = 0
+    for s, n in enumerate(lens):
+        B = budget_for(n) if args.workload == "ragged16_zipf" else wl.budget
+        q, k, v = gen_model(wl, device=dev, n_tokens=n, seq=s)
+        keep = torch.empty(L, Hk, B, dtype=torch.int32, device=dev)
+        ok = torch.empty(L, Hk, B, D, dtype=torch.bfloat16, device=dev)
+        ov = torch.empty_like(ok)
+        keep_bufs.append((q, k, v, keep, ok, ov))
+        for l in range(L):
+            items.append(dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=ok[l], out_v=ov[l],
+                              kv_head_stride=n * D, out_head_stride=B * D, n_tokens=n,
+                              budget=B, layer=l, seq_id=s))
+        tokens += L * Hk * n
+        kept_rows += L * Hk * min(B, n)
+    n_max = max(lens)
+    units = nx.make_units(items, device=dev)
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, D, wl.window, torch.bfloat16)
+    ws = nx.new_workspace(cfg, n_max, len(items), wl.walk_iters, device=dev)
+    b_max = max(it["budget"] for it in items)
+
+    def step(i):
+        nx.nx_evict_batch(cfg, units, len(items), n_max, wl.walk_iters, 0, workspace=ws, step=i,
+                          max_out_rows=b_max)
+
+    for i in range(args.warmup):
+        step(i)
+    nx.nx_read_device_status(cfg, ws)
+    torch.cuda.synchronize()
+    nx.profile_enable(True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    nx.profile_enable(False)
+    per_launch = {name: (ms / max(cnt, 1), cnt) for name, (ms, cnt) in nx.profile_read().items() if cnt}
+    e = 2
+    k_bytes = tokens * D * e
+    compact_bytes = kept_rows * (4 * D * e + 4)
+    qk_flops = tokens * 2 * wl.group * wl.window * D       # one sweep
+    if args.workload == "llama70b_share":
+        work = {"score_stats": (qk_flops / 1e12, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma"),
+                "score_probs": (qk_flops / 1e12, "TFLOP/s", BF16_PEAK_TFLOPS, "mfma")}
+    else:
+        work = {"score_stats": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm"),
+                "score_probs": (k_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm")}
+    work["kv_compact"] = (compact_bytes / 1e9, "GB/s", HBM_PEAK_GBS, "hbm")
+    dominant = max((s for s in per_launch if s in work), key=lambda s: per_launch[s][0])
+    nx.profile_enable(True, stages=[dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nx.profile_enable(False)
+    dom_ms, dom_cnt = nx.profile_read()[dominant]
+    nx.nx_read_device_status(cfg, ws)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom = dom_ms / max(dom_cnt, 1)
+    amount, unit, peak, bound = work[dominant]
+    achieved = amount / (dom * 1e-3)
+    print(json.dumps({
+        "metric": f"KV tokens scored+sampled/sec and eviction-step latency, {args.workload}, 1 MI355X",
+        "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "KV tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "items": len(items), "layers": L, "kv_heads": Hk,
+                   "group": wl.group, "window": wl.window, "walk_iters": wl.walk_iters,
+                   "n_tokens_min": min(lens), "n_tokens_max": n_max, "kv_tokens": tokens,
+                   "kept_rows": kept_rows},
+        "stage_ms_per_launch": {k: round(v[0], 4) for k, v in per_launch.items()},
+        "qk_tflops_per_sweep": {s: round(qk_flops / (per_launch[s][0] * 1e-3) / 1e12, 1)
+                                for s in ("score_stats", "score_probs") if s in per_launch},
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": dominant,
+                     "kernel_ms_per_launch": round(dom, 4), "launches_timed": dom_cnt},
+        "step_roofline": {"bound": "hbm", "algorithmic_bytes": int(k_bytes + compact_bytes),
+                          "ms_at_peak": round((k_bytes + compact_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+                          "frac": round((k_bytes + compact_bytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +331,10 @@ def main():
     ap.add_argument("--score", choices=["two-sweeps", "one-read"], default="two-sweeps",
                     help="score pass: two sweeps over K (default), or K read once with "
                          "in-kernel per-unit barriers")
+    ap.add_argument("--workload", choices=["llama3_8b_stream32", "ragged16_zipf", "llama70b_share"],
+                    default="llama3_8b_stream32",
+                    help="the headline 32-layer event (default), the ragged 16-sequence batch, or "
+                         "the 8-layer 70B-shaped share at N = 131072")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1-GiB device copy (3 times), the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -260,6 +357,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "repeats": 3}))
         return
 
+    if args.workload != "llama3_8b_stream32":
+        other_workload(args)
+        return
     wl = WORKLOADS["llama3_8b_stream32"]
     if args.survival:
         survival_bench(args)

@@ -29,6 +29,8 @@
 // [half*D/2, half*D/2 + D/2), the same dims for A and B, so every lane reads
 // one contiguous half-row of 16-B chunks.  Output register v of lane l is
 // C[8*(v/4) + 4*(l/32) + v%4][l % 32].
+#include <atomic>
+
 #include "nx_device.hpp"
 
 namespace nx {
@@ -1164,10 +1166,10 @@ hipError_t launch_pass(const Args& a, hipStream_t s) {
 // Workgroups of the fused kernel that fit on the device at once (cached per
 // device): the grid of its cooperative launch.
 int fused_capacity(int kWalkMode) {
-  static int cap[64][3];
+  static std::atomic<int> cap[64][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& c = cap[dev][kWalkMode];
+  int c = cap[dev][kWalkMode].load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per_cu = 0, coop = 0;
     const void* f = kWalkMode == 0 ? reinterpret_cast<const void*>(score_fused_kernel<kWalkNone>)
@@ -1179,6 +1181,7 @@ int fused_capacity(int kWalkMode) {
       c = -1;
     else
       c = cus * per_cu > 0 ? cus * per_cu : -1;
+    cap[dev][kWalkMode].store(c, std::memory_order_relaxed);
   }
   return c;
 }
