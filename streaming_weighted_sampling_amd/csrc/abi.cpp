@@ -174,13 +174,14 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 }
 
 // Enqueue stages [first, last] in order.
-// Items of up to kFusedMaxTokens tokens select on estimate codes held in the
-// select kernel's registers (estimate_keys + sample_select) when the call goes
-// on to selection (not the weights-only export) with one draw per token.
+// Items of up to kWideMaxTokens units select on estimate codes (estimate_keys
+// + sample_select; held in the select kernel's registers up to
+// kFusedMaxTokens) when the call goes on to selection (not the weights-only
+// export) with one draw per token.
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   hipError_t err = hipSuccess;
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
-  const bool fused = max_units <= kFusedMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
+  const bool fused = max_units <= kWideMaxTokens && !a.stop_after_weights && a.n_avg == 1 &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
   // The stages from the keys on read the per-head budgets of this call.
   Args live = a;

@@ -11,9 +11,10 @@
 //                  barriers inside a cooperative grid)
 //   walk_coef      reduce the Gram partials, run the walk recurrence, store
 //                  the per-row coefficients gamma_t / ||C||_1
-//   estimate_keys + sample_select (head units of up to kFusedMaxTokens units,
+//   estimate_keys + sample_select (head units of up to kWideMaxTokens units,
 //                  one draw per token): fp32 estimates of the keys, radix
-//                  select in registers, exact fp64 keys near the boundary
+//                  select (codes in registers up to kFusedMaxTokens units,
+//                  else re-read per pass), exact fp64 keys near the boundary
 //   reservoir_keys + topb_select (otherwise): Nexus weight, Philox uniform,
 //                  fp64 key; radix select of the budget largest keys
 //   kv_compact     gather of the kept K/V rows (+ optional appended rows), or
@@ -37,7 +38,8 @@ constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two
 constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
 constexpr int kFusedPer = 32;        // tokens per lane of the fused keys + select kernel
-constexpr int kFusedMaxTokens = 1024 * kFusedPer;   // largest n it handles
+constexpr int kFusedMaxTokens = 1024 * kFusedPer;   // largest n it handles in registers
+constexpr int kWideMaxTokens = 8 * kFusedMaxTokens;  // largest n of the estimate-code select
 constexpr int kAllocBins = 4096;     // per-item histogram of bits 30..19 of the weight codes
 constexpr int kAllocShift = 19;
 constexpr int kAllocCand = 8192;     // boundary-bin codes held per item (and per head unit)
@@ -50,8 +52,8 @@ enum Stage {
   kStageReservoirKeys,
   kStageTopbSelect,
   kStageKvCompact,
-  kStageSampleSelect,   // select on estimate codes in registers (n <= kFusedMaxTokens)
-  kStageEstimateKeys,   // estimate codes of the keys (n <= kFusedMaxTokens)
+  kStageSampleSelect,   // select on estimate codes (n <= kWideMaxTokens)
+  kStageEstimateKeys,   // estimate codes of the keys (n <= kWideMaxTokens)
   kStageHeadBudget,     // per-head budgets (before the keys; NX_HEADS_GIVEN / _ALLOC)
   kStageScoreFused,     // single-read scoring in place of stats, combine and probs
   kNumStages

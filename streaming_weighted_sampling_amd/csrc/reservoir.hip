@@ -226,8 +226,14 @@ __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
 // under `mask` exceed `prefix` are kept; of the `eq` keys equal to it under
 // the mask, `need` are kept (all of them when eq == need, else the ones with
 // the largest indices: true ties, every bit fixed).
+// Each digit bin is counted in kHistCopies words, one per lane residue mod
+// kHistCopies: lanes that share a bin then hit at most 64 / kHistCopies the
+// same LDS word (same-address atomics of a wavefront serialise; the estimate
+// codes' first digit puts most of a wavefront in a few bins).
+constexpr int kHistCopies = 8;
+
 struct SelCore {
-  uint32_t hist[256];
+  uint32_t hist[256 * kHistCopies];   // [bin][copy]
   uint64_t prefix, mask;
   int need, eq, done, start, cut;
   int cnt[kSelWaves];
@@ -258,8 +264,9 @@ __device__ inline void sel_init(SelCore& sh, uint64_t o, uint64_t an, int n, int
 // the lanes find the bin that holds the need-th largest candidate.
 __device__ inline void sel_pick_bin(SelCore& sh, int shift, uint32_t dmask) {
   const int lane = threadIdx.x & 63;
-  const uint32_t h0 = sh.hist[4 * lane], h1 = sh.hist[4 * lane + 1], h2 = sh.hist[4 * lane + 2],
-                 h3 = sh.hist[4 * lane + 3];
+  // (copy 0 of each bin holds the bin's total; see sel_passes)
+  const uint32_t h0 = sh.hist[(4 * lane) * kHistCopies], h1 = sh.hist[(4 * lane + 1) * kHistCopies],
+                 h2 = sh.hist[(4 * lane + 2) * kHistCopies], h3 = sh.hist[(4 * lane + 3) * kHistCopies];
   const uint32_t own = h0 + h1 + h2 + h3;
   uint32_t suf = own;
 #pragma unroll
@@ -286,21 +293,39 @@ __device__ inline void sel_pick_bin(SelCore& sh, int shift, uint32_t dmask) {
 // until the boundary bin holds exactly the missing count or every bit is
 // fixed; at most 64 bits, so at most 8 passes.  code_at(i) gives the code of
 // the i-th candidate slot of this thread (slot count `slots`, valid(i)).
-template <typename CodeAt, typename Valid>
+template <int kBatch = 1, typename CodeAt, typename Valid>
 __device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Valid&& valid) {
   int start = sh.start;
   while (!sh.done && start >= 0) {
     const int shift = start >= 7 ? start - 7 : 0;
     const int width = start - shift + 1;
     const uint32_t dmask = (1u << width) - 1u;
-    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
+    for (int b = threadIdx.x; b < 256 * kHistCopies; b += blockDim.x) sh.hist[b] = 0;
     __syncthreads();
     const uint64_t prefix = sh.prefix, mask = sh.mask;
-    for (int i = 0; i < slots; ++i) {
-      if (valid(i)) {
-        const uint64_t c = code_at(i);
-        if ((c & mask) == prefix) atomicAdd(&sh.hist[uint32_t(c >> shift) & dmask], 1u);
+    const uint32_t copy = threadIdx.x & (kHistCopies - 1);
+    // kBatch candidate slots at a time: for codes read from memory (kBatch
+    // 8) their loads are all issued before the first is used, one round
+    // trip per batch; codes in registers or LDS take kBatch 1.
+    for (int i0 = 0; i0 < slots; i0 += kBatch) {
+      uint64_t c[kBatch];
+      bool ok[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        ok[k] = i0 + k < slots && valid(i0 + k);
+        c[k] = ok[k] ? code_at(i0 + k) : 0ull;
       }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (ok[k] && (c[k] & mask) == prefix)
+          atomicAdd(&sh.hist[((uint32_t(c[k] >> shift) & dmask) * kHistCopies) | copy], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {   // fold bin threadIdx.x's copies into copy 0
+      uint32_t t = 0;
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c) t += sh.hist[threadIdx.x * kHistCopies + c];
+      sh.hist[threadIdx.x * kHistCopies] = t;
     }
     __syncthreads();
     if (threadIdx.x < 64) sel_pick_bin(sh, shift, dmask);
@@ -317,7 +342,7 @@ __device__ inline void select_global(const Args& a, const HeadUnit& u, const uin
   if (tid == 0) sel_init(sh, o, an, n, u.budget);
   __syncthreads();
   const int slots = (n + kSelThreads - 1) / kSelThreads;
-  sel_passes(sh, slots, [&](int i) { return keys[tid + kSelThreads * i]; },
+  sel_passes<8>(sh, slots, [&](int i) { return keys[tid + kSelThreads * i]; },
              [&](int i) { return tid + kSelThreads * i < n; });
   if (!sh.done) {
     // Unreachable with consistent inputs; report and keep the oldest tokens.
@@ -348,11 +373,14 @@ __device__ inline void select_global(const Args& a, const HeadUnit& u, const uin
   }
   const int cut = sh.cut;
   int base = 0;
+  uint64_t next = tid < n ? keys[tid] : 0ull;   // this round's key, loaded a round ahead
   for (int r = 0; r < slots; ++r) {
     const int j = r * kSelThreads + tid;
+    const uint64_t kj = next;
+    next = j + kSelThreads < n ? keys[j + kSelThreads] : 0ull;
     bool keep = false;
     if (j < n) {
-      const uint64_t top = keys[j] & mask;
+      const uint64_t top = kj & mask;
       keep = top > prefix || (top == prefix && (!ties || j >= cut));
     }
     int tot;
@@ -774,6 +802,194 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   }
 }
 
+// Selection on estimate codes for head units of more than kFusedMaxTokens
+// units (up to kWideMaxTokens): the radix select, band and exact keys of
+// sample_select_kernel, with the 32-bit codes read from the head unit's key
+// array on every pass instead of held in registers.  The band argument does
+// not depend on n, so the kept set again equals the selection on exact keys.
+// f(j, code) for this thread's tokens j = tid + 1024 i < n, eight loads issued
+// before the first use.
+template <typename F>
+__device__ __forceinline__ void for_codes(const uint32_t* codes, int n, int slots, F&& f) {
+  for (int i0 = 0; i0 < slots; i0 += 8) {
+    uint32_t c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = int(threadIdx.x) + kSelThreads * (i0 + k);
+      c[k] = j < n ? codes[j] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = int(threadIdx.x) + kSelThreads * (i0 + k);
+      if (j < n) f(j, c[k]);
+    }
+  }
+}
+
+struct WideShared {
+  SelCore core;
+  float coef[kMaxWalk];
+  int n_band, n_above;
+  uint32_t cb;
+  uint32_t band_idx[kBandCap];
+  uint64_t band_code[kBandCap];
+  uint32_t chosen[kWideMaxTokens / 32];
+};
+
+__global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int n = u.nu;
+  __shared__ WideShared sh;
+  SelCore& core = sh.core;
+  const int tid = threadIdx.x;
+  if (tid < kMaxWalk) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
+  __syncthreads();
+  const size_t ext = size_t(u.h) * u.nu;
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
+                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
+  const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
+  if (u.keep != nullptr && u.budget >= n && a.keys_out == nullptr) {
+    for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+    return;
+  }
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
+  const int slots = (n + kSelThreads - 1) / kSelThreads;
+  bool fallback = !uses_estimate(a, u) || n > kWideMaxTokens;
+  uint32_t hi = 0;
+  int need2 = 0, m = 0;
+  if (!fallback) {
+    uint32_t v_or = 0, v_and = 0xFFFFFFFFu;
+    for_codes(codes, n, slots, [&](int, uint32_t c) { v_or |= c; v_and &= c; });
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      v_or |= uint32_t(__shfl_xor(int(v_or), mm, 64));
+      v_and &= uint32_t(__shfl_xor(int(v_and), mm, 64));
+    }
+    if ((tid & 63) == 0) { core.red_or[tid >> 6] = v_or; core.red_and[tid >> 6] = v_and; }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t o = 0, an = 0xFFFFFFFFull;
+      for (int w = 0; w < kSelWaves; ++w) { o |= core.red_or[w]; an &= core.red_and[w]; }
+      sel_init(core, o | 0xFFFFFFFF00000000ull, an | 0xFFFFFFFF00000000ull, n, u.budget);
+      sh.n_band = 0;
+      sh.n_above = 0;
+      sh.cb = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    sel_passes<8>(core, slots, [&](int i) { return uint64_t(codes[tid + kSelThreads * i]) | 0xFFFFFFFF00000000ull; },
+               [&](int i) { return tid + kSelThreads * i < n; });
+    if (!core.done) {
+      if (tid == 0) raise_status(a, kStatusBadItem);
+      for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+      return;
+    }
+    // The B-th largest estimate: the smallest code of the boundary bin.
+    {
+      uint32_t mn = 0xFFFFFFFFu;
+      const uint64_t prefix = core.prefix, mask = core.mask;
+      for_codes(codes, n, slots, [&](int, uint32_t c) {
+        if (((uint64_t(c) | 0xFFFFFFFF00000000ull) & mask) == prefix) mn = min(mn, c);
+      });
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), mm, 64)));
+      if ((tid & 63) == 0) atomicMin(&sh.cb, mn);
+    }
+    __syncthreads();
+    const uint32_t cb = sh.cb;
+    uint32_t lo;
+    if (cb == 0u || cb == 0xFFFFFFFFu) {
+      lo = hi = cb;   // boundary in the -inf or +inf class: exact there, decided by index
+    } else {
+      const float v = f32_decode(cb);
+      lo = min(max(f32_code(v - kBand), 1u), 0xFFFFFFFEu);
+      hi = min(max(f32_code(v + kBand), 1u), 0xFFFFFFFEu);
+    }
+    int above = 0;
+    for_codes(codes, n, slots, [&](int j, uint32_t c) {
+      if (c > hi) {
+        ++above;
+      } else if (c >= lo) {
+        const int pos = atomicAdd(&sh.n_band, 1);
+        if (pos < kBandCap) sh.band_idx[pos] = uint32_t(j);
+      }
+    });
+    for (int c = tid; c < (n + 31) / 32; c += kSelThreads) sh.chosen[c] = 0;
+    atomicAdd(&sh.n_above, above);
+    __syncthreads();
+    m = sh.n_band;
+    need2 = u.budget - sh.n_above;
+    fallback = m > kBandCap || need2 < 1 || need2 > m;
+  }
+
+  if (fallback) {
+    // Exact keys of every token (over the codes, all read by now), then the
+    // global-memory selection.
+    __syncthreads();
+    uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
+    uint64_t o = 0, an = ~0ull;
+    for (int j = tid; j < n; j += kSelThreads) {
+      const double key = exact_key(a, u, j, ws(a, sh.coef, j), k0, k1);
+      if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
+      const uint64_t c = key_code(key);
+      keys[j] = c;
+      o |= c;
+      an &= c;
+    }
+    if (u.keep == nullptr) return;
+    if (u.budget >= n) {
+      for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+      return;
+    }
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      o |= __shfl_xor(o, mm, 64);
+      an &= __shfl_xor(an, mm, 64);
+    }
+    if ((tid & 63) == 0) { core.red_or[tid >> 6] = o; core.red_and[tid >> 6] = an; }
+    __syncthreads();
+    uint64_t ob = 0, anb = ~0ull;
+    for (int w = 0; w < kSelWaves; ++w) { ob |= core.red_or[w]; anb &= core.red_and[w]; }
+    __syncthreads();
+    select_global(a, u, keys, ob, anb, core);
+    return;
+  }
+
+  // Exact keys of the band; the first need2 in ((code, index) descending) win.
+  for (int t = tid; t < m; t += kSelThreads) {
+    const int j = int(sh.band_idx[t]);
+    sh.band_code[t] = key_code(exact_key(a, u, j, ws(a, sh.coef, j), k0, k1));
+  }
+  __syncthreads();
+  for (int t = tid; t < m; t += kSelThreads) {
+    const uint64_t ct = sh.band_code[t];
+    const uint32_t it = sh.band_idx[t];
+    int rank = 0;
+    for (int q = 0; q < m; ++q) {
+      const uint64_t cq = sh.band_code[q];
+      rank += (cq > ct || (cq == ct && sh.band_idx[q] > it)) ? 1 : 0;
+    }
+    if (rank < need2) atomicOr(&sh.chosen[it >> 5], 1u << (it & 31));
+  }
+  __syncthreads();
+  // Ascending write, 1024 tokens per round (the next round's code is loaded
+  // before this round's ranks).
+  int base = 0;
+  uint32_t next = tid < n ? codes[tid] : 0u;
+  for (int r = 0; r < slots; ++r) {
+    const int j = r * kSelThreads + tid;
+    const uint32_t c = next;
+    next = j + kSelThreads < n ? codes[j + kSelThreads] : 0u;
+    const bool keep = j < n && (c > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u));
+    int tot;
+    const int pos = block_rank(keep, core.cnt, &tot);
+    if (keep && base + pos < u.budget) u.keep[base + pos] = j;
+    base += tot;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
@@ -1106,7 +1322,7 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
       }
       __syncthreads();
       const int slots = (total + kSelThreads - 1) / kSelThreads;
-      sel_passes(sh, slots, [&](int i) { return code_at(tid + kSelThreads * i); },
+      sel_passes<8>(sh, slots, [&](int i) { return code_at(tid + kSelThreads * i); },
                  [&](int i) { return tid + kSelThreads * i < total; });
       const uint64_t prefix = sh.prefix, mask = sh.mask;
       int cur = -1, gt = 0, eq = 0;
@@ -1180,7 +1396,11 @@ hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
 }
 
 hipError_t launch_sample_select(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(sample_select_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
+  if (max_units <= kFusedMaxTokens)
+    hipLaunchKernelGGL(sample_select_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(sample_select_wide_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -108,9 +108,11 @@ def _weights(kind, h_kv, n, gen):
 @pytest.mark.parametrize("kind", ["cubic", "zeros_negative", "subnormal", "wide_range", "equal"])
 @pytest.mark.parametrize("n,budget,sink,recent", [
     (32768, 6554, 0, 0), (20001, 1, 0, 0), (5000, 4999, 0, 0), (9000, 3000, 7, 9), (1000, 250, 0, 0),
+    (32769, 6554, 0, 0), (131072, 13107, 5, 7), (262144, 52429, 0, 0), (100003, 99000, 0, 0),
 ])
 def test_estimate_select_equals_exact_select(kind, n, budget, sink, recent):
-    """Without a key export the fused kernel ranks tokens by an fp32 estimate and
+    """Without a key export the select kernel ranks tokens by an fp32 estimate
+    (codes in registers up to 32768 tokens, re-read from memory above) and
     computes fp64 keys only near the boundary; with the export every key is
     exact.  Both must keep exactly the same tokens."""
     h_kv = 8
@@ -172,15 +174,17 @@ def test_reservoir_inclusion_frequencies_match_enumeration():
 
 @pytest.mark.parametrize("n", [32768, 20001])
 def test_fused_and_two_kernel_selection_agree(n):
-    """Keys + select run fused when max_tokens <= 32768 and as two kernels
-    otherwise; the same items must give the same kept rows either way."""
+    """The selection runs on estimate codes held in registers when max_tokens
+    <= 32768, on codes re-read from memory up to 262144, and as exact keys plus
+    a global radix select above; the same items must give the same kept rows
+    on all three paths."""
     wl = WORKLOADS["llama3_8b_layer"]
     cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window)
     budget = n // 5
     layers = 2
     data = [gen_layer(wl, device=DEV, n_tokens=n, layer=l) for l in range(layers)]
     outs = []
-    for max_tokens in (n, 32769):
+    for max_tokens in (n, 32769, 262145):
         keep = torch.full((layers, wl.h_kv, budget), -1, dtype=torch.int32, device=DEV)
         ok = torch.empty(layers, wl.h_kv, budget, wl.head_dim, dtype=torch.bfloat16, device=DEV)
         ov = torch.empty_like(ok)
@@ -197,9 +201,10 @@ def test_fused_and_two_kernel_selection_agree(n):
     for l in range(layers):
         for h in range(wl.h_kv):
             gc.check_keep_valid(outs[0][0][l, h].cpu().numpy(), n, budget)
-    assert torch.equal(outs[0][0], outs[1][0])
-    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
-    assert torch.equal(outs[0][2].view(torch.int16), outs[1][2].view(torch.int16))
+    for other in outs[1:]:
+        assert torch.equal(outs[0][0], other[0])
+        assert torch.equal(outs[0][1].view(torch.int16), other[1].view(torch.int16))
+        assert torch.equal(outs[0][2].view(torch.int16), other[2].view(torch.int16))
 
 
 # ------------------------------------------ n-averaged priority (Eq. 6) --
