@@ -372,7 +372,9 @@ constexpr int kWalkNone = 0;    // H = 0
 constexpr int kWalkFast4 = 1;   // G = 4, H <= 4: P_t from register group sums
 constexpr int kWalkFast8 = 2;   // G = 8, H <= 4
 constexpr int kWalkLds = 3;     // any other shape: walk rows through LDS
-constexpr int kWalkFast4Deep = 4;   // G = 4, 4 < H <= 8
+constexpr int kWalkFast4Deep = 4;   // G = 4, 6 < H <= 8
+constexpr int kWalkFast4Mid = 5;    // G = 4, 4 < H <= 6 (fewer Gram pairs per lane than Deep,
+                                    // which keeps the kernel within 128 VGPRs)
 
 // Pass 2 on one (head unit, tile) item.
 //
@@ -408,8 +410,11 @@ template <typename T, int D, int MPW, int kWalk, bool kBlocks>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   constexpr bool kHasWalk = kWalk != kWalkNone;
-  constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep;
-  constexpr int kMaxT = kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4 : kMaxWalk;   // deepest walk
+  constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep ||
+                             kWalk == kWalkFast4Mid;
+  constexpr int kMaxT = kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4
+                        : kWalk == kWalkFast4Mid                   ? 6
+                                                                   : kMaxWalk;   // deepest walk
   constexpr int kHalfWaves = 2 * kWaves;
   constexpr int kPairsPerLane = (kMaxT * (kMaxT + 1) / 2 + kHalfWaves - 1) / kHalfWaves;
   auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(smem + GE::kSlotsProbs * GE::kTileBytes);
@@ -1102,6 +1107,7 @@ int walk_mode(const Geometry& g) {
   if (g.walk == 0) return kWalkNone;
   if (g.walk <= 4 && g.group == 4) return kWalkFast4;
   if (g.walk <= 4 && g.group == 8) return kWalkFast8;
+  if (g.walk <= 6 && g.group == 4) return kWalkFast4Mid;
   if (g.walk_rows <= 32 && g.group == 4) return kWalkFast4Deep;
   return kWalkLds;
 }
@@ -1126,6 +1132,9 @@ void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
       break;
     case kWalkFast4Deep:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4Deep, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      break;
+    case kWalkFast4Mid:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4Mid, kBlocks>), grid, dim3(kThreads), 0, s, a);
       break;
     default:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkLds, kBlocks>), grid, dim3(kThreads), 0, s, a);

@@ -461,6 +461,8 @@ SCORE_CASES = [
     ("llama_ragged_h0", 32, 8, 128, 32, torch.bfloat16, 4100, 0),
     ("llama_h1", 32, 8, 128, 32, torch.bfloat16, 777, 1),
     ("llama_h5", 32, 8, 128, 32, torch.bfloat16, 3000, 5),
+    ("llama_h6", 32, 8, 128, 32, torch.bfloat16, 2222, 6),
+    ("llama_h7", 32, 8, 128, 32, torch.bfloat16, 1999, 7),
     ("g8_w64", 64, 8, 128, 64, torch.bfloat16, 2000, 3),
     ("bf16_d64", 16, 4, 64, 8, torch.bfloat16, 1500, 8),
     ("one_token", 4, 2, 128, 4, torch.bfloat16, 1, 2),
