@@ -16,7 +16,7 @@ using namespace nx;
 namespace {
 
 constexpr int32_t kMaxTokens = 1 << 24;
-constexpr int32_t kMaxRowsPad = 512;    // 4 waves x 4 M-tiles x 32 rows
+constexpr int32_t kMaxRowsPad = 512;    // 16 wavefronts x one 32-row tile
 
 int32_t elem_size(int32_t dtype) { return dtype == NX_BF16 ? 2 : 4; }
 

@@ -101,7 +101,7 @@ __device__ inline bool row_source(const Geometry& g, int rho, int& qh, int& wpos
   return true;
 }
 
-template <typename T, int D, int MPW>
+template <typename T, int D, int MPW, int NW = kWaves>
 __device__ inline void load_q(const Args& a, const HeadUnit& u, int wave, int nn, int hh,
                               uint4 (&qf)[MPW][Geo<T, D>::kChunks]) {
   using GE = Geo<T, D>;
@@ -109,7 +109,7 @@ __device__ inline void load_q(const Args& a, const HeadUnit& u, int wave, int nn
   const Buf qb(u.q, uint32_t(a.g.group * a.g.window * GE::kRowBytes));
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
-    const int mt = wave + kWaves * i;
+    const int mt = wave + NW * i;
     int qh = 0, wpos = 0;
     const bool ok = mt < n_mt && row_source(a.g, mt * 32 + nn, qh, wpos);
     const uint32_t src = uint32_t((qh * a.g.window + wpos) * GE::kRowBytes + hh * GE::kHalfBytes);
@@ -161,7 +161,7 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
 // barrier (everyone's copies landed, everyone is done with the slot about to
 // be refilled), refill, body(st, lds).  Rows past the cache end read as zero.
 // Ends on a barrier.
-template <typename T, int D, int kSlots, int kLoaders, typename Body>
+template <typename T, int D, int kSlots, int kLoaders, int NW, typename Body>
 __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role,
                                    Body&& body) {
   using GE = Geo<T, D>;
@@ -170,7 +170,7 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* r
   static_assert((kSlots - 2) * kPerWave < 64, "vmcnt range");
   const int t1 = min(t0 + 32 * n_sub, u.n);
   const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
-  const int lw = role - (kWaves - kLoaders);   // loader index, < 0: not a loader
+  const int lw = role - (NW - kLoaders);   // loader index, < 0: not a loader
   const bool loader = lw >= 0;
   const int lane = threadIdx.x & 63;
   // Copy i of loader lw fills LDS chunk (i * kLoaders + lw) * 64 + lane.
@@ -215,7 +215,7 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* r
 // row max over the first 32 tokens) and adds 2^(y - shift) per logit;
 // kExact = true keeps a per-lane running max (two exponentials per logit) and
 // only runs when the cheap sweep overflowed.
-template <typename T, int D, int MPW, bool kExact>
+template <typename T, int D, int MPW, int NW, bool kExact>
 __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int n_sub,
                                    const uint4 (&qf)[MPW][Geo<T, D>::kChunks],
                                    float (&my)[MPW][16], float (&z)[MPW][16], char* ring) {
@@ -223,14 +223,16 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
   const int n_mt = a.g.rows_pad / 32;
   const float c = a.c_log2;
-  sweep_tiles<T, D, GE::kSlotsStats, kWaves>(u, t0, n_sub, ring, wave, [&](int st, const char* cur) {
+  // Every wavefront copies K, at least one 1-KB copy each per sub-tile.
+  constexpr int kLoaders = NW < GE::kTileBytes / 1024 ? NW : GE::kTileBytes / 1024;
+  sweep_tiles<T, D, GE::kSlotsStats, kLoaders, NW>(u, t0, n_sub, ring, wave, [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     const bool full = t0 + 32 * st + 32 <= u.n;      // wave-uniform
     const bool valid = t0 + 32 * st + nn < u.n;
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-      if (wave + kWaves * i < n_mt) {
+      if (wave + NW * i < n_mt) {
         const floatx16_t acc = mfma_tile<T, D>(qf[i], kf);
         if constexpr (!kExact) {
           if (st == 0) {
@@ -265,7 +267,7 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
 
 // Pass 1 on one (head unit, tile) item: writes the tile's (max, sum) pair
 // for every window row.
-template <typename T, int D, int MPW>
+template <typename T, int D, int MPW, int NW>
 __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   const int tpb = a.g.tok_per_block;
@@ -276,13 +278,13 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
   const int n_mt = a.g.rows_pad / 32;
 
   uint4 qf[MPW][GE::kChunks];
-  load_q<T, D, MPW>(a, u, wave, nn, hh, qf);
+  load_q<T, D, MPW, NW>(a, u, wave, nn, hh, qf);
   float my[MPW][16], z[MPW][16];
 #pragma unroll
   for (int i = 0; i < MPW; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) { my[i][v] = 0.f; z[i][v] = 0.f; }
-  stats_sweep<T, D, MPW, false>(a, u, t0, n_sub, qf, my, z, smem);
+  stats_sweep<T, D, MPW, NW, false>(a, u, t0, n_sub, qf, my, z, smem);
 
   // Merge the 32 lanes of each half (they share rows); detect overflow.
   float zr[MPW][16];
@@ -292,7 +294,7 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       zr[i][v] = half_sum(z[i][v]);
-      bad |= (wave + kWaves * i < n_mt) && !(zr[i][v] <= 0x1p126f);
+      bad |= (wave + NW * i < n_mt) && !(zr[i][v] <= 0x1p126f);
     }
   }
   if (__syncthreads_or(bad)) {
@@ -300,7 +302,7 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
     for (int i = 0; i < MPW; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) { my[i][v] = -INFINITY; z[i][v] = 0.f; }
-    stats_sweep<T, D, MPW, true>(a, u, t0, n_sub, qf, my, z, smem);
+    stats_sweep<T, D, MPW, NW, true>(a, u, t0, n_sub, qf, my, z, smem);
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
 #pragma unroll
@@ -314,7 +316,7 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
   float* out = a.part1 + (size_t(hu) * a.g.n_t1 + tile) * a.g.rows_pad * 2;
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
-    const int mt = wave + kWaves * i;
+    const int mt = wave + NW * i;
     if (mt < n_mt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -398,15 +400,15 @@ constexpr int kWalkFast4Mid = 5;    // G = 4, 4 < H <= 6 (fewer Gram pairs per l
 //     for the LDS walk, two) sub-tiles late: half-wave k = 2r + half owns the
 //     pairs p = 7 - k, 15 - k, ... (p = t(t+1)/2 + t') at one token per lane.
 // Every sum runs in a fixed order, whatever the roles.
-template <typename T, int D, int kWalk>
+template <typename T, int D, int kWalk, int NW>
 constexpr int probs_smem_bytes() {
   return Geo<T, D>::kSlotsProbs * Geo<T, D>::kTileBytes +
-         int(sizeof(float)) * 2 * 32 * ((kWalk == kWalkLds ? kMaxWalkRows : 0) + kMaxWalk + kWaves);
+         int(sizeof(float)) * 2 * 32 * ((kWalk == kWalkLds ? kMaxWalkRows : 0) + kMaxWalk + NW);
 }
 
 // kBlocks: the call selects blocks of b > 1 tokens (b = 1 kernels carry no
 // block-sum code, which keeps them within 128 VGPRs).
-template <typename T, int D, int MPW, int kWalk, bool kBlocks>
+template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   constexpr bool kHasWalk = kWalk != kWalkNone;
@@ -415,33 +417,33 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   constexpr int kMaxT = kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4
                         : kWalk == kWalkFast4Mid                   ? 6
                                                                    : kMaxWalk;   // deepest walk
-  constexpr int kHalfWaves = 2 * kWaves;
+  constexpr int kHalfWaves = 2 * NW;
   constexpr int kPairsPerLane = (kMaxT * (kMaxT + 1) / 2 + kHalfWaves - 1) / kHalfWaves;
   auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(smem + GE::kSlotsProbs * GE::kTileBytes);
-  auto s_a = reinterpret_cast<float (*)[kWaves][32]>(smem + GE::kSlotsProbs * GE::kTileBytes +
+  auto s_a = reinterpret_cast<float (*)[NW][32]>(smem + GE::kSlotsProbs * GE::kTileBytes +
                                                      2 * kMaxWalk * 32 * 4);
   auto s_walk = reinterpret_cast<float (*)[kMaxWalkRows][32]>(
-      smem + GE::kSlotsProbs * GE::kTileBytes + 2 * (kMaxWalk + kWaves) * 32 * 4);
+      smem + GE::kSlotsProbs * GE::kTileBytes + 2 * (kMaxWalk + NW) * 32 * 4);
   const int tpb = a.g.tok_per_block;
   const int t0 = tile * tpb;
   if (t0 >= u.n) return;
   const int n_sub = (min(t0 + tpb, u.n) - t0 + 31) / 32;
   const int lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
-  const int role = ((threadIdx.x >> 6) + blockIdx.x + blockIdx.y) & (kWaves - 1);
+  const int role = ((threadIdx.x >> 6) + blockIdx.x + blockIdx.y) & (NW - 1);
   const Geometry& g = a.g;
   const int n_mt = g.rows_pad / 32;
-  const int row_roles = min(n_mt, kWaves);
+  const int row_roles = min(n_mt, NW);
   const float c = a.c_log2;
   const int walk = min(g.walk, kMaxT);          // == g.walk for the mode the host picked
   const int n_pairs = walk * (walk + 1) / 2;
   const int pg = kHalfWaves - 1 - (2 * role + hh);   // first Gram pair of this half-wave
 
   uint4 qf[MPW][GE::kChunks];
-  load_q<T, D, MPW>(a, u, role, nn, hh, qf);
+  load_q<T, D, MPW, NW>(a, u, role, nn, hh, qf);
   float bt[MPW][16];
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
-    const int mt = role + kWaves * i;
+    const int mt = role + NW * i;
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       bt[i][v] = mt < n_mt ? a.beta[size_t(hu) * g.rows_pad + mt * 32 + out_row(v, hh)] : INFINITY;
@@ -536,16 +538,16 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   };
   // a_j of sub-tile s: M-tile-ordered sum of the partials (role 1, half 0),
   // likewise split into the reads and the sum and store.
-  auto a_load = [&](int s, float (&la)[kWaves]) {
+  auto a_load = [&](int s, float (&la)[NW]) {
 #pragma unroll
-    for (int r = 0; r < kWaves; ++r) la[r] = s_a[s & 1][r][nn];
+    for (int r = 0; r < NW; ++r) la[r] = s_a[s & 1][r][nn];
   };
-  auto a_store = [&](int s, const float (&la)[kWaves]) {
+  auto a_store = [&](int s, const float (&la)[NW]) {
     if (hh != 0) return;
     const int tok = t0 + 32 * s + nn;
     float sum = la[0];
 #pragma unroll
-    for (int r = 1; r < kWaves; ++r)
+    for (int r = 1; r < NW; ++r)
       if (r < row_roles) sum += la[r];
     if (blk == 1) {
       if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
@@ -556,27 +558,32 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   };
   auto a_final = [&](int s) {
     if (role != 1) return;
-    float la[kWaves];
+    float la[NW];
     a_load(s, la);
     a_store(s, la);
   };
 
-  sweep_tiles<T, D, GE::kSlotsProbs, 2>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
+  sweep_tiles<T, D, GE::kSlotsProbs, 2, NW>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
     // Lagged work on slots the previous barrier made visible: the LDS reads
     // now, ahead of the K fragment reads; the sums after the MFMA issue.
     // (The LDS walk mode keeps its lagged work in one piece, ahead of the
     // fragment reads: splitting it costs it occupancy.)
-    constexpr bool kSplitLag = kWalk != kWalkLds;
+    // With 16 wavefronts the lagged work also stays in one piece: holding
+    // sixteen a_j partials across the MFMA chain would spill.
+    constexpr bool kSplitLag = kWalk != kWalkLds && NW == kWaves;
     const bool lag = st > 0;
-    float la[kWaves], gx[kPairsPerLane], gy[kPairsPerLane];
+    float la[NW], gx[kPairsPerLane], gy[kPairsPerLane];
     if (lag) {
       if constexpr (kSplitLag) {
         if (role == 1) a_load(st - 1, la);
         if constexpr (kFastWalk) gram_load(st - 1, gx, gy);
-      } else {
+      } else if constexpr (kWalk == kWalkLds) {
         a_final(st - 1);
         walk_lds(st - 1);
         if (st > 1) gram_step(st - 2);
+      } else {
+        a_final(st - 1);
+        if constexpr (kFastWalk) gram_step(st - 1);
       }
     }
     uint4 kf[GE::kChunks];
@@ -584,7 +591,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     float tp = 0.f;
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-      const int mt = role + kWaves * i;
+      const int mt = role + NW * i;
       auto consume_lag = [&] {
         if constexpr (kSplitLag) {
           if (role == 1) a_store(st - 1, la);
@@ -1081,12 +1088,15 @@ __global__ __launch_bounds__(kThreads) void sync_zero_kernel(uint32_t* p, int n)
 }
 
 // Pass 1: one workgroup per (tile, head unit).
-template <typename T, int D, int MPW>
-__global__ __launch_bounds__(kThreads) void score_stats_kernel(const Args a) {
+// NW wavefronts per workgroup (4, or 16 for more than 4 row tiles): one row
+// tile per wavefront keeps its query fragments and row statistics within 128
+// VGPRs, four wavefronts per SIMD (four tiles per wavefront took 252-256).
+template <typename T, int D, int MPW, int NW>
+__global__ __launch_bounds__(64 * NW) void score_stats_kernel(const Args a) {
   __shared__ __align__(16) char smem[Geo<T, D>::kSlotsStats * Geo<T, D>::kTileBytes];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
-  if (u.valid) stats_item<T, D, MPW>(a, u, hu, tile, smem);
+  if (u.valid) stats_item<T, D, MPW, NW>(a, u, hu, tile, smem);
 }
 
 // Row merge: one workgroup per head unit.
@@ -1095,12 +1105,12 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 }
 
 // Pass 2: one workgroup per (tile, head unit).
-template <typename T, int D, int MPW, int kWalk, bool kBlocks>
-__global__ __launch_bounds__(kThreads) void score_probs_kernel(const Args a) {
-  __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk>()];
+template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
+__global__ __launch_bounds__(64 * NW) void score_probs_kernel(const Args a) {
+  __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk, NW>()];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
-  if (u.valid) probs_item<T, D, MPW, kWalk, kBlocks>(a, u, hu, tile, smem);
+  if (u.valid) probs_item<T, D, MPW, NW, kWalk, kBlocks>(a, u, hu, tile, smem);
 }
 
 int walk_mode(const Geometry& g) {
@@ -1112,43 +1122,41 @@ int walk_mode(const Geometry& g) {
   return kWalkLds;
 }
 
-int mtiles_per_wave(const Geometry& g) {
-  const int n_mt = g.rows_pad / 32;
-  const int per = (n_mt + kWaves - 1) / kWaves;
-  return per <= 1 ? 1 : per <= 2 ? 2 : 4;
-}
+// Wavefronts per workgroup, one row tile each: 4 up to 4 row tiles, else 16
+// (the host allows at most 16: G*W <= 512).
+int waves_per_group(const Geometry& g) { return g.rows_pad / 32 <= 4 ? 4 : 16; }
 
-template <int MPW, typename T, int D, bool kBlocks>
+template <int MPW, int NW, typename T, int D, bool kBlocks>
 void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
   switch (walk_mode(a.g)) {
     case kWalkNone:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkNone, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkNone, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkFast4:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkFast8:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast8, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast8, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkFast4Deep:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4Deep, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4Deep, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkFast4Mid:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkFast4Mid, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4Mid, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, kWalkLds, kBlocks>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkLds, kBlocks>), grid, dim3(64 * NW), 0, s, a);
   }
 }
 
-template <bool kProbs, int MPW, typename T, int D>
+template <bool kProbs, int NW, typename T, int D>
 hipError_t launch_t(const Args& a, hipStream_t s) {
   const dim3 grid(a.g.n_tmax, a.g.n_hu);
   if constexpr (kProbs) {
-    if (a.g.block > 1) launch_probs<MPW, T, D, true>(a, grid, s);
-    else launch_probs<MPW, T, D, false>(a, grid, s);
+    if (a.g.block > 1) launch_probs<1, NW, T, D, true>(a, grid, s);
+    else launch_probs<1, NW, T, D, false>(a, grid, s);
   } else {
-    hipLaunchKernelGGL((score_stats_kernel<T, D, MPW>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((score_stats_kernel<T, D, 1, NW>), grid, dim3(64 * NW), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -1156,13 +1164,10 @@ hipError_t launch_t(const Args& a, hipStream_t s) {
 template <bool kProbs>
 hipError_t launch_pass(const Args& a, hipStream_t s) {
   const Geometry& g = a.g;
-  const int mpw = mtiles_per_wave(g);
-#define NX_MPW(T, D)                                 \
-  switch (mpw) {                                     \
-    case 1: return launch_t<kProbs, 1, T, D>(a, s);  \
-    case 2: return launch_t<kProbs, 2, T, D>(a, s);  \
-    default: return launch_t<kProbs, 4, T, D>(a, s); \
-  }
+  const int nw = waves_per_group(g);
+#define NX_MPW(T, D)                                            \
+  if (nw == 4) return launch_t<kProbs, 4, T, D>(a, s);          \
+  return launch_t<kProbs, 16, T, D>(a, s);
   if (g.dtype == NX_BF16) {
     if (g.head_dim == 128) { NX_MPW(uint16_t, 128) }
     NX_MPW(uint16_t, 64)
