@@ -542,13 +542,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int r = 0; r < NW; ++r) la[r] = s_a[s & 1][r][nn];
   };
-  auto a_store = [&](int s, const float (&la)[NW]) {
-    if (hh != 0) return;
+  auto a_put = [&](int s, float sum) {   // lanes of half 0
     const int tok = t0 + 32 * s + nn;
-    float sum = la[0];
-#pragma unroll
-    for (int r = 1; r < NW; ++r)
-      if (r < row_roles) sum += la[r];
     if (blk == 1) {
       if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
     } else {
@@ -556,11 +551,34 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       if (lead && tok < u.n) a_out.stf(uint32_t((tok / blk) * 4), sum);
     }
   };
+  auto a_store = [&](int s, const float (&la)[NW]) {
+    if (hh != 0) return;
+    float sum = la[0];
+#pragma unroll
+    for (int r = 1; r < NW; ++r)
+      if (r < row_roles) sum += la[r];
+    a_put(s, sum);
+  };
   auto a_final = [&](int s) {
     if (role != 1) return;
-    float la[NW];
-    a_load(s, la);
-    a_store(s, la);
+    if constexpr (NW > kWaves) {
+      // Each lane half sums half of the partials (in role order), one swap
+      // adds the two halves.
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < NW / 2; ++r) {
+        const int rr = hh * (NW / 2) + r;
+        if (rr < row_roles) part += s_a[s & 1][rr][nn];
+      }
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                       false, false);
+      const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (hh == 0) a_put(s, sum);
+    } else {
+      float la[NW];
+      a_load(s, la);
+      a_store(s, la);
+    }
   };
 
   sweep_tiles<T, D, GE::kSlotsProbs, 2, NW>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
