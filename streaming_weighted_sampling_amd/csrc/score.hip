@@ -651,10 +651,12 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
             }
           }
         } else if constexpr (kWalk == kWalkLds) {
-          if (i == 0 && role == 0) {
+          // Walk rows are rows 0 .. G*H - 1: every row tile that holds some
+          // of them (G*H may exceed one tile's 32 rows) leaves their values.
+          if (mt * 32 < g.walk_rows) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int rho = out_row(v, hh);
+              const int rho = mt * 32 + out_row(v, hh);
               if (rho < g.walk_rows) s_walk[st & 1][rho][nn] = e[v];
             }
           }

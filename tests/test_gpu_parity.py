@@ -311,6 +311,37 @@ def test_block_mode_end_to_end(block, n):
         assert gc.rows_equal(ov[h][:len(rows)], d["v"][h], rows)
 
 
+@pytest.mark.parametrize("h_q,window,block,n", [(64, 32, 16, 3000), (64, 64, 32, 2000)])
+def test_block_mode_wide_groups(h_q, window, block, n):
+    """Blocks with G = 8 query heads per KV head and 256 or 512 window rows:
+    the score sweeps run 16-wavefront workgroups (one row tile each)."""
+    h_kv, walk = 8, 3
+    cfg = _cfg(h_q, h_kv, 128, window, block=block)
+    q, k = _synthetic(h_q, h_kv, 128, window, torch.bfloat16, n, seed=4000 + window + block)
+    v = torch.randn(k.shape, device=DEV).bfloat16()
+    nu = cfg.units(n)
+    budget = max(1, round(nu / 5))
+    ws = _ws(cfg, n, 1, walk)
+    w_gpu = nx.nx_nexus_weights(cfg, q, k, n, walk, workspace=ws)
+    nx.nx_read_device_status(cfg, ws)
+    keep, ok, ov = nx.nx_evict_step(cfg, q, k, v, n, budget, walk, 9, workspace=ws, layer=2, step=1)
+    nx.nx_read_device_status(cfg, ws)
+    qh, dt = gc.host(q)
+    kh, _ = gc.host(k)
+    vh, _ = gc.host(v)
+    ref = nexus.evict_step(qh, kh, vh, budget, walk, 9, dtype=dt, layer=2, step=1, block=block,
+                           heads=[0, 7])
+    _, on_gpu_w = nexus.select_from_weights(w_gpu.cpu().numpy(), budget, 9, layer=2, step=1)
+    for h in (0, 7):
+        gc.assert_weights_close(w_gpu[h].cpu().numpy(), ref["w"][h], f"block {block} head {h}")
+        got = gc.check_keep_valid(keep[h].cpu().numpy(), nu, budget)
+        np.testing.assert_array_equal(got, on_gpu_w[h])
+        assert gc.overlap_fraction(got, ref["keep"][h]) >= 1 - 1.0 / len(got)
+        rows = np.concatenate([np.arange(b * block, min(b * block + block, n)) for b in got])
+        assert gc.rows_equal(ok[h][:len(rows)], k[h], rows)
+        assert gc.rows_equal(ov[h][:len(rows)], v[h], rows)
+
+
 def test_block_mode_streaming_appends_after_whole_blocks():
     """Four events of append-256 / evict with blocks of 32 on four layers."""
     from streaming_weighted_sampling_amd.stream import StreamingCache
@@ -464,6 +495,9 @@ SCORE_CASES = [
     ("llama_h6", 32, 8, 128, 32, torch.bfloat16, 2222, 6),
     ("llama_h7", 32, 8, 128, 32, torch.bfloat16, 1999, 7),
     ("g8_w64", 64, 8, 128, 64, torch.bfloat16, 2000, 3),
+    ("g8_w32_h4", 64, 8, 128, 32, torch.bfloat16, 2500, 4),
+    ("g4_w48_h8", 32, 8, 128, 48, torch.bfloat16, 1700, 8),
+    ("g8_w32_lds_h6", 64, 8, 128, 32, torch.bfloat16, 1900, 6),
     ("bf16_d64", 16, 4, 64, 8, torch.bfloat16, 1500, 8),
     ("one_token", 4, 2, 128, 4, torch.bfloat16, 1, 2),
 ]
