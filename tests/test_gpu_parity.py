@@ -498,6 +498,11 @@ SCORE_CASES = [
     ("g8_w32_h4", 64, 8, 128, 32, torch.bfloat16, 2500, 4),
     ("g4_w48_h8", 32, 8, 128, 48, torch.bfloat16, 1700, 8),
     ("g8_w32_lds_h6", 64, 8, 128, 32, torch.bfloat16, 1900, 6),
+    ("g2_w16_h5", 16, 8, 128, 16, torch.bfloat16, 3000, 5),
+    ("g16_w8_h4_64walkrows", 128, 8, 128, 8, torch.bfloat16, 2100, 4),
+    ("mha_w32_h3", 8, 8, 128, 32, torch.bfloat16, 2600, 3),
+    ("f32_d128_g4", 32, 8, 128, 32, torch.float32, 1500, 3),
+    ("bf16_d64_g8_w64", 64, 8, 64, 64, torch.bfloat16, 1800, 3),
     ("bf16_d64", 16, 4, 64, 8, torch.bfloat16, 1500, 8),
     ("one_token", 4, 2, 128, 4, torch.bfloat16, 1, 2),
 ]
