@@ -834,6 +834,8 @@ struct WideShared {
   uint32_t band_idx[kBandCap];
   uint64_t band_code[kBandCap];
   uint32_t chosen[kWideMaxTokens / 32];
+  int round_cnt[kFusedPer * kSelWaves];
+  int group_total;
 };
 
 __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const Args a) {
@@ -974,19 +976,52 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
     if (rank < need2) atomicOr(&sh.chosen[it >> 5], 1u << (it & 31));
   }
   __syncthreads();
-  // Ascending write, 1024 tokens per round (the next round's code is loaded
-  // before this round's ranks).
+  // Ascending write in groups of kFusedPer rounds of 1024 tokens: per-lane
+  // keep masks, per (round, wavefront) counts, one exclusive scan per group
+  // (as sample_select_kernel writes its one group), then the positions.
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint64_t below_lane = (1ull << lane) - 1ull;
   int base = 0;
-  uint32_t next = tid < n ? codes[tid] : 0u;
-  for (int r = 0; r < slots; ++r) {
-    const int j = r * kSelThreads + tid;
-    const uint32_t c = next;
-    next = j + kSelThreads < n ? codes[j + kSelThreads] : 0u;
-    const bool keep = j < n && (c > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u));
-    int tot;
-    const int pos = block_rank(keep, core.cnt, &tot);
-    if (keep && base + pos < u.budget) u.keep[base + pos] = j;
-    base += tot;
+  for (int r0 = 0; r0 < slots; r0 += kFusedPer) {
+    uint32_t kmask = 0;
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const int j = (r0 + r) * kSelThreads + tid;
+      if (j < n && (codes[j] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u))) kmask |= 1u << r;
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const uint64_t bal = __ballot((kmask >> r) & 1u);
+      if (lane == 0) sh.round_cnt[r * kSelWaves + wave] = __popcll(bal);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int kPerLane = kFusedPer * kSelWaves / 64;
+      int loc[kPerLane], sum = 0;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += sh.round_cnt[lane * kPerLane + q]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      const int excl = incl - sum;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) sh.round_cnt[lane * kPerLane + q] = excl + loc[q];
+      if (lane == 63) sh.group_total = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const uint64_t bal = __ballot((kmask >> r) & 1u);
+      if ((kmask >> r) & 1u) {
+        const int pos = base + sh.round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
+        if (pos < u.budget) u.keep[pos] = (r0 + r) * kSelThreads + tid;
+      }
+    }
+    base += sh.group_total;
+    __syncthreads();   // round_cnt and group_total are rewritten by the next group
   }
 }
 
