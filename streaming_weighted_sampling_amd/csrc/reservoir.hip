@@ -222,6 +222,61 @@ __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
   return off + below;
 }
 
+// Kept indices in ascending order: keep_at(j) decides token j; tokens are
+// taken in groups of kFusedPer rounds of kSelThreads (thread tid holds tokens
+// (r0 + r) * kSelThreads + tid), with per-lane keep masks, per (round,
+// wavefront) counts and one exclusive scan per group.  round_cnt holds
+// kFusedPer * kSelWaves ints; every thread of the block calls this.
+template <typename KeepAt>
+__device__ inline void write_ascending(int n, int budget, int32_t* keep, int* round_cnt,
+                                       int* group_total, KeepAt&& keep_at) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below_lane = (1ull << lane) - 1ull;
+  const int slots = (n + kSelThreads - 1) / kSelThreads;
+  int base = 0;
+  for (int r0 = 0; r0 < slots; r0 += kFusedPer) {
+    uint32_t kmask = 0;
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const int j = (r0 + r) * kSelThreads + tid;
+      if (j < n && keep_at(j)) kmask |= 1u << r;
+    }
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const uint64_t bal = __ballot((kmask >> r) & 1u);
+      if (lane == 0) round_cnt[r * kSelWaves + wave] = __popcll(bal);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int kPerLane = kFusedPer * kSelWaves / 64;
+      int loc[kPerLane], sum = 0;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += round_cnt[lane * kPerLane + q]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      const int excl = incl - sum;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) round_cnt[lane * kPerLane + q] = excl + loc[q];
+      if (lane == 63) *group_total = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kFusedPer; ++r) {
+      const uint64_t bal = __ballot((kmask >> r) & 1u);
+      if ((kmask >> r) & 1u) {
+        const int pos = base + round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
+        if (pos < budget) keep[pos] = (r0 + r) * kSelThreads + tid;
+      }
+    }
+    base += *group_total;
+    __syncthreads();   // round_cnt and group_total are rewritten by the next group
+  }
+}
+
 // Shared state of one radix selection.  After the passes: keys whose bits
 // under `mask` exceed `prefix` are kept; of the `eq` keys equal to it under
 // the mask, `need` are kept (all of them when eq == need, else the ones with
@@ -238,6 +293,8 @@ struct SelCore {
   int need, eq, done, start, cut;
   int cnt[kSelWaves];
   uint64_t red_or[kSelWaves], red_and[kSelWaves];
+  int round_cnt[kFusedPer * kSelWaves];   // write_ascending
+  int group_total;
 };
 
 // Thread 0: the state before the passes, from the OR and AND of all codes
@@ -372,22 +429,10 @@ __device__ inline void select_global(const Args& a, const HeadUnit& u, const uin
     __syncthreads();
   }
   const int cut = sh.cut;
-  int base = 0;
-  uint64_t next = tid < n ? keys[tid] : 0ull;   // this round's key, loaded a round ahead
-  for (int r = 0; r < slots; ++r) {
-    const int j = r * kSelThreads + tid;
-    const uint64_t kj = next;
-    next = j + kSelThreads < n ? keys[j + kSelThreads] : 0ull;
-    bool keep = false;
-    if (j < n) {
-      const uint64_t top = kj & mask;
-      keep = top > prefix || (top == prefix && (!ties || j >= cut));
-    }
-    int tot;
-    const int pos = block_rank(keep, sh.cnt, &tot);
-    if (keep && base + pos < u.budget) u.keep[base + pos] = j;
-    base += tot;
-  }
+  write_ascending(n, u.budget, u.keep, sh.round_cnt, &sh.group_total, [&](int j) {
+    const uint64_t top = keys[j] & mask;
+    return top > prefix || (top == prefix && (!ties || j >= cut));
+  });
 }
 
 __global__ __launch_bounds__(kSelThreads) void topb_select_kernel(const Args a) {
@@ -834,8 +879,6 @@ struct WideShared {
   uint32_t band_idx[kBandCap];
   uint64_t band_code[kBandCap];
   uint32_t chosen[kWideMaxTokens / 32];
-  int round_cnt[kFusedPer * kSelWaves];
-  int group_total;
 };
 
 __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const Args a) {
@@ -976,53 +1019,10 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
     if (rank < need2) atomicOr(&sh.chosen[it >> 5], 1u << (it & 31));
   }
   __syncthreads();
-  // Ascending write in groups of kFusedPer rounds of 1024 tokens: per-lane
-  // keep masks, per (round, wavefront) counts, one exclusive scan per group
-  // (as sample_select_kernel writes its one group), then the positions.
-  const int lane = tid & 63, wave = tid >> 6;
-  const uint64_t below_lane = (1ull << lane) - 1ull;
-  int base = 0;
-  for (int r0 = 0; r0 < slots; r0 += kFusedPer) {
-    uint32_t kmask = 0;
-#pragma unroll
-    for (int r = 0; r < kFusedPer; ++r) {
-      const int j = (r0 + r) * kSelThreads + tid;
-      if (j < n && (codes[j] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u))) kmask |= 1u << r;
-    }
-#pragma unroll
-    for (int r = 0; r < kFusedPer; ++r) {
-      const uint64_t bal = __ballot((kmask >> r) & 1u);
-      if (lane == 0) sh.round_cnt[r * kSelWaves + wave] = __popcll(bal);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      constexpr int kPerLane = kFusedPer * kSelWaves / 64;
-      int loc[kPerLane], sum = 0;
-#pragma unroll
-      for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += sh.round_cnt[lane * kPerLane + q]; }
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-      }
-      const int excl = incl - sum;
-#pragma unroll
-      for (int q = 0; q < kPerLane; ++q) sh.round_cnt[lane * kPerLane + q] = excl + loc[q];
-      if (lane == 63) sh.group_total = incl;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kFusedPer; ++r) {
-      const uint64_t bal = __ballot((kmask >> r) & 1u);
-      if ((kmask >> r) & 1u) {
-        const int pos = base + sh.round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
-        if (pos < u.budget) u.keep[pos] = (r0 + r) * kSelThreads + tid;
-      }
-    }
-    base += sh.group_total;
-    __syncthreads();   // round_cnt and group_total are rewritten by the next group
-  }
+  // Ascending write (groups of kFusedPer rounds, one scan per group).
+  write_ascending(n, u.budget, u.keep, core.round_cnt, &core.group_total, [&](int j) {
+    return codes[j] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u);
+  });
 }
 
 }  // namespace
