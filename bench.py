@@ -341,8 +341,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the eviction path has no multi-GPU mode "
-              "(head units are independent; see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+              "(head units are independent, so units would be split across GPUs with no "
+              "exchange between them).", file=sys.stderr)
         sys.exit(2)
 
     dev = "cuda"

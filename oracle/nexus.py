@@ -5,7 +5,7 @@ Streaming KV-Cache Eviction Under Fixed Budgets" (academ.us article page) and
 says which passage.  No blocking, fusion or reordering beyond the definitions:
 one BLAS matmul for the logits, then elementwise numpy.
 
-Readings of passages the pages leave open (each also listed in the design doc):
+Readings of passages the pages leave open:
   granularity  tokens by default, i.e. block size b = 1, so BlockSum_b and
                rownorm of section 2.1 Eq. (1) are identities on softmax rows;
                block = b > 1 scores, samples and keeps blocks of b tokens
