@@ -531,25 +531,66 @@ __device__ inline float f32_decode(uint32_t c) {
 // Then s = (eE - ew) + log2(mE / mw) from the exact binary exponents and
 // mantissas of E and w (subnormal w included).  |error of s| < 5e-5, twenty
 // times inside kBand.
-__device__ inline uint32_t estimate_code(uint32_t x0, uint32_t x1, float w, bool forced) {
-  if (forced) return 0xFFFFFFFFu;
-  if (!(w > 0.f)) return 0u;
+// E = -ln u of the uniform from words (x0, x1), as above; exactly 0 for u = 1.
+__device__ inline float neg_log_u(uint32_t x0, uint32_t x1) {
   const uint64_t m = (((uint64_t(x0) << 32) | uint64_t(x1)) >> 11) + 1;
   const uint64_t d = (1ull << 53) - m;
-  if (d == 0) return f32_code(INFINITY);   // u = 1: key 0, the largest finite key
-  float e;
+  if (d == 0) return 0.f;
   if (d < (1ull << 46)) {
     const float x = float(uint32_t(d)) * 0x1p-53f + float(uint32_t(d >> 32)) * 0x1p-21f;
-    e = x * (1.f + x * (0.5f + x * (0.333333343f + x * 0.25f)));
-  } else {
-    const float uf = (float(uint32_t(m >> 21)) * 0x1p21f + float(uint32_t(m) & 0x1FFFFFu)) * 0x1p-53f;
-    e = -__builtin_amdgcn_logf(uf) * kLn2f;
+    return x * (1.f + x * (0.5f + x * (0.333333343f + x * 0.25f)));
   }
+  const float uf = (float(uint32_t(m >> 21)) * 0x1p21f + float(uint32_t(m) & 0x1FFFFFu)) * 0x1p-53f;
+  return -__builtin_amdgcn_logf(uf) * kLn2f;
+}
+
+// Code of -s, s = log2(X) - log2(w) for a key -X/w (X > 0; X = 0, key 0, is
+// the largest finite key).
+__device__ inline uint32_t order_code(float x, float w) {
+  if (!(x > 0.f)) return f32_code(INFINITY);
   int ee, ew;
-  const float me = __builtin_frexpf(e, &ee);
+  const float me = __builtin_frexpf(x, &ee);
   const float mw = __builtin_frexpf(w, &ew);
   const float sv = float(ee - ew) + __builtin_amdgcn_logf(me * __builtin_amdgcn_rcpf(mw));
   return min(max(f32_code(-sv), 1u), 0xFFFFFFFEu);
+}
+
+__device__ inline uint32_t estimate_code(uint32_t x0, uint32_t x1, float w, bool forced) {
+  if (forced) return 0xFFFFFFFFu;
+  if (!(w > 0.f)) return 0u;
+  return order_code(neg_log_u(x0, x1), w);
+}
+
+// n >= 2 draws (section 2.3 Eq. 6): with E_i = -ln u_i (draws 2c, 2c + 1 from
+// Philox block c, key word 1 bumped by c, as token_key takes them) the key is
+// ln pi = -E_min / w + L, L = ln(sum_i exp(-(E_i - E_min) / w)) - ln n in
+// [-ln n, 0], so -key = (E_min + |L| w) / w with no cancellation: the fp32
+// estimate of log2(E_min + |L| w) - log2(w) carries the error of E_min
+// (above) plus a few ulp of the sum and log, well inside kBand.
+__device__ inline uint32_t estimate_code_avg(const Args& a, const HeadUnit& u, int j, float w,
+                                             bool forced, uint32_t k0, uint32_t k1) {
+  if (forced) return 0xFFFFFFFFu;
+  if (!(w > 0.f)) return 0u;
+  const float c2 = 1.4426950408889634f / w;   // log2(e) / w
+  float emin = INFINITY, sum = 0.f;
+  for (int c = 0; 2 * c < a.n_avg; ++c) {
+    const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0,
+                                  k1 + uint32_t(c));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (2 * c + h < a.n_avg) {
+        const float e = h == 0 ? neg_log_u(x.x, x.y) : neg_log_u(x.z, x.w);
+        if (e < emin) {
+          sum = emin == INFINITY ? 1.f : sum * __builtin_amdgcn_exp2f((e - emin) * c2) + 1.f;
+          emin = e;
+        } else {
+          sum += __builtin_amdgcn_exp2f((emin - e) * c2);
+        }
+      }
+    }
+  }
+  const float abs_l = __builtin_amdgcn_logf(float(a.n_avg) * __builtin_amdgcn_rcpf(sum)) * kLn2f;
+  return order_code(emin + fmaxf(abs_l, 0.f) * w, w);
 }
 
 // Exact fp64 key of token j (reservoir_keys' definition).
@@ -615,8 +656,13 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
       nonfinite |= !isfinite(w[i]);
       if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
       if (estimate) {
-        const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
-        codes[j] = estimate_code(x.x, x.y, w[i], j < a.n_sink || j >= n - a.n_recent);
+        const bool forced = j < a.n_sink || j >= n - a.n_recent;
+        if (a.n_avg <= 1) {
+          const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
+          codes[j] = estimate_code(x.x, x.y, w[i], forced);
+        } else {
+          codes[j] = estimate_code_avg(a, u, j, w[i], forced, k0, k1);
+        }
       }
     }
   }

@@ -172,6 +172,30 @@ def test_reservoir_inclusion_frequencies_match_enumeration():
     assert np.all(np.abs(freq - pi) < 5 * sigma), (freq, pi)
 
 
+@pytest.mark.parametrize("kind", ["cubic", "zeros_negative", "wide_range", "equal"])
+@pytest.mark.parametrize("n_avg", [2, 5, 64])
+@pytest.mark.parametrize("n,budget,sink,recent", [(32768, 6554, 0, 0), (131072, 13107, 5, 7), (9000, 3000, 7, 9)])
+def test_estimate_select_equals_exact_select_averaged(kind, n_avg, n, budget, sink, recent):
+    """n >= 2 draws per token (Eq. 6): the select ranks tokens by an fp32
+    estimate of ln(pi) and computes exact fp64 keys only near the boundary;
+    with the key export every key is exact.  Both keep the same tokens."""
+    h_kv = 4
+    cfg = _cfg(8, h_kv, 128, 8, n_sink=sink, n_recent=recent, n_avg=n_avg)
+    ws = _ws(cfg, n, walk=0)
+    gen = torch.Generator(device="cpu").manual_seed(zlib.crc32(f"{kind}/{n}/{n_avg}".encode()))
+    w = _weights(kind, h_kv, n, gen)
+    wd = w.to(DEV)
+    for step in range(2):
+        fast, _ = nx.nx_reservoir_select(cfg, wd, budget, 31, workspace=ws, layer=1, step=step)
+        exact, keys = nx.nx_reservoir_select(cfg, wd, budget, 31, workspace=ws, layer=1, step=step,
+                                             with_keys=True)
+        nx.nx_read_device_status(cfg, ws)
+        assert torch.equal(fast, exact), (kind, n_avg, step)
+        k = keys.cpu().numpy()
+        for h in range(h_kv):
+            np.testing.assert_array_equal(exact[h].cpu().numpy(), nexus.select_top(k[h], budget))
+
+
 @pytest.mark.parametrize("n", [32768, 20001])
 def test_fused_and_two_kernel_selection_agree(n):
     """The selection runs on estimate codes held in registers when max_tokens
