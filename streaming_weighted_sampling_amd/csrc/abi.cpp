@@ -177,11 +177,11 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 // Items of up to kWideMaxTokens units select on estimate codes (estimate_keys
 // + sample_select; held in the select kernel's registers up to
 // kFusedMaxTokens) when the call goes on to selection (not the weights-only
-// export) with n >= 1 draws per token (not the top-B-by-weight limit).
+// export): n >= 1 draws per token, or the top-B-by-weight limit.
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   hipError_t err = hipSuccess;
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
-  const bool fused = max_units <= kWideMaxTokens && !a.stop_after_weights && a.n_avg != NX_TOPK &&
+  const bool fused = max_units <= kWideMaxTokens && !a.stop_after_weights &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
   // The stages from the keys on read the per-head budgets of this call.
   Args live = a;

@@ -657,7 +657,13 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
       if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
       if (estimate) {
         const bool forced = j < a.n_sink || j >= n - a.n_recent;
-        if (a.n_avg <= 1) {
+        if (a.n_avg == NX_TOPK) {
+          // The key is w itself (appendix 8.2 limit): code of log2(w), same
+          // order, within an ulp of the log, and exact keys (w) in the band.
+          codes[j] = forced ? 0xFFFFFFFFu
+                     : !(w[i] > 0.f) ? 0u
+                     : min(max(f32_code(__builtin_amdgcn_logf(w[i])), 1u), 0xFFFFFFFEu);
+        } else if (a.n_avg <= 1) {
           const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
           codes[j] = estimate_code(x.x, x.y, w[i], forced);
         } else {

@@ -173,12 +173,13 @@ def test_reservoir_inclusion_frequencies_match_enumeration():
 
 
 @pytest.mark.parametrize("kind", ["cubic", "zeros_negative", "wide_range", "equal"])
-@pytest.mark.parametrize("n_avg", [2, 5, 64])
+@pytest.mark.parametrize("n_avg", [2, 5, 64, nx.TOPK])
 @pytest.mark.parametrize("n,budget,sink,recent", [(32768, 6554, 0, 0), (131072, 13107, 5, 7), (9000, 3000, 7, 9)])
 def test_estimate_select_equals_exact_select_averaged(kind, n_avg, n, budget, sink, recent):
-    """n >= 2 draws per token (Eq. 6): the select ranks tokens by an fp32
-    estimate of ln(pi) and computes exact fp64 keys only near the boundary;
-    with the key export every key is exact.  Both keep the same tokens."""
+    """n >= 2 draws per token (Eq. 6), or the top-B-by-weight limit: the
+    select ranks tokens by an fp32 estimate of the key and computes exact keys
+    only near the boundary; with the key export every key is exact.  Both
+    keep the same tokens."""
     h_kv = 4
     cfg = _cfg(8, h_kv, 128, 8, n_sink=sink, n_recent=recent, n_avg=n_avg)
     ws = _ws(cfg, n, walk=0)
