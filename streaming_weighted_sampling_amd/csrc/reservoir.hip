@@ -16,11 +16,17 @@
 //     order-preserving uint64 code, plus the chunk's OR and AND of the codes
 // topb_select  (one 1024-thread workgroup per head unit)
 //   * skips the common prefix of all codes, then MSD radix select with
-//     8-bit digits: LDS histogram of the candidates, boundary bin by a
-//     wavefront suffix scan, until the boundary bin holds exactly the missing
-//     count or all 64 bits are fixed (true ties: larger index wins)
-//   * writes the kept indices in ascending order with ballot / popcount
-//     prefix sums, 1024 tokens per round.
+//     8-bit digits: LDS histogram of the candidates (each bin in 8 words, one
+//     per lane residue), boundary bin by a wavefront suffix scan, until the
+//     boundary bin holds exactly the missing count or all 64 bits are fixed
+//     (true ties: larger index wins)
+//   * writes the kept indices in ascending order with per-lane keep masks,
+//     ballots and one scan per 32 rounds of 1024 tokens.
+// estimate_keys + sample_select (the default path, head units of up to
+// 262144 units): an fp32 order code of every key (n = 1, n >= 2 averaged
+// draws, or the top-B limit), the same radix select on the codes (held in
+// registers up to 32768 units, re-read from memory above), and exact fp64
+// keys only for the tokens within +-2^-9 of the boundary estimate.
 #include <type_traits>
 
 #include "nx_device.hpp"

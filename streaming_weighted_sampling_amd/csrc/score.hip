@@ -28,7 +28,11 @@
 // l % 32; its half l / 32 supplies the contraction slots of head dims
 // [half*D/2, half*D/2 + D/2), the same dims for A and B, so every lane reads
 // one contiguous half-row of 16-B chunks.  Output register v of lane l is
-// C[8*(v/4) + 4*(l/32) + v%4][l % 32].
+// C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Each wavefront owns one 32-row tile:
+// workgroups of 4 wavefronts up to 128 rows, of 16 above (up to 512 rows).
+//
+// score_fused (on request) replaces the three kernels with one read of K:
+// see the section before the kernels below.
 #include <atomic>
 
 #include "nx_device.hpp"
