@@ -9,8 +9,8 @@
 // moves kCompactRows rows of K and of V; every lane moves 16-B chunks, so a
 // 256-B row is one fully used 256-B segment read and written by 16 lanes.
 // Loads and stores go through buffer resources sized to the head's rows.
-// Output stores are non-temporal: the compacted cache is consumed by later
-// decode steps, not by this event.
+// Loads and stores are non-temporal: every source row is read once, and the
+// compacted cache is consumed by later decode steps, not by this event.
 #include "nx_device.hpp"
 
 namespace nx {
@@ -67,8 +67,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       if (src[i] >= 0) {
-        xk[i] = app[i] ? kab.ld16(uint32_t(src[i])) : kb.ld16(uint32_t(src[i]));
-        xv[i] = app[i] ? vab.ld16(uint32_t(src[i])) : vb.ld16(uint32_t(src[i]));
+        xk[i] = app[i] ? kab.ld16<kNonTemporal>(uint32_t(src[i])) : kb.ld16<kNonTemporal>(uint32_t(src[i]));
+        xv[i] = app[i] ? vab.ld16<kNonTemporal>(uint32_t(src[i])) : vb.ld16<kNonTemporal>(uint32_t(src[i]));
       }
     }
 #pragma unroll
@@ -133,8 +133,8 @@ __device__ __forceinline__ bool fill_holes(const HeadUnit& u, Keep keep) {
       }
       const int hole = j + l;
       if (src < kept || src >= u.n || hole >= kept) { bad = true; continue; }
-      const uint4 xk = kb.ld16(uint32_t(src * kRowBytes + 16 * col));
-      const uint4 xv = vb.ld16(uint32_t(src * kRowBytes + 16 * col));
+      const uint4 xk = kb.ld16<kNonTemporal>(uint32_t(src * kRowBytes + 16 * col));
+      const uint4 xv = vb.ld16<kNonTemporal>(uint32_t(src * kRowBytes + 16 * col));
       kb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xk);
       vb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xv);
     }
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
   for (int r0 = blockIdx.x * kCompactRows; r0 < u.n_append; r0 += gridDim.x * kCompactRows) {
     for (int r = threadIdx.x / kPerRow; r < kCompactRows && r0 + r < u.n_append; r += kRowsPerPass) {
       const uint32_t off = uint32_t((r0 + r) * kRowBytes + 16 * col);
-      const uint4 xk = kab.ld16(off);
-      const uint4 xv = vab.ld16(off);
+      const uint4 xk = kab.ld16<kNonTemporal>(off);
+      const uint4 xv = vab.ld16<kNonTemporal>(off);
       kb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xk);
       vb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xv);
     }

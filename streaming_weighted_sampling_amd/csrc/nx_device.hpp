@@ -22,8 +22,9 @@ struct Buf {
   __amdgpu_buffer_rsrc_t r;
   __device__ Buf(const void* base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kRsrcWord3)) {}
+  template <int kAux = 0>
   __device__ uint4 ld16(uint32_t off) const {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
     return make_uint4(v.x, v.y, v.z, v.w);
   }
   __device__ float ldf(uint32_t off) const {
