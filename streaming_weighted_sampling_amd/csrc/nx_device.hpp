@@ -45,7 +45,8 @@ struct Buf {
 // M0 + 16 * l, so one instruction fills 1 KB of LDS.  Issued through inline
 // assembly so that the compiler does not order every later LDS read behind
 // all such copies; the caller waits with vm_wait<>() and a barrier.  Offsets
-// at or past `bytes` read as zero.
+// at or past `bytes` read as zero.  The copies carry the non-temporal hint:
+// every user streams K through them, each byte once per sweep.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 struct LdsDma {
@@ -60,7 +61,7 @@ struct LdsDma {
   __device__ void load16(uint32_t lds_addr, uint32_t voff) const {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
                  : "memory", "m0");
 #pragma clang diagnostic pop
