@@ -123,6 +123,10 @@ Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
   Args a;
   std::memset(&a, 0, sizeof(a));
   a.g = g;
+  // K streams of more than twice the 256 MB Infinity Cache bypass the caches
+  // (faster sweeps); smaller ones stay cached, where the compaction that
+  // follows finds part of the kept rows.
+  a.k_stream_nt = int64_t(g.n_hu) * g.max_tokens * g.head_dim * elem_size(g.dtype) > (int64_t(512) << 20);
   a.lambda = d->lambda;
   a.eps_tie = d->eps_tie;
   a.c_log2 = float(1.4426950408889634 / std::sqrt(double(d->head_dim)));

@@ -45,13 +45,14 @@ struct Buf {
 // M0 + 16 * l, so one instruction fills 1 KB of LDS.  Issued through inline
 // assembly so that the compiler does not order every later LDS read behind
 // all such copies; the caller waits with vm_wait<>() and a barrier.  Offsets
-// at or past `bytes` read as zero.  The copies carry the non-temporal hint:
-// every user streams K through them, each byte once per sweep.
+// at or past `bytes` read as zero.  With `nt` (wave-uniform) the copies carry
+// the non-temporal hint, for K streams far larger than the caches.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 struct LdsDma {
   i32x4_t r;
-  __device__ LdsDma(const void* base, uint32_t bytes) {
+  bool nt;
+  __device__ LdsDma(const void* base, uint32_t bytes, bool nt_ = false) : nt(nt_) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     r = i32x4_t{__builtin_amdgcn_readfirstlane(int(uint32_t(b))),
                 __builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32) & 0xFFFF)),
@@ -61,9 +62,14 @@ struct LdsDma {
   __device__ void load16(uint32_t lds_addr, uint32_t voff) const {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
-                 : "memory", "m0");
+    if (nt)
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
+                   : "memory", "m0");
 #pragma clang diagnostic pop
   }
 };

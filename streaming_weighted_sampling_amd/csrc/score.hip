@@ -166,14 +166,14 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
 // be refilled), refill, body(st, lds).  Rows past the cache end read as zero.
 // Ends on a barrier.
 template <typename T, int D, int kSlots, int kLoaders, int NW, typename Body>
-__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role,
+__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role, bool nt,
                                    Body&& body) {
   using GE = Geo<T, D>;
   constexpr int kPerWave = GE::kTileBytes / (1024 * kLoaders);   // copies per loader per tile
   static_assert(kPerWave >= 1 && kPerWave * 1024 * kLoaders == GE::kTileBytes, "tile split");
   static_assert((kSlots - 2) * kPerWave < 64, "vmcnt range");
   const int t1 = min(t0 + 32 * n_sub, u.n);
-  const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
+  const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes), nt);
   const int lw = role - (NW - kLoaders);   // loader index, < 0: not a loader
   const bool loader = lw >= 0;
   const int lane = threadIdx.x & 63;
@@ -229,7 +229,8 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
   const float c = a.c_log2;
   // Every wavefront copies K, at least one 1-KB copy each per sub-tile.
   constexpr int kLoaders = NW < GE::kTileBytes / 1024 ? NW : GE::kTileBytes / 1024;
-  sweep_tiles<T, D, GE::kSlotsStats, kLoaders, NW>(u, t0, n_sub, ring, wave, [&](int st, const char* cur) {
+  sweep_tiles<T, D, GE::kSlotsStats, kLoaders, NW>(u, t0, n_sub, ring, wave, a.k_stream_nt != 0,
+                                                   [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
     const bool full = t0 + 32 * st + 32 <= u.n;      // wave-uniform
@@ -585,7 +586,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     }
   };
 
-  sweep_tiles<T, D, GE::kSlotsProbs, 2, NW>(u, t0, n_sub, smem, role, [&](int st, const char* cur) {
+  sweep_tiles<T, D, GE::kSlotsProbs, 2, NW>(u, t0, n_sub, smem, role, a.k_stream_nt != 0,
+                                           [&](int st, const char* cur) {
     // Lagged work on slots the previous barrier made visible: the LDS reads
     // now, ahead of the K fragment reads; the sums after the MFMA issue.
     // (The LDS walk mode keeps its lagged work in one piece, ahead of the
@@ -860,7 +862,8 @@ void score_fused_kernel(const Args a) {
   const uint32_t ring_lds = lds_address(sm.ring) + uint32_t(lw * 1024);
   auto issue = [&](const FuseItem& it, int st) {
     const int t1 = min(it.t0 + kFuseTok, it.n);
-    const LdsDma dma(it.k + int64_t(it.t0) * GE::kRowBytes, uint32_t((t1 - it.t0) * GE::kRowBytes));
+    const LdsDma dma(it.k + int64_t(it.t0) * GE::kRowBytes, uint32_t((t1 - it.t0) * GE::kRowBytes),
+                     a.k_stream_nt != 0);
     const uint32_t dst = ring_lds + uint32_t((st % kFuseSlots) * GE::kTileBytes);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
