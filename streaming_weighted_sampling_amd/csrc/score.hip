@@ -1132,8 +1132,18 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 }
 
 // Pass 2: one workgroup per (tile, head unit).
+// bf16 without blocks and with a register-lean walk form is held to 128 VGPRs
+// (4 wavefronts per SIMD), which it reaches without spilling; fp32, blocks and
+// the LDS and deep walk forms need more and run at 2-3.
+template <typename T, int kWalk, bool kBlocks>
+constexpr int probs_min_waves() {
+  return sizeof(T) == 2 && !kBlocks && kWalk != kWalkLds && kWalk != kWalkFast4Deep ? 4 : 1;
+}
+
 template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
-__global__ __launch_bounds__(64 * NW) void score_probs_kernel(const Args a) {
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(probs_min_waves<T, kWalk, kBlocks>())))
+void score_probs_kernel(const Args a) {
   __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk, NW>()];
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
