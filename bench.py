@@ -328,9 +328,6 @@ def main():
                     help="selection unit of Eq. 1: 1 = tokens, else blocks of that many tokens")
     ap.add_argument("--n-avg", type=int, default=1,
                     help="priority averaging count of Eq. 6 (1: A-Res key; -1: top-B by weight)")
-    ap.add_argument("--score", choices=["two-sweeps", "one-read"], default="two-sweeps",
-                    help="score pass: two sweeps over K (default), or K read once with "
-                         "in-kernel per-unit barriers")
     ap.add_argument("--workload", choices=["llama3_8b_stream32", "ragged16_zipf", "llama70b_share"],
                     default="llama3_8b_stream32",
                     help="the headline 32-layer event (default), the ragged 16-sequence batch, or "
@@ -373,8 +370,7 @@ def main():
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
                          n_avg=args.n_avg, block=args.block,
                          head_alloc=nx.NX_HEADS_ALLOC if heads else nx.NX_HEADS_UNIFORM,
-                         head_floor=data["budget"] // 5 if heads else 0,
-                         score_mode=nx.SCORE_ONE_READ if args.score == "one-read" else nx.SCORE_TWO_SWEEPS)
+                         head_floor=data["budget"] // 5 if heads else 0)
     ws = nx.new_workspace(cfg, wl.n_tokens, wl.n_layers, wl.walk_iters, device=dev)
     stream = torch.cuda.current_stream()
 

@@ -130,22 +130,12 @@ typedef struct nx_desc {
                                nx_kv_compact need 0. */
   int32_t head_floor;       /* NX_HEADS_ALLOC: per-head floor f >= 0 (units); an allocation
                                below n_sink + n_recent marks the item bad */
-  int32_t score_mode;       /* how K is read for Eq. 1's softmax normaliser:
-                               NX_SCORE_TWO_SWEEPS (0): a statistics sweep, then a
-                               probabilities sweep (the faster path on MI355X);
-                               NX_SCORE_ONE_READ (1): K read once; the logits of each
-                               256-token tile stay in registers while the tiles of a head
-                               unit meet at two device-scope barriers inside one cooperative
-                               launch.  Needs bf16, head_dim 128, G * W <= 128, block <= 1,
-                               and walk_iters 0, or G = 4 and walk_iters <= 8, or G = 8 and
-                               walk_iters <= 4; else NX_EUNSUPPORTED.  Same weights up to
-                               fp32 rounding order.  A barrier that gives up is reported as
-                               NX_EHIP by nx_read_device_status().
-                               Other values: NX_EINVAL */
+  float* out_w;             /* nx_evict_step only, nullable: [n_kv_heads][units] fp32 (units =
+                               ceil(n_tokens / block), row stride units), written with the Nexus
+                               weights w of section 2.2 Eq. 5 exactly as the selection of this call
+                               used them, so that a caller can re-run the reservoir of section 2.3
+                               on them; must not overlap any other buffer of the call */
 } nx_desc;
-
-#define NX_SCORE_TWO_SWEEPS 0
-#define NX_SCORE_ONE_READ 1
 
 #define NX_COMPACT_COPY 0
 #define NX_COMPACT_INPLACE 1
@@ -188,6 +178,8 @@ typedef struct nx_unit {
   int32_t head_cap;         /* per-head capacity with desc->head_alloc != 0 (0: budget) */
   int32_t* head_budget;     /* [n_kv_heads] int32 device array with desc->head_alloc != 0:
                                read (NX_HEADS_GIVEN) or written (NX_HEADS_ALLOC); else ignored */
+  float* out_w;             /* nullable: [n_kv_heads][units] fp32 (units = ceil(n_tokens / block)),
+                               the Nexus weights w (section 2.2 Eq. 5) the item's selection used */
 } nx_unit;
 
 /*
@@ -274,13 +266,27 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
 
 /*
  * Waits for desc->stream, reads and clears the workspace status word.
- * Returns NX_OK, NX_ENONFINITE, NX_EINVAL (a bad batch item) or NX_EHIP (a HIP
- * call failed, or a single-read scoring barrier timed out).
+ * Returns NX_OK, NX_ENONFINITE or NX_EINVAL (a bad batch item), or NX_EHIP if
+ * a HIP call failed.
  */
 nx_status nx_read_device_status(const nx_desc* desc);
 
 /* Human-readable name of a status code.  Pure host function. */
 const char* nx_status_str(nx_status status);
+
+/*
+ * Read-bandwidth probe (a measurement aid, not part of an eviction event): reads
+ * `bytes` bytes at `src` (device memory, 16-B aligned, bytes a multiple of 256)
+ * `passes` times, one kernel launch per pass, on `stream` (a hipStream_t), with
+ * the score sweeps' access pattern: 256-B rows, 512 KB per workgroup.
+ *   mode 0: global -> LDS copies through the sweeps' ring of LDS slots
+ *   mode 1: plain 16-byte vector loads into registers
+ * sink: >= 1 KB of device memory that the kernels may write (it keeps the loads
+ * live; nothing is written unless the XOR of all data hits a fixed value).
+ * Errors: NX_EINVAL, NX_EUNSUPPORTED (more than 2^22 * 65535 rows), NX_EHIP.
+ */
+nx_status nx_stream_read(const void* src, size_t bytes, int32_t mode, int32_t passes, void* sink,
+                         void* stream);
 
 /*
  * Per-stage timing with HIP events recorded on desc->stream around the

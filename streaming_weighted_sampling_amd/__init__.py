@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     load, status_str,
 )
 from .api import (  # noqa: F401
-    NexusConfig, TOPK, SCORE_TWO_SWEEPS, SCORE_ONE_READ, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,
+    NexusConfig, TOPK, workspace_bytes, new_workspace, nx_evict_step, nx_nexus_weights,
     nx_reservoir_select, nx_kv_compact, nx_head_budgets, make_units, nx_evict_batch,
     nx_read_device_status,
     profile_enable, profile_read,

@@ -13,8 +13,6 @@ NX_EWORKSPACE = -3
 NX_EUNSUPPORTED = -4
 NX_ENONFINITE = -5
 NX_EHIP = -6
-NX_SCORE_TWO_SWEEPS = 0
-NX_SCORE_ONE_READ = 1
 NX_COMPACT_COPY = 0
 NX_COMPACT_INPLACE = 1
 NX_HEADS_UNIFORM = 0
@@ -50,7 +48,7 @@ class NxDesc(ctypes.Structure):
         ("compact", ctypes.c_int32),
         ("head_alloc", ctypes.c_int32),
         ("head_floor", ctypes.c_int32),
-        ("score_mode", ctypes.c_int32),
+        ("out_w", ctypes.c_void_p),
     ]
 
 
@@ -73,6 +71,7 @@ class NxUnit(ctypes.Structure):
         ("seq_id", ctypes.c_uint32),
         ("head_cap", ctypes.c_int32),
         ("head_budget", ctypes.c_void_p),
+        ("out_w", ctypes.c_void_p),
     ]
 
 
@@ -90,6 +89,7 @@ SIGNATURES = {
     "nx_kv_compact": (_I32, [_P(NxDesc), _VP, _VP, _VP, _I32, _I32, _VP, _VP]),
     "nx_head_budgets": (_I32, [_P(NxDesc), _VP, _I32, _I32, _I32, _VP]),
     "nx_read_device_status": (_I32, [_P(NxDesc)]),
+    "nx_stream_read": (_I32, [_VP, ctypes.c_size_t, _I32, _I32, _VP, _VP]),
     "nx_status_str": (ctypes.c_char_p, [_I32]),
     "nx_profile_enable": (_I32, [_I32]),
     "nx_profile_read": (_I32, [_P(ctypes.c_float), _P(_I32), _I32]),

@@ -17,8 +17,6 @@ _DTYPES = {torch.bfloat16: NX_BF16, torch.float32: NX_F32}
 
 
 TOPK = -1                     # n_avg value of the deterministic top-B-by-weight limit
-SCORE_TWO_SWEEPS = 0          # score_mode: statistics sweep, then probabilities sweep
-SCORE_ONE_READ = 1            # score_mode: K read once (NX_EUNSUPPORTED where it cannot)
 
 
 @dataclass
@@ -38,7 +36,6 @@ class NexusConfig:
     compact: int = 0          # 0: copy kept rows to new buffers; 1: compact k / v in place
     head_alloc: int = 0       # appendix 10 per-head budgets: 0 uniform, 1 given, 2 allocated
     head_floor: int = 0       # per-head floor of the allocation (head_alloc = 2)
-    score_mode: int = 0       # 0: two sweeps over K, 1: K read once (in-kernel barriers)
 
     def units(self, n_tokens):
         """Selection units of a head: tokens, or ceil(n_tokens / block) blocks."""
@@ -49,7 +46,7 @@ class NexusConfig:
         return min(min(budget, self.units(n_tokens)) * self.block, n_tokens)
 
     def desc(self, workspace=None, *, layer=0, step=0, seq_id=0, kv_head_stride=0,
-             out_head_stride=0, max_out_rows=0, stream=None):
+             out_head_stride=0, max_out_rows=0, stream=None, out_w=None):
         d = NxDesc()
         d.n_q_heads = self.n_q_heads
         d.n_kv_heads = self.n_kv_heads
@@ -65,7 +62,7 @@ class NexusConfig:
         d.compact = self.compact
         d.head_alloc = self.head_alloc
         d.head_floor = self.head_floor
-        d.score_mode = self.score_mode
+        d.out_w = _ptr(out_w)
         d.layer = layer
         d.step = step
         d.seq_id = seq_id
@@ -101,6 +98,12 @@ def _check_cache(cfg, t, name):
     return t.stride(0)
 
 
+def _check_weights(cfg, w, n_tokens, name):
+    if w.dtype != torch.float32 or not w.is_contiguous() or \
+            tuple(w.shape) != (cfg.n_kv_heads, cfg.units(n_tokens)):
+        raise ValueError(f"{name} must be a contiguous float32 [n_kv_heads, units] tensor")
+
+
 def workspace_bytes(cfg, max_tokens, max_units=1, walk_iters=3):
     d = cfg.desc()
     n = load().nx_evict_workspace_bytes(ctypes.byref(d), max_tokens, max_units, walk_iters)
@@ -116,8 +119,11 @@ def new_workspace(cfg, max_tokens, max_units=1, walk_iters=3, device="cuda"):
 
 
 def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace, layer=0,
-                  step=0, seq_id=0, out_k=None, out_v=None, keep=None, stream=None):
-    """One eviction event; returns (keep [H_kv, B] int32, out_k, out_v)."""
+                  step=0, seq_id=0, out_k=None, out_v=None, keep=None, out_w=None, stream=None):
+    """One eviction event; returns (keep [H_kv, B] int32, out_k, out_v).
+
+    out_w: optional float32 [H_kv, units] tensor that receives the Nexus weights
+    the selection used."""
     kst = _check_cache(cfg, k, "k")
     if _check_cache(cfg, v, "v") != kst:
         raise ValueError("k and v must share the head stride")
@@ -141,8 +147,10 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
             raise ValueError("out_k and out_v must share the head stride")
     if keep is None:
         keep = torch.empty(cfg.n_kv_heads, budget, dtype=torch.int32, device=k.device)
+    if out_w is not None:
+        _check_weights(cfg, out_w, n_tokens, "out_w")
     d = cfg.desc(workspace, layer=layer, step=step, seq_id=seq_id, kv_head_stride=kst,
-                 out_head_stride=ost, stream=stream)
+                 out_head_stride=ost, stream=stream, out_w=out_w)
     check(load().nx_evict_step(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), n_tokens, budget,
                                walk_iters, seed, _ptr(keep), _ptr(out_k), _ptr(out_v)),
           "nx_evict_step")
@@ -210,7 +218,7 @@ def make_units(items, device="cuda"):
     """Device array of nx_unit records from a list of dicts (see nx_unit in nexus.h)."""
     arr = (NxUnit * len(items))()
     for rec, it in zip(arr, items):
-        for key in ("q", "k", "v", "keep", "out_k", "out_v", "app_k", "app_v"):
+        for key in ("q", "k", "v", "keep", "out_k", "out_v", "app_k", "app_v", "out_w"):
             setattr(rec, key, _ptr(it.get(key)))
         rec.kv_head_stride = it["kv_head_stride"]
         rec.out_head_stride = it["out_head_stride"]

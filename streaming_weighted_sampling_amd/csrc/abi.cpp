@@ -30,7 +30,6 @@ nx_status check_desc(const nx_desc* d) {
   if (d->n_avg != NX_TOPK && (d->n_avg < 0 || d->n_avg > NX_MAX_AVG)) return NX_EINVAL;
   if (d->block < 0) return NX_EINVAL;
   if (d->compact != NX_COMPACT_COPY && d->compact != NX_COMPACT_INPLACE) return NX_EINVAL;
-  if (d->score_mode != NX_SCORE_TWO_SWEEPS && d->score_mode != NX_SCORE_ONE_READ) return NX_EINVAL;
   if (d->head_alloc < NX_HEADS_UNIFORM || d->head_alloc > NX_HEADS_ALLOC || d->head_floor < 0)
     return NX_EINVAL;
   if (d->compact == NX_COMPACT_INPLACE && d->block > 1) return NX_EUNSUPPORTED;
@@ -89,13 +88,6 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->tok_per_block = tpb;
   g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
-  // One read of K (score_fused) on request, where the shape and the device allow it.
-  if (d->score_mode == NX_SCORE_ONE_READ) {
-    if (!score_fused_fits(*g)) return NX_EUNSUPPORTED;
-    g->fused = 1;
-    g->tok_per_block = kMinTokPerBlock;
-    g->n_tmax = (max_tokens + kMinTokPerBlock - 1) / kMinTokPerBlock;
-  }
   return NX_OK;
 }
 
@@ -104,7 +96,6 @@ nx_status bind_workspace(const nx_desc* d, const Geometry& g, Args* a) {
   if (d->workspace == nullptr || d->workspace_bytes < L.total) return NX_EWORKSPACE;
   char* base = static_cast<char*>(d->workspace);
   a->status = reinterpret_cast<uint32_t*>(base + L.status);
-  a->sync = reinterpret_cast<uint32_t*>(base + L.sync);
   a->part1 = reinterpret_cast<float*>(base + L.part1);
   a->beta = reinterpret_cast<float*>(base + L.beta);
   a->a = reinterpret_cast<float*>(base + L.a);
@@ -192,16 +183,9 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
   live.heads_live = 1;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {
-      case kStageScoreStats:
-        if (a.g.fused) err = run_stage(kStageScoreFused, s, [&] { return launch_score_fused(a, s); });
-        else err = run_stage(st, s, [&] { return launch_score_stats(a, s); });
-        break;
-      case kStageScoreCombine:
-        if (!a.g.fused) err = run_stage(st, s, [&] { return launch_score_combine(a, s); });
-        break;
-      case kStageScoreProbs:
-        if (!a.g.fused) err = run_stage(st, s, [&] { return launch_score_probs(a, s); });
-        break;
+      case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
+      case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
+      case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
       case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
       case kStageReservoirKeys: {
         // Per-head budgets are settled before any stage that reads them.  On
@@ -283,8 +267,9 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   if (!q_window || !k_cache || !v_cache || !out_keep_idx) return NX_EINVAL;
   if (inplace ? (out_k || out_v) : (!out_k || !out_v)) return NX_EINVAL;
   if (budget < 1 || desc->n_sink + desc->n_recent > budget) return NX_EINVAL;
-  const nx_unit u = single_unit(desc, q_window, k_cache, v_cache, out_keep_idx, out_k, out_v,
-                                n_tokens, budget);
+  nx_unit u = single_unit(desc, q_window, k_cache, v_cache, out_keep_idx, out_k, out_v,
+                          n_tokens, budget);
+  u.out_w = desc->out_w;
   const int64_t d = desc->head_dim, hk = desc->n_kv_heads;
   const int32_t blk = desc->block > 1 ? desc->block : 1;
   const int32_t units = (n_tokens + blk - 1) / blk;
@@ -296,6 +281,17 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   const Range rv = span(v_cache, hk, u.kv_head_stride, n_tokens * d, esz);
   const Range rq = span(q_window, 1, 0, int64_t(desc->n_q_heads) * desc->window * d, esz);
   const Range rkeep = span(out_keep_idx, 1, 0, hk * budget, 4);
+  if (desc->out_w != nullptr) {
+    // The weight export must not overlap anything else the call reads or writes.
+    const Range rw = span(desc->out_w, 1, 0, hk * units, 4);
+    for (Range i : {rk, rv, rq, rkeep})
+      if (overlap(rw, i)) return NX_EALIAS;
+    if (!inplace) {
+      if (overlap(rw, span(out_k, hk, u.out_head_stride, kept * d, esz)) ||
+          overlap(rw, span(out_v, hk, u.out_head_stride, kept * d, esz)))
+        return NX_EALIAS;
+    }
+  }
   if (inplace) {
     // k and v are compacted in place: only the keep array must stay apart.
     for (Range i : {rk, rv, rq})
@@ -341,10 +337,10 @@ nx_status nx_nexus_weights(const nx_desc* desc, const void* q_window, const void
                           n_tokens);
   if (u.kv_head_stride < int64_t(n_tokens) * desc->head_dim) return NX_EINVAL;
   if (desc->n_sink + desc->n_recent > n_tokens) return NX_EINVAL;
+  u.out_w = out_w;
   Args a = base_args(desc, g, 0);
   if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
   a.single = u;
-  a.w_out = out_w;
   a.stop_after_weights = 1;
   return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageReservoirKeys);
 }
@@ -443,7 +439,6 @@ nx_status nx_read_device_status(const nx_desc* desc) {
     if (hipMemcpy(desc->workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
       return NX_EHIP;
   }
-  if (word & kStatusSyncTimeout) return NX_EHIP;
   if (word & kStatusNonFinite) return NX_ENONFINITE;
   if (word & kStatusBadItem) return NX_EINVAL;
   return NX_OK;
@@ -460,6 +455,18 @@ const char* nx_status_str(nx_status s) {
     case NX_EHIP: return "NX_EHIP: HIP runtime error";
     default: return "unknown nx_status";
   }
+}
+
+nx_status nx_stream_read(const void* src, size_t bytes, int32_t mode, int32_t passes, void* sink,
+                         void* stream) {
+  if (src == nullptr || sink == nullptr || passes < 1 || (mode != 0 && mode != 1)) return NX_EINVAL;
+  if (bytes == 0 || bytes % 256 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0) return NX_EINVAL;
+  const int64_t rows = int64_t(bytes / 256);
+  if (rows > (int64_t(1) << 22) * 65535) return NX_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t p = 0; p < passes; ++p)
+    if (launch_stream_read(src, rows, mode, static_cast<uint32_t*>(sink), s) != hipSuccess) return NX_EHIP;
+  return NX_OK;
 }
 
 nx_status nx_profile_enable(int32_t stage_mask) {
@@ -496,7 +503,7 @@ const char* nx_stage_name(int32_t stage) {
   static const char* names[kNumStages] = {"score_stats", "score_combine",  "score_probs",
                                           "walk_coef",   "reservoir_keys", "topb_select",
                                           "kv_compact",  "sample_select", "estimate_keys",
-                                          "head_budget", "score_fused"};
+                                          "head_budget"};
   return stage >= 0 && stage < kNumStages ? names[stage] : "unknown";
 }
 

@@ -97,6 +97,7 @@ struct HeadUnit {
   char* out_v;
   const char* app_k;
   const char* app_v;
+  float* w_out;        // nullable: this head's weight export row (nu entries)
   int32_t n, budget, kept, n_append;
   int32_t nu;          // selection units: ceil(n / block); kept = min(budget, nu) of them
   int32_t cap;         // keep row length: budget, or the per-head capacity
@@ -142,6 +143,7 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   r.out_v = u.out_v ? static_cast<char*>(u.out_v) + int64_t(h) * u.out_head_stride * esz : nullptr;
   r.app_k = u.app_k ? static_cast<const char*>(u.app_k) + int64_t(h) * u.n_append * d * esz : nullptr;
   r.app_v = u.app_v ? static_cast<const char*>(u.app_v) + int64_t(h) * u.n_append * d * esz : nullptr;
+  r.w_out = u.out_w ? u.out_w + int64_t(h) * r.nu : nullptr;
   bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && u.budget >= 1 &&
             u.n_append >= 0 && r.budget >= 1 && r.budget <= r.cap &&
             (a.n_sink + a.n_recent <= r.budget || r.budget >= r.nu) &&

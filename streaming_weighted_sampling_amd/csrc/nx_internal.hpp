@@ -7,8 +7,6 @@
 //   score_combine  merge the tile statistics of every window row
 //   score_probs    logits again, probabilities averaged over the GQA group:
 //                  direct score a, the H walk rows, and their Gram partials
-//   (score_fused   on request, the three above with one read of K: per-unit
-//                  barriers inside a cooperative grid)
 //   walk_coef      reduce the Gram partials, run the walk recurrence, store
 //                  the per-row coefficients gamma_t / ||C||_1
 //   estimate_keys + sample_select (head units of up to kWideMaxTokens units,
@@ -55,7 +53,6 @@ enum Stage {
   kStageSampleSelect,   // select on estimate codes (n <= kWideMaxTokens)
   kStageEstimateKeys,   // estimate codes of the keys (n <= kWideMaxTokens)
   kStageHeadBudget,     // per-head budgets (before the keys; NX_HEADS_GIVEN / _ALLOC)
-  kStageScoreFused,     // single-read scoring in place of stats, combine and probs
   kNumStages
 };
 
@@ -73,12 +70,11 @@ struct Geometry {
   int32_t block;         // tokens per selection unit (1, or a block size up to 32)
   int32_t inplace;       // 1: compaction rearranges k / v in place (hole filling)
   int32_t head_alloc;    // NX_HEADS_UNIFORM / _GIVEN / _ALLOC
-  int32_t fused;         // 1: one score_fused launch replaces the two sweeps (tok_per_block 256)
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
-  size_t status, sync, part1, beta, a, p, gram, coef, keys, selp, ahist, acand, acnt, total;
+  size_t status, part1, beta, a, p, gram, coef, keys, selp, ahist, acand, acnt, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -88,7 +84,6 @@ inline WsLayout ws_layout(const Geometry& g) {
   size_t off = 0;
   const size_t hu = size_t(g.n_hu), nm = size_t(g.max_tokens);
   L.status = off; off = align256(off + 256);
-  L.sync = off;   off = align256(off + hu * 2 * sizeof(uint32_t));
   L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
   L.a = off;      off = align256(off + hu * nm * sizeof(float));
@@ -112,7 +107,6 @@ inline WsLayout ws_layout(const Geometry& g) {
 // Device status bits (OR-ed into the workspace status word).
 constexpr uint32_t kStatusNonFinite = 1u;
 constexpr uint32_t kStatusBadItem = 2u;
-constexpr uint32_t kStatusSyncTimeout = 4u;   // a per-unit barrier of score_fused gave up
 
 // Kernel argument block, passed by value to every stage.
 struct Args {
@@ -127,7 +121,6 @@ struct Args {
   uint64_t seed;
   // workspace
   uint32_t* status;
-  uint32_t* sync;  // [n_hu][2]: arrival counters of score_fused's two per-unit barriers
   float* part1;    // [n_hu][n_t1][rows_pad][2]: (max, sum) in log2 units
   float* beta;     // [n_hu][rows_pad]
   float* a;        // [n_hu][max_tokens]: direct score
@@ -141,9 +134,8 @@ struct Args {
   int32_t* acnt;   // [n_hu][2]: codes above the boundary bin, codes in it
   // stage-only extras
   const float* w_in;    // reservoir-only mode: weights [h_kv][n] (row stride n)
-  float* w_out;         // optional weight export [h_kv][n]
   double* keys_out;     // optional key export [h_kv][n]
-  int32_t stop_after_weights;  // 1: reservoir_keys writes w_out and stops
+  int32_t stop_after_weights;  // 1: reservoir_keys writes the weight export and stops
   int32_t head_floor;   // NX_HEADS_ALLOC floor
   int32_t heads_live;   // 1: the items' head_budget arrays hold this call's budgets
   int32_t est_wcodes;   // 1: estimate_keys also writes the allocation's weight codes
@@ -153,8 +145,6 @@ struct Args {
 hipError_t launch_score_stats(const Args& a, hipStream_t s);
 hipError_t launch_score_combine(const Args& a, hipStream_t s);
 hipError_t launch_score_probs(const Args& a, hipStream_t s);
-hipError_t launch_score_fused(const Args& a, hipStream_t s);
-bool score_fused_fits(const Geometry& g);   // shape and device allow score_fused
 hipError_t launch_walk_coef(const Args& a, hipStream_t s);
 hipError_t launch_reservoir_keys(const Args& a, hipStream_t s);
 hipError_t launch_topb_select(const Args& a, hipStream_t s);
@@ -162,5 +152,8 @@ hipError_t launch_sample_select(const Args& a, hipStream_t s);
 hipError_t launch_estimate_keys(const Args& a, hipStream_t s);
 hipError_t launch_kv_compact(const Args& a, hipStream_t s);
 hipError_t launch_head_budget(const Args& a, hipStream_t s);
+// Read-ceiling probe: rows of 256 B at src, mode 0 (LDS ring) or 1 (vector loads).
+hipError_t launch_stream_read(const void* src, int64_t rows, int mode, uint32_t* sink,
+                              hipStream_t s);
 
 }  // namespace nx

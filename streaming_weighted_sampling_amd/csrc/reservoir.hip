@@ -86,6 +86,20 @@ __global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
   }
 }
 
+// w_j = a_j + lambda c~_j + eps r_j (section 2.2 Eqs. 2 and 5) with
+// c~_j = sum_t coef_t P_t[j] and r_j = j ramp, ramp = 1/(N-1).  Every fused
+// multiply-add is written out, so each kernel that forms a token's weight gets
+// the same bits (a weight export equals the weight the keys were drawn on).
+__device__ __attribute__((always_inline)) inline float combine_weight(
+    const Args& a, const float* s_coef, float aj, const float (&pv)[kMaxWalk], int j, float ramp) {
+  float cj = 0.f;
+#pragma unroll
+  for (int t = 0; t < kMaxWalk; ++t)
+    if (t < a.g.walk) cj = fmaf(s_coef[t], pv[t], cj);
+  const float r = float(j) * ramp;
+  return fmaf(a.eps_tie, r, fmaf(a.lambda, cj, aj));
+}
+
 // The fp64 key of token j with weight w (section 2.3 Eq. 6).  n = 1: ln(u)/w
 // (A-Res).  n >= 2: ln(pi), pi = (1/n) sum_i u_i^(1/w), by an online
 // log-sum-exp of t_i = ln(u_i)/w (u^(1/w) underflows for small w); draws 2c
@@ -168,12 +182,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
       float pv[kMaxWalk];
 #pragma unroll
       for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < g.walk ? p_in[size_t(t) * g.max_tokens + jc] : 0.f;
-      const float aj = a_in[jc];
-      float cj = 0.f;
-#pragma unroll
-      for (int t = 0; t < kMaxWalk; ++t)
-        if (t < g.walk) cj = fmaf(s_coef[t], pv[t], cj);
-      w[i] = aj + a.lambda * cj + a.eps_tie * (float(jc) * ramp);
+      w[i] = combine_weight(a, s_coef, a_in[jc], pv, jc, ramp);
     }
   }
 #pragma unroll
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     if (!in[i]) continue;
     const int j = j0 + threadIdx.x + kKeysThreads * i;
     nonfinite |= !isfinite(w[i]);
-    if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
+    if (u.w_out != nullptr) u.w_out[j] = w[i];
     if (a.stop_after_weights) continue;
     const double key = token_key(a, u, j, w[i], k0, k1);
     if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
@@ -497,12 +506,7 @@ __device__ __attribute__((always_inline)) inline float token_weight(
   float pv[kMaxWalk];
 #pragma unroll
   for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < a.g.walk ? p_in[size_t(t) * a.g.max_tokens + j] : 0.f;
-  const float aj = a_in[j];
-  float cj = 0.f;
-#pragma unroll
-  for (int t = 0; t < kMaxWalk; ++t)
-    if (t < a.g.walk) cj = fmaf(s_coef[t], pv[t], cj);
-  return aj + a.lambda * cj + a.eps_tie * (float(j) * ramp);
+  return combine_weight(a, s_coef, a_in[j], pv, j, ramp);
 }
 
 // Weight of token j of this head unit (given weights, or a + lambda c~ + ramp).
@@ -660,7 +664,7 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
     const int j = j0 + threadIdx.x + kKeysThreads * i;
     if (j < n) {
       nonfinite |= !isfinite(w[i]);
-      if (a.w_out != nullptr) a.w_out[ext + j] = w[i];
+      if (u.w_out != nullptr) u.w_out[j] = w[i];
       if (estimate) {
         const bool forced = j < a.n_sink || j >= n - a.n_recent;
         if (a.n_avg == NX_TOPK) {

@@ -30,10 +30,6 @@
 // one contiguous half-row of 16-B chunks.  Output register v of lane l is
 // C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Each wavefront owns one 32-row tile:
 // workgroups of 4 wavefronts up to 128 rows, of 16 above (up to 512 rows).
-//
-// score_fused (on request) replaces the three kernels with one read of K:
-// see the section before the kernels below.
-#include <atomic>
 
 #include "nx_device.hpp"
 
@@ -701,419 +697,6 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   }
 }
 
-// ---------------------------------------------------------------------------
-// Single-read scoring: bf16, D = 128, one 32-row M-tile per wavefront (G*W <=
-// 128 window rows), token granularity.
-//
-// Eq. (1) needs each row's softmax normaliser over all N tokens before any
-// probability exists, which the two sweeps above meet by reading K twice.
-// Here a persistent grid (every workgroup resident, cooperative launch) walks
-// (head unit, 256-token tile) items.  A workgroup reads its tile's K once
-// through the same LDS ring and keeps the R x 256 logits in registers (16 per
-// lane per 32 tokens).  Then, per head unit:
-//   * each tile turns its logits into 2^(y - m_tile) and publishes the row
-//     pairs (m_tile, sum) (the score_stats output);
-//   * first barrier of the unit's tiles; tile k merges the rows k, k + n_t, ...
-//     (n_t tiles) in a fixed order and publishes beta_r as score_combine does;
-//   * second barrier; every tile scales its held values by 2^(m_tile - beta_r),
-//     giving e = 2^(y - beta_r) = p_r / (G*W), and writes a, the walk rows and
-//     the Gram partials of its tile exactly as score_probs does.
-// A barrier is an arrival counter per head unit in the workspace (zeroed by a
-// small kernel before the launch).  Everything tiles exchange (the tile pairs
-// and beta) is written and read with device-scope relaxed atomic accesses,
-// which are coherent across the XCDs' L2 caches by themselves; a tile waits
-// for its own such stores to complete before one thread increments the
-// counter, and reads the others' only after the counter is full.  Fences at
-// device scope would instead write back and invalidate a whole L2 each time.  A workgroup
-// handles items x, x + P, x + 2P, ... (P = grid size); since P is at least the
-// tile count of any head unit, the tiles of a unit run on distinct,
-// co-resident workgroups, and the lowest unfinished unit can always finish.
-// Every poll loop is bounded: past the limit the device status records a
-// barrier timeout and the kernel runs to its end.
-//
-// Wavefronts 0 and 1 ("storers") issue every global load and store after the
-// first item; wavefronts 2 and 3 ("loaders") issue the global -> LDS copies of
-// K, so a loader's vmcnt holds nothing but its copies.  The loaders receive
-// their query fragments of later items through LDS from the storers.  The
-// copies of an item's first sub-tiles are issued as soon as the previous
-// item's sweep has ended, so they land during that item's barriers.
-constexpr int kFuseSub = 8;                    // 32-token sub-tiles per item
-constexpr int kFuseTok = 32 * kFuseSub;        // 256 tokens per item
-constexpr int kFuseSlots = 7;                  // LDS ring slots of 8 KB
-constexpr int kFuseLoaders = 2;
-constexpr uint32_t kSpinLimit = 1u << 16;      // polls (each after a short sleep), ~0.1 s
-static_assert(kFuseTok == kMinTokPerBlock, "tile partials sized for 256-token tiles");
-
-struct FuseSmem {
-  char ring[kFuseSlots * 32 * 256];
-  float2 stat[128];                 // this tile's (m, sum) per row
-  float beta[128];
-  union {
-    struct {
-      float a[kWaves][kFuseTok];    // per-M-tile partials of a_j
-      float pt[kMaxWalk][kFuseTok]; // walk rows P_t
-    } red;
-    uint4 q[2][8][64];              // loaders' query fragments [M-tile - 2][chunk][lane]
-  } u;
-};
-
-// One item of the persistent walk: head unit, tile, sub-tile count (0 = no
-// work), and the few head-unit fields the kernel reads, made wave-uniform (the
-// item records of a batch come in through vector loads).
-struct FuseItem {
-  int hu, tile, t0, n_sub, n;
-  bool valid;
-  const char* q;
-  const char* k;
-};
-
-__device__ inline const char* uniform_ptr(const char* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
-  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
-}
-
-__device__ inline FuseItem fuse_item(const Args& a, int x) {
-  FuseItem it;
-  it.hu = x / a.g.n_tmax;
-  it.tile = x - it.hu * a.g.n_tmax;
-  const HeadUnit u = head_unit(a, it.hu);
-  it.valid = __builtin_amdgcn_readfirstlane(int(u.valid)) != 0;
-  it.n = __builtin_amdgcn_readfirstlane(u.n);
-  it.q = uniform_ptr(u.q);
-  it.k = uniform_ptr(u.k);
-  it.t0 = it.tile * kFuseTok;
-  it.n_sub = it.valid && it.t0 < it.n ? min(kFuseSub, (it.n - it.t0 + 31) / 32) : 0;
-  return it;
-}
-
-// load_q for a FuseItem (only the query pointer of the head unit is read).
-__device__ inline void fuse_load_q(const Args& a, const FuseItem& it, int mt, int nn, int hh,
-                                   uint4 (&qf)[1][Geo<uint16_t, 128>::kChunks]) {
-  HeadUnit u{};
-  u.q = it.q;
-  load_q<uint16_t, 128, 1>(a, u, mt, nn, hh, qf);
-}
-
-// Device-scope coherent store / load of the values the tiles of a unit share.
-__device__ inline void st_shared(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_shared2(float* p, float2 v) {
-  const uint64_t b = uint64_t(__float_as_uint(v.x)) | (uint64_t(__float_as_uint(v.y)) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float ld_shared(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ inline float2 ld_shared2(const float* p) {
-  const uint64_t b = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float(uint32_t(b)), __uint_as_float(uint32_t(b >> 32)));
-}
-
-// Arrive at a head unit's barrier and wait for all n_t tiles (whole workgroup;
-// the caller's wavefronts have waited for their shared stores to complete).
-// A workgroup whose wait once ran out (gave_up, thread 0 only) arrives at
-// later barriers without waiting, so the grid still drains quickly.
-__device__ inline void unit_barrier(const Args& a, uint32_t* ctr, uint32_t n_t, bool& gave_up) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t spins = 0;
-    while (!gave_up && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n_t) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins == kSpinLimit) {
-        raise_status(a, kStatusSyncTimeout);
-        gave_up = true;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-template <int kWalk>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void score_fused_kernel(const Args a) {
-  using GE = Geo<uint16_t, 128>;
-  constexpr int kPerWave = GE::kTileBytes / (1024 * kFuseLoaders);   // copies per loader per sub-tile
-  __shared__ __align__(16) FuseSmem sm;
-  const Geometry& g = a.g;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nn = lane & 31, hh = lane >> 5;
-  const bool storer = wave < kWaves - kFuseLoaders;
-  const int lw = wave - (kWaves - kFuseLoaders);
-  const int n_items = g.n_hu * g.n_tmax;
-  const float c = a.c_log2;
-  const float wf = float(g.window);
-  const float log2_gw = log2f(float(g.group * g.window));
-  const int walk = g.walk;
-
-  // LDS destinations of this loader's copies within a ring slot.
-  uint32_t voff[kPerWave];
-#pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int lc = (i * kFuseLoaders + lw) * 64 + lane;
-    const int row = lc / GE::kCpr, slot = lc % GE::kCpr;
-    voff[i] = uint32_t(row * GE::kRowBytes + ((slot ^ GE::swz(row)) << 4));
-  }
-  const uint32_t ring_lds = lds_address(sm.ring) + uint32_t(lw * 1024);
-  auto issue = [&](const FuseItem& it, int st) {
-    const int t1 = min(it.t0 + kFuseTok, it.n);
-    const LdsDma dma(it.k + int64_t(it.t0) * GE::kRowBytes, uint32_t((t1 - it.t0) * GE::kRowBytes),
-                     a.k_stream_nt != 0);
-    const uint32_t dst = ring_lds + uint32_t((st % kFuseSlots) * GE::kTileBytes);
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i)
-      dma.load16(dst + uint32_t(i * kFuseLoaders * 1024), voff[i] + uint32_t(st * GE::kTileBytes));
-  };
-  // The first item at or after x that has tokens (x = n_items when none is left).
-  auto next_work = [&](int& x) {
-    FuseItem it{};
-    it.n_sub = 0;
-    while (x < n_items) {
-      it = fuse_item(a, x);
-      if (it.n_sub > 0) break;
-      if (threadIdx.x == 0 && it.tile == 0 && !it.valid) raise_status(a, kStatusBadItem);
-      x += int(gridDim.x);
-    }
-    return it;
-  };
-
-  // First item: every wavefront loads its own query fragments, then the
-  // loaders start the ring.
-  int x = int(blockIdx.x);
-  FuseItem cur = next_work(x);
-  bool gave_up = false;
-  uint4 qf[1][GE::kChunks];
-  if (x < n_items) fuse_load_q(a, cur, wave, nn, hh, qf);
-  vm_wait<0>();
-  if (!storer && x < n_items)
-    for (int st = 0; st < kFuseSlots - 1; ++st)
-      if (st < cur.n_sub) issue(cur, st);
-
-  while (x < n_items) {
-    const int n_sub = cur.n_sub;
-    // ---- sweep: logits of 32 rows x 256 tokens per wavefront, in registers
-    float y[kFuseSub][16];
-#pragma unroll
-    for (int st = 0; st < kFuseSub; ++st) {
-      if (st < n_sub) {
-        if (!storer) {
-          // Copies issued after sub-tile st: min(n_sub, slots - 1 + st) - st - 1.
-          const int later = min(n_sub, kFuseSlots - 1 + st) - st - 1;
-          switch (later) {
-            case 5: vm_wait<5 * kPerWave>(); break;
-            case 4: vm_wait<4 * kPerWave>(); break;
-            case 3: vm_wait<3 * kPerWave>(); break;
-            case 2: vm_wait<2 * kPerWave>(); break;
-            case 1: vm_wait<1 * kPerWave>(); break;
-            default: vm_wait<0>();
-          }
-        }
-        __syncthreads();
-        if (!storer && st + kFuseSlots - 1 < n_sub) issue(cur, st + kFuseSlots - 1);
-        uint4 kf[GE::kChunks];
-        read_frag<uint16_t, 128>(sm.ring + (st % kFuseSlots) * GE::kTileBytes, nn, hh, kf);
-        const floatx16_t acc = mfma_tile<uint16_t, 128>(qf[0], kf);
-        const bool valid = cur.t0 + 32 * st + nn < cur.n;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) y[st][v] = valid ? acc[v] * c : -INFINITY;
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) y[st][v] = -INFINITY;
-      }
-    }
-    __syncthreads();   // every ring read of this item is done
-
-    // ---- next item: resolve it and start its copies (the ring is empty).
-    int xn = x + int(gridDim.x);
-    const FuseItem nxt = next_work(xn);
-    if (!storer && xn < n_items)
-      for (int st = 0; st < kFuseSlots - 1; ++st)
-        if (st < nxt.n_sub) issue(nxt, st);
-
-    // ---- tile statistics: m = row max over the tile, e = 2^(y - m), sum.
-    float mv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float m = y[0][v];
-#pragma unroll
-      for (int st = 1; st < kFuseSub; ++st) m = fmaxf(m, y[st][v]);
-      mv[v] = half_max(m);
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float z = 0.f;
-#pragma unroll
-      for (int st = 0; st < kFuseSub; ++st) {
-        const float e = __builtin_amdgcn_exp2f(y[st][v] - mv[v]);
-        y[st][v] = e;
-        z += e;
-      }
-      z = half_sum(z);
-      if (nn == v) sm.stat[wave * 32 + out_row(v, hh)] = make_float2(mv[v], z);
-    }
-    const int n_t = (cur.n + kFuseTok - 1) / kFuseTok;
-    uint32_t* ctr = a.sync + size_t(cur.hu) * 2;
-    __syncthreads();
-    if (storer) {
-      if (threadIdx.x < g.rows_pad) {
-        float* part = a.part1 + (size_t(cur.hu) * g.n_t1 + cur.tile) * g.rows_pad * 2;
-        st_shared2(part + 2 * threadIdx.x, sm.stat[threadIdx.x]);
-      }
-      vm_wait<0>();
-    }
-    unit_barrier(a, ctr, uint32_t(n_t), gave_up);
-
-    // ---- merge: this tile owns rows r = 2 * tile + wave + 2 n_t k (storers).
-    if (storer) {
-      const float* part = a.part1 + size_t(cur.hu) * g.n_t1 * g.rows_pad * 2;
-      for (int r = 2 * cur.tile + wave; r < g.rows; r += 2 * n_t) {
-        constexpr int kPer = 8;   // n_t <= 512 tiles: 8 per lane
-        float2 p[kPer];
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int k = lane + 64 * i;
-          p[i] = k < n_t ? ld_shared2(part + (size_t(k) * g.rows_pad + r) * 2) : make_float2(-INFINITY, 0.f);
-        }
-        float m = p[0].x;
-#pragma unroll
-        for (int i = 1; i < kPer; ++i) m = fmaxf(m, p[i].x);
-        float z = 0.f;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) z += p[i].x == -INFINITY ? 0.f : p[i].y * __builtin_amdgcn_exp2f(p[i].x - m);
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-          const float m2 = __shfl_xor(m, s, 64), z2 = __shfl_xor(z, s, 64);
-          const float mm = fmaxf(m, m2);
-          z = (m == -INFINITY ? 0.f : z * __builtin_amdgcn_exp2f(m - mm)) +
-              (m2 == -INFINITY ? 0.f : z2 * __builtin_amdgcn_exp2f(m2 - mm));
-          m = mm;
-        }
-        if (lane == 0) st_shared(a.beta + size_t(cur.hu) * g.rows_pad + r, m + log2f(z) + log2_gw);
-      }
-      vm_wait<0>();
-    }
-    unit_barrier(a, ctr + 1, uint32_t(n_t), gave_up);
-    if (storer) {
-      // Rows past G*W (zero queries) get beta = +inf, so they add nothing.
-      sm.beta[threadIdx.x] = int(threadIdx.x) < g.rows ? ld_shared(a.beta + size_t(cur.hu) * g.rows_pad + threadIdx.x)
-                                                       : INFINITY;
-    }
-    __syncthreads();
-
-    // ---- e = 2^(y - beta): partials of a_j and the walk rows, through LDS.
-    {
-      float f[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) f[v] = __builtin_amdgcn_exp2f(mv[v] - sm.beta[wave * 32 + out_row(v, hh)]);
-#pragma unroll
-      for (int st = 0; st < kFuseSub; ++st) {
-        float sq[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float e0 = y[st][4 * q] * f[4 * q], e1 = y[st][4 * q + 1] * f[4 * q + 1];
-          const float e2 = y[st][4 * q + 2] * f[4 * q + 2], e3 = y[st][4 * q + 3] * f[4 * q + 3];
-          sq[q] = (e0 + e1) + (e2 + e3);
-        }
-        float tp = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tp), __float_as_uint(tp), false, false);
-        tp = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        if (hh == 0) sm.u.red.a[wave][32 * st + nn] = tp;
-        if constexpr (kWalk != kWalkNone) {
-          if (wave == 0) {
-            float grp[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const auto gs = __builtin_amdgcn_permlane32_swap(__float_as_uint(sq[q]), __float_as_uint(sq[q]),
-                                                               false, false);
-              grp[2 * q] = __uint_as_float(gs[0]);
-              grp[2 * q + 1] = __uint_as_float(gs[1]);
-            }
-            if (hh == 0) {
-#pragma unroll
-              for (int t = 0; t < kMaxWalk; ++t) {
-                if (kWalk == kWalkFast8 && t >= 4) break;
-                if (t < walk)
-                  sm.u.red.pt[t][32 * st + nn] = wf * (kWalk == kWalkFast8 ? grp[2 * t] + grp[2 * t + 1] : grp[t]);
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- storers: a_j, the walk rows and the Gram partials of the tile.
-    if (storer) {
-      const int tid = threadIdx.x;   // 0 .. 127
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = tid + 128 * h;
-        const int tok = cur.t0 + j;
-        if (tok < cur.n) {
-          float s = sm.u.red.a[0][j];
-#pragma unroll
-          for (int r = 1; r < kWaves; ++r) s += sm.u.red.a[r][j];
-          a.a[size_t(cur.hu) * g.max_tokens + tok] = s;
-          if constexpr (kWalk != kWalkNone)
-            for (int t = 0; t < walk; ++t)
-              a.p[(size_t(cur.hu) * walk + t) * g.max_tokens + tok] = sm.u.red.pt[t][j];
-        }
-      }
-      if constexpr (kWalk != kWalkNone) {
-        // Gram pair p = t (t + 1) / 2 + t' (t' <= t): the diagonal holds |P_t|_1.
-        // Tokens past the cache end hold zero walk rows (their logits were -inf).
-        const int n_pairs = walk * (walk + 1) / 2;
-        float* gout = a.gram + (size_t(cur.hu) * g.n_t2 + cur.tile) * (kMaxWalk * kMaxWalk);
-        for (int p = wave; p < n_pairs; p += kWaves - kFuseLoaders) {
-          int t = 0;
-          while ((t + 1) * (t + 2) / 2 <= p) ++t;
-          const int t2 = p - t * (t + 1) / 2;
-          float s = 0.f;
-#pragma unroll
-          for (int i = 0; i < kFuseTok / 64; ++i) {
-            const int j = lane + 64 * i;
-            const float v = sm.u.red.pt[t][j];
-            s = fmaf(v, t2 == t ? 1.f : sm.u.red.pt[t2][j], s);
-          }
-#pragma unroll
-          for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-          if (lane == 0) gout[t * kMaxWalk + t2] = s;
-        }
-      }
-    }
-    __syncthreads();   // the reduction buffers are free again
-
-    // ---- query fragments of the next item: storers load their own and the
-    // loaders' (through LDS).
-    if (xn < n_items) {
-      if (storer) {
-        fuse_load_q(a, nxt, wave, nn, hh, qf);
-        uint4 ql[1][GE::kChunks];
-        fuse_load_q(a, nxt, wave + kFuseLoaders, nn, hh, ql);
-#pragma unroll
-        for (int ch = 0; ch < GE::kChunks; ++ch) sm.u.q[wave][ch][lane] = ql[0][ch];
-      }
-      __syncthreads();
-      if (!storer) {
-#pragma unroll
-        for (int ch = 0; ch < GE::kChunks; ++ch) qf[0][ch] = sm.u.q[lw][ch][lane];
-      }
-    }
-    cur = nxt;
-    x = xn;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void sync_zero_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 // Pass 1: one workgroup per (tile, head unit).
 // NW wavefronts per workgroup (4, or 16 for more than 4 row tiles): one row
 // tile per wavefront keeps its query fragments and row statistics within 128
@@ -1214,65 +797,61 @@ hipError_t launch_pass(const Args& a, hipStream_t s) {
 #undef NX_MPW
 }
 
-// Workgroups of the fused kernel that fit on the device at once (cached per
-// device): the grid of its cooperative launch.
-int fused_capacity(int kWalkMode) {
-  static std::atomic<int> cap[64][3];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int c = cap[dev][kWalkMode].load(std::memory_order_relaxed);
-  if (c == 0) {
-    int cus = 0, per_cu = 0, coop = 0;
-    const void* f = kWalkMode == 0 ? reinterpret_cast<const void*>(score_fused_kernel<kWalkNone>)
-                    : kWalkMode == 1 ? reinterpret_cast<const void*>(score_fused_kernel<kWalkFast4>)
-                                     : reinterpret_cast<const void*>(score_fused_kernel<kWalkFast8>);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, 0) != hipSuccess || !coop)
-      c = -1;
-    else
-      c = cus * per_cu > 0 ? cus * per_cu : -1;
-    cap[dev][kWalkMode].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
+// ---------------------------------------------------------------------------
+// Read-ceiling probe (measurement only): streams a buffer the way the score
+// sweeps stream K.  The buffer is cut into "heads" of up to 2^22 rows of 256 B
+// (1 GiB, so 32-bit buffer offsets address them); one workgroup reads
+// kProbeRows consecutive rows, the same span as a score workgroup at 2048
+// tokens.  Mode 0 copies through the sweeps' LDS ring (global -> LDS, four
+// slots of 8 KB, every wavefront a loader) and reads each slot back as MFMA
+// fragments; mode 1 issues plain 16-B vector loads, eight in flight per lane.
+// Every value read is folded into an XOR that is stored only if it equals an
+// unlikely constant, so no load is dead and nothing else is written.
+constexpr int kProbeRows = 2048;
+constexpr int64_t kProbeHeadRows = int64_t(1) << 22;
 
-int fused_walk_mode(const Geometry& g) {
-  if (g.walk == 0) return 0;
-  if (g.group == 4 && g.walk <= 8) return 1;
-  if (g.group == 8 && g.walk <= 4) return 2;
-  return -1;
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, int64_t rows,
+                                                               uint32_t* sink) {
+  using GE = Geo<uint16_t, 128>;
+  __shared__ __align__(16) char smem[GE::kSlotsStats * GE::kTileBytes];
+  const int64_t head_row0 = int64_t(blockIdx.y) * kProbeHeadRows;
+  const int64_t head_rows = min(kProbeHeadRows, rows - head_row0);
+  const int t0 = int(blockIdx.x) * kProbeRows;
+  if (t0 >= head_rows) return;
+  const int n = int(head_rows);
+  const char* base = src + head_row0 * GE::kRowBytes;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  if constexpr (kMode == 0) {
+    HeadUnit u{};
+    u.k = base;
+    u.n = n;
+    const int n_sub = (min(t0 + kProbeRows, n) - t0 + 31) / 32;
+    sweep_tiles<uint16_t, 128, GE::kSlotsStats, kWaves, kWaves>(u, t0, n_sub, smem, wave, false,
+                                                                [&](int, const char* cur) {
+      uint4 kf[GE::kChunks];
+      read_frag<uint16_t, 128>(cur, lane & 31, lane >> 5, kf);
+#pragma unroll
+      for (int c = 0; c < GE::kChunks; ++c) acc ^= kf[c].x ^ kf[c].y ^ kf[c].z ^ kf[c].w;
+    });
+  } else {
+    const int t1 = min(t0 + kProbeRows, n);
+    const Buf b(base + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
+    const uint32_t bytes = uint32_t((t1 - t0) * GE::kRowBytes);
+    constexpr int kInFlight = 8;
+    for (uint32_t off = threadIdx.x * 16u; off < bytes; off += kThreads * 16u * kInFlight) {
+      uint4 v[kInFlight];
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i) v[i] = b.ld16(off + uint32_t(i) * kThreads * 16u);
+#pragma unroll
+      for (int i = 0; i < kInFlight; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
 }
 
 }  // namespace
-
-bool score_fused_fits(const Geometry& g) {
-  if (g.dtype != NX_BF16 || g.head_dim != 128 || g.rows_pad > 128 || g.block != 1) return false;
-  const int mode = fused_walk_mode(g);
-  if (mode < 0) return false;
-  const int cap = fused_capacity(mode);
-  const int n_t = (g.max_tokens + kFuseTok - 1) / kFuseTok;
-  return cap > 0 && n_t <= cap;
-}
-
-hipError_t launch_score_fused(const Args& a, hipStream_t s) {
-  const int n_sync = a.g.n_hu * 2;
-  hipLaunchKernelGGL(sync_zero_kernel, dim3((n_sync + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
-                     a.sync, n_sync);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int mode = fused_walk_mode(a.g);
-  const int cap = mode < 0 ? 0 : fused_capacity(mode);
-  const int n_items = a.g.n_hu * a.g.n_tmax;
-  if (cap <= 0 || a.g.n_tmax > cap || a.g.tok_per_block != kFuseTok) return hipErrorInvalidValue;
-  const int grid = n_items < cap ? n_items : cap;
-  Args arg = a;
-  void* params[] = {&arg};
-  const void* f = mode == 0 ? reinterpret_cast<const void*>(score_fused_kernel<kWalkNone>)
-                  : mode == 1 ? reinterpret_cast<const void*>(score_fused_kernel<kWalkFast4>)
-                              : reinterpret_cast<const void*>(score_fused_kernel<kWalkFast8>);
-  return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kThreads), params, 0, s);
-}
 
 hipError_t launch_score_stats(const Args& a, hipStream_t s) { return launch_pass<false>(a, s); }
 
@@ -1282,5 +861,19 @@ hipError_t launch_score_combine(const Args& a, hipStream_t s) {
 }
 
 hipError_t launch_score_probs(const Args& a, hipStream_t s) { return launch_pass<true>(a, s); }
+
+hipError_t launch_stream_read(const void* src, int64_t rows, int mode, uint32_t* sink,
+                              hipStream_t s) {
+  const int64_t heads = (rows + kProbeHeadRows - 1) / kProbeHeadRows;
+  const int64_t per_head = rows < kProbeHeadRows ? rows : kProbeHeadRows;
+  const dim3 grid(unsigned((per_head + kProbeRows - 1) / kProbeRows), unsigned(heads));
+  if (mode == 0)
+    hipLaunchKernelGGL(stream_read_kernel<0>, grid, dim3(kThreads), 0, s,
+                       static_cast<const char*>(src), rows, sink);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<1>, grid, dim3(kThreads), 0, s,
+                       static_cast<const char*>(src), rows, sink);
+  return hipGetLastError();
+}
 
 }  // namespace nx

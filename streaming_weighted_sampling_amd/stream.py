@@ -27,10 +27,12 @@ class StreamingCache:
     order; with inplace=True one buffer is compacted in place (hole filling:
     only the kept rows past the kept count move, then the new rows follow), so
     an event writes about n_append rows per head instead of budget.
+    With export_w=True every event also writes the Nexus weights its selection
+    used (read them back with weights()).
     """
 
     def __init__(self, cfg: NexusConfig, n_layers, capacity, budget, n_append, walk_iters,
-                 seed=0, seq_id=0, device="cuda", inplace=False):
+                 seed=0, seq_id=0, device="cuda", inplace=False, export_w=False):
         if inplace:
             cfg = replace(cfg, compact=1)
         self.inplace = inplace
@@ -47,6 +49,9 @@ class StreamingCache:
                                  dtype=cfg.dtype, device=device)
         self.app_v = torch.zeros_like(self.app_k)
         self.keep = torch.zeros(n_layers, cfg.n_kv_heads, budget, dtype=torch.int32, device=device)
+        self.w = (torch.zeros(n_layers, cfg.n_kv_heads * cfg.units(capacity), dtype=torch.float32,
+                              device=device) if export_w else None)
+        self.last_units = 0   # selection units per head of the last event
         self.ws = new_workspace(cfg, capacity, n_layers, walk_iters, device=device)
         self.cur = 0          # which buffer holds the live cache
         self.n_tokens = 0     # live rows per head
@@ -71,7 +76,8 @@ class StreamingCache:
                           out_v=None if out_v is None else out_v[l], app_k=self.app_k[l],
                           app_v=self.app_v[l], kv_head_stride=rows, out_head_stride=rows,
                           n_tokens=n_tokens, budget=self.budget, n_append=self.n_append,
-                          layer=l, seq_id=self.seq_id)
+                          layer=l, seq_id=self.seq_id,
+                          out_w=None if self.w is None else self.w[l])
                      for l in range(self.n_layers)]
             self._units[key] = make_units(items, device=self.device)
         return self._units[key]
@@ -87,8 +93,16 @@ class StreamingCache:
                        workspace=self.ws, step=self.step_no, max_out_rows=kept + self.n_append)
         if not self.inplace:
             self.cur = 1 - self.cur
+        self.last_units = self.cfg.units(self.n_tokens)
         self.n_tokens = kept + self.n_append
         self.step_no += 1
+
+    def weights(self, layer):
+        """The weights [n_kv_heads, units] the last event selected on (export_w=True)."""
+        if self.w is None:
+            raise ValueError("StreamingCache was built without export_w")
+        nu = self.last_units
+        return self.w[layer][:self.cfg.n_kv_heads * nu].view(self.cfg.n_kv_heads, nu)
 
     def live(self):
         """(k, v) views of the live cache: [n_layers, n_kv_heads, n_tokens, head_dim]."""

@@ -53,7 +53,7 @@ int main(void) {
   F(nx_desc, max_out_rows); F(nx_desc, kv_head_stride); F(nx_desc, workspace);
   F(nx_desc, stream); F(nx_desc, n_avg); F(nx_unit, app_v); F(nx_unit, kv_head_stride); F(nx_unit, n_tokens);
   F(nx_unit, seq_id); F(nx_unit, head_cap); F(nx_unit, head_budget);
-  F(nx_desc, head_alloc); F(nx_desc, head_floor); F(nx_desc, score_mode);
+  F(nx_desc, head_alloc); F(nx_desc, head_floor); F(nx_desc, out_w); F(nx_unit, out_w);
   return 0;
 }''')
     exe = tmp_path / "layout"
@@ -76,7 +76,8 @@ int main(void) {
     assert int(out["nx_unit.head_budget"]) == NxUnit.head_budget.offset
     assert int(out["nx_desc.head_alloc"]) == NxDesc.head_alloc.offset
     assert int(out["nx_desc.head_floor"]) == NxDesc.head_floor.offset
-    assert int(out["nx_desc.score_mode"]) == NxDesc.score_mode.offset
+    assert int(out["nx_desc.out_w"]) == NxDesc.out_w.offset
+    assert int(out["nx_unit.out_w"]) == NxUnit.out_w.offset
 
 
 def _desc(**kw):
@@ -98,8 +99,7 @@ def test_status_strings(lib):
     assert lib.nx_stage_name(7) == b"sample_select"
     assert lib.nx_stage_name(8) == b"estimate_keys"
     assert lib.nx_stage_name(9) == b"head_budget"
-    assert lib.nx_stage_name(10) == b"score_fused"
-    assert lib.nx_stage_name(11) == b"unknown"
+    assert lib.nx_stage_name(10) == b"unknown"
 
 
 def test_workspace_query(lib):
@@ -134,11 +134,6 @@ def test_host_validation_codes(lib):
     assert _step(lib, _desc(), n=0) == _lib.NX_EINVAL
     assert _step(lib, _desc(n_sink=500, n_recent=500)) == _lib.NX_EINVAL
     assert _step(lib, _desc(), q=None) == _lib.NX_EINVAL
-    assert _step(lib, _desc(score_mode=2)) == _lib.NX_EINVAL
-    assert _step(lib, _desc(score_mode=-1)) == _lib.NX_EINVAL
-    # single-read scoring needs bf16, head_dim 128 and at most 128 window rows per KV head
-    assert _step(lib, _desc(score_mode=_lib.NX_SCORE_ONE_READ, head_dim=64)) == _lib.NX_EUNSUPPORTED
-    assert _step(lib, _desc(score_mode=_lib.NX_SCORE_ONE_READ, window=64)) == _lib.NX_EUNSUPPORTED
     assert _step(lib, _desc(head_dim=96)) == _lib.NX_EUNSUPPORTED
     assert _step(lib, _desc(dtype=7)) == _lib.NX_EUNSUPPORTED
     assert _step(lib, _desc(), h=9) == _lib.NX_EUNSUPPORTED              # walk depth > 8
@@ -148,6 +143,10 @@ def test_host_validation_codes(lib):
     assert _step(lib, _desc(), ok=FAKE + (1 << 32) + 64) == _lib.NX_EALIAS
     assert _step(lib, _desc(), ov=FAKE) == _lib.NX_EALIAS
     assert _step(lib, _desc(), keep=FAKE + (4 << 32)) == _lib.NX_EALIAS
+    # the weight export overlapping the cache, the keep array or an output
+    assert _step(lib, _desc(out_w=FAKE + (1 << 32) + 4096)) == _lib.NX_EALIAS
+    assert _step(lib, _desc(out_w=FAKE + (3 << 32))) == _lib.NX_EALIAS
+    assert _step(lib, _desc(out_w=FAKE + (5 << 32) + 256)) == _lib.NX_EALIAS
     # valid arguments but no workspace
     assert _step(lib, _desc()) == _lib.NX_EWORKSPACE
     d = _desc(workspace=FAKE + (6 << 32), workspace_bytes=1024)

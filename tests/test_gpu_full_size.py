@@ -1,11 +1,13 @@
 """Full-size parity of the batched path (the launch configuration bench.py times)
-and of the streaming loop, on sampled head units the oracle can afford.
+and of the streaming loop.
 
-For every head unit of the batch the kept set is checked for its properties
-(exactly min(B, N) ascending indices in range, compacted rows equal to the
-gathered rows); for sampled units the weights must match the oracle within
-1e-3, the kept set must equal the oracle's selection on the GPU's weights, and
-it must share at least 99.9% with the pure-oracle result.
+Every head unit of the 32-layer event and of the 70B-shaped share, and one KV
+head of every item of the ragged batch, is checked against the oracle: the
+weights the batch exported (the ones its selection used) within 1e-3 of the
+oracle's, the kept set equal to the oracle's selection on those weights, the
+pure oracle's kept set shared to the stated bar (at least ceil(0.999 B),
+flips only at the boundary), and the compacted rows equal to the gathered rows.
+The oracle runs the units in threads on the host.
 """
 
 import numpy as np
@@ -16,7 +18,7 @@ import streaming_weighted_sampling_amd as nx
 from oracle import nexus
 from streaming_weighted_sampling_amd.stream import StreamingCache
 from tests import gpu_common as gc
-from workloads import (WORKLOADS, budget_for, gen_layer, gen_model, gen_stream_queries,
+from workloads import (WORKLOADS, bf16_bits, budget_for, gen_model, gen_stream_queries,
                        gen_stream_rows, ragged_lengths)
 
 pytestmark = pytest.mark.gpu
@@ -36,60 +38,79 @@ def _check_all_keeps(keep, n_tokens, budget):
     assert bool((k[..., 1:] > k[..., :-1]).all())
 
 
-def _check_unit(cfg, wl, q, k, v, keep, out_k, out_v, n, budget, walk, seed, layer, step,
-                seq_id, heads):
-    """Sampled-unit parity for KV heads `heads` of one (sequence, layer) item."""
-    ws = nx.new_workspace(cfg, n, 1, walk, device=DEV)
-    w_gpu = nx.nx_nexus_weights(cfg, q, k, n, walk, workspace=ws).cpu().numpy()
-    nx.nx_read_device_status(cfg, ws)
-    qh, dt = gc.host(q)
-    kh, _ = gc.host(k[:, :n])
-    vh, _ = gc.host(v[:, :n])
-    ref = nexus.evict_step(qh, kh, vh, budget, walk, seed, dtype=dt, layer=layer, step=step,
-                           seq_id=seq_id, heads=heads)
-    _, on_gpu_w = nexus.select_from_weights(w_gpu, budget, seed, layer=layer, step=step,
-                                            seq_id=seq_id)
+def _oracle_unit(job):
+    """The oracle on one head unit, checked against the GPU's results for it.
+
+    job: (tag, q_bits [G, W, D], k_bits [N, D], budget, walk, seed, layer, step,
+    unit_id, w_gpu [N], keep_gpu [kept])."""
+    tag, qb, kb, budget, walk, seed, layer, step, unit_id, w_gpu, keep_gpu = job
+    n = kb.shape[0]
     kept = min(budget, n)
-    for h in heads:
-        got = keep[h, :kept].cpu().numpy()
-        gc.assert_weights_close(w_gpu[h], ref["w"][h], f"layer {layer} head {h}")
-        np.testing.assert_array_equal(got, on_gpu_w[h])
-        assert gc.overlap_fraction(got, ref["keep"][h]) >= 0.999
-        assert gc.rows_equal(out_k[h], k[h], got)
-        assert gc.rows_equal(out_v[h], v[h], got)
+    w_ref = nexus.head_weights(nexus.as_f64(qb, "bf16"), nexus.as_f64(kb, "bf16"), walk)["w"]
+    keys_ref = nexus.head_keys(w_ref, n, unit_id, layer, step, seed, 1)
+    keep_ref = nexus.select_top(keys_ref, budget)
+    gc.assert_weights_close(w_gpu, w_ref, tag)
+    keys_gpu_w = nexus.head_keys(np.asarray(w_gpu, np.float64), n, unit_id, layer, step, seed, 1)
+    np.testing.assert_array_equal(keep_gpu, nexus.select_top(keys_gpu_w, budget), err_msg=tag)
+    gc.assert_kept_matches_oracle(keep_gpu, keep_ref, keys_ref, kept, tag)
+    return kept - len(set(keep_gpu.tolist()) & set(keep_ref.tolist()))
 
 
-def test_stream32_event_full_size():
-    """One eviction event over all 32 layers at N = 32768 (the benchmarked step)."""
-    wl = WORKLOADS["llama3_8b_stream32"]
+def _check_rows(keep, out_k, out_v, k, v, kept):
+    """Compacted rows of every head of one item equal the gathered rows (on the GPU)."""
+    idx = keep[:, :kept].long()
+    for src, out in ((k, out_k), (v, out_v)):
+        ref = torch.gather(src, 1, idx[:, :, None].expand(-1, -1, src.shape[2]))
+        assert torch.equal(out[:, :kept].view(torch.int16), ref.view(torch.int16))
+
+
+def _full_model_event(wl, seed, step):
+    """One nx_evict_batch over every layer of `wl` at its full size, weights
+    exported; returns the host-side inputs and outputs for the oracle."""
     cfg = _cfg(wl)
-    n, B, L = wl.n_tokens, wl.budget, wl.n_layers
+    n, B, L, H, G = wl.n_tokens, wl.budget, wl.n_layers, wl.h_kv, wl.group
     q, k, v = gen_model(wl, device=DEV)
-    keep = torch.empty(L, wl.h_kv, B, dtype=torch.int32, device=DEV)
-    out_k = torch.empty(L, wl.h_kv, B, wl.head_dim, dtype=torch.bfloat16, device=DEV)
+    keep = torch.empty(L, H, B, dtype=torch.int32, device=DEV)
+    out_k = torch.empty(L, H, B, wl.head_dim, dtype=torch.bfloat16, device=DEV)
     out_v = torch.empty_like(out_k)
+    w_sel = torch.full((L, H, n), float("nan"), device=DEV)
     items = [dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=out_k[l], out_v=out_v[l],
                   kv_head_stride=n * wl.head_dim, out_head_stride=B * wl.head_dim,
-                  n_tokens=n, budget=B, layer=l) for l in range(L)]
+                  n_tokens=n, budget=B, layer=l, out_w=w_sel[l]) for l in range(L)]
     units = nx.make_units(items, device=DEV)
     ws = nx.new_workspace(cfg, n, L, wl.walk_iters, device=DEV)
-    step = 7
-    nx.nx_evict_batch(cfg, units, L, n, wl.walk_iters, 0, workspace=ws, step=step,
+    nx.nx_evict_batch(cfg, units, L, n, wl.walk_iters, seed, workspace=ws, step=step,
                       max_out_rows=B)
     nx.nx_read_device_status(cfg, ws)
     _check_all_keeps(keep, n, B)
-    for l, heads in ((0, [0]), (13, [5]), (31, [7])):
-        _check_unit(cfg, wl, q[l], k[l], v[l], keep[l], out_k[l], out_v[l], n, B,
-                    wl.walk_iters, 0, l, step, 0, heads)
+    for l in range(L):
+        _check_rows(keep[l], out_k[l], out_v[l], k[l], v[l], min(B, n))
+    qb, kb = bf16_bits(q), bf16_bits(k)
+    del k, v, out_k, out_v
+    w_h, keep_h = w_sel.cpu().numpy(), keep.cpu().numpy()
+    jobs = [(f"layer {l} head {h}", qb[l, h * G:(h + 1) * G], kb[l, h], B, wl.walk_iters, seed, l,
+             step, h, w_h[l, h], keep_h[l, h, :min(B, n)]) for l in range(L) for h in range(H)]
+    return jobs
+
+
+def test_stream32_event_full_size():
+    """One eviction event over all 32 layers at N = 32768 (the benchmarked step):
+    all 256 head units against the oracle."""
+    wl = WORKLOADS["llama3_8b_stream32"]
+    jobs = _full_model_event(wl, seed=0, step=7)
+    flips = gc.oracle_map(_oracle_unit, jobs)
+    assert len(flips) == wl.n_layers * wl.h_kv
+    print(f"256 head units checked; flips against the pure oracle: {sum(flips)}")
 
 
 def test_ragged_batch_full_size():
-    """16 sequences of 4K..16K tokens x 32 layers in one call (Zipf salience)."""
+    """16 sequences of 4K..16K tokens x 32 layers in one call (Zipf salience):
+    one KV head of every one of the 512 items against the oracle."""
     wl = WORKLOADS["ragged16_zipf"]
     cfg = _cfg(wl)
     lens = ragged_lengths(wl)
     n_max = max(lens)
-    D, Hk, L = wl.head_dim, wl.h_kv, wl.n_layers
+    D, Hk, L, G = wl.head_dim, wl.h_kv, wl.n_layers, wl.group
     bufs, items = [], []
     for s, n in enumerate(lens):
         B = budget_for(n)
@@ -97,53 +118,47 @@ def test_ragged_batch_full_size():
         keep = torch.empty(L, Hk, B, dtype=torch.int32, device=DEV)
         ok = torch.empty(L, Hk, B, D, dtype=torch.bfloat16, device=DEV)
         ov = torch.empty_like(ok)
-        bufs.append((q, k, v, keep, ok, ov, n, B))
+        w_sel = torch.full((L, Hk, n), float("nan"), device=DEV)
+        bufs.append((q, k, v, keep, ok, ov, w_sel, n, B))
         for l in range(L):
             items.append(dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=ok[l], out_v=ov[l],
                               kv_head_stride=n * D, out_head_stride=B * D, n_tokens=n,
-                              budget=B, layer=l, seq_id=s))
+                              budget=B, layer=l, seq_id=s, out_w=w_sel[l]))
     units = nx.make_units(items, device=DEV)
     ws = nx.new_workspace(cfg, n_max, len(items), wl.walk_iters, device=DEV)
     nx.nx_evict_batch(cfg, units, len(items), n_max, wl.walk_iters, 11, workspace=ws, step=3,
                       max_out_rows=budget_for(n_max))
     nx.nx_read_device_status(cfg, ws)
-    for (q, k, v, keep, ok, ov, n, B) in bufs:
+    jobs = []
+    for s, (q, k, v, keep, ok, ov, w_sel, n, B) in enumerate(bufs):
         _check_all_keeps(keep, n, B)
-    shortest = int(np.argmin(lens))
-    longest = int(np.argmax(lens))
-    for s, l, h in ((shortest, 0, 2), (longest, 31, 6), (5, 16, 0)):
-        q, k, v, keep, ok, ov, n, B = bufs[s]
-        _check_unit(cfg, wl, q[l], k[l], v[l], keep[l], ok[l], ov[l], n, B, wl.walk_iters, 11,
-                    l, 3, s, [h])
+        for l in range(L):
+            _check_rows(keep[l], ok[l], ov[l], k[l], v[l], min(B, n))
+            h = (s * L + l) % Hk
+            jobs.append((f"seq {s} layer {l} head {h}", bf16_bits(q[l, h * G:(h + 1) * G]),
+                         bf16_bits(k[l, h]), B, wl.walk_iters, 11, l, 3, s * Hk + h,
+                         w_sel[l, h].cpu().numpy(), keep[l, h, :min(B, n)].cpu().numpy()))
+    del bufs
+    flips = gc.oracle_map(_oracle_unit, jobs)
+    assert len(flips) == len(items)
+    print(f"{len(items)} items checked; flips against the pure oracle: {sum(flips)}")
 
 
 def test_llama70b_share_full_size():
-    """8 layers, GQA 64:8, W = 64, N = 131072 -> B = 13107 (10x reduction)."""
+    """8 layers, GQA 64:8, W = 64, N = 131072 -> B = 13107 (10x reduction):
+    all 64 head units against the oracle."""
     wl = WORKLOADS["llama70b_share"]
-    cfg = _cfg(wl)
-    n, B, L = wl.n_tokens, wl.budget, wl.n_layers
-    q, k, v = gen_model(wl, device=DEV)
-    keep = torch.empty(L, wl.h_kv, B, dtype=torch.int32, device=DEV)
-    out_k = torch.empty(L, wl.h_kv, B, wl.head_dim, dtype=torch.bfloat16, device=DEV)
-    out_v = torch.empty_like(out_k)
-    items = [dict(q=q[l], k=k[l], v=v[l], keep=keep[l], out_k=out_k[l], out_v=out_v[l],
-                  kv_head_stride=n * wl.head_dim, out_head_stride=B * wl.head_dim,
-                  n_tokens=n, budget=B, layer=l) for l in range(L)]
-    units = nx.make_units(items, device=DEV)
-    ws = nx.new_workspace(cfg, n, L, wl.walk_iters, device=DEV)
-    nx.nx_evict_batch(cfg, units, L, n, wl.walk_iters, 0, workspace=ws, step=0, max_out_rows=B)
-    nx.nx_read_device_status(cfg, ws)
-    _check_all_keeps(keep, n, B)
-    for l, heads in ((0, [3]), (7, [6])):
-        _check_unit(cfg, wl, q[l], k[l], v[l], keep[l], out_k[l], out_v[l], n, B,
-                    wl.walk_iters, 0, l, 0, 0, heads)
+    jobs = _full_model_event(wl, seed=0, step=0)
+    flips = gc.oracle_map(_oracle_unit, jobs, workers=8)
+    assert len(flips) == wl.n_layers * wl.h_kv
+    print(f"64 head units checked; flips against the pure oracle: {sum(flips)}")
 
 
-def _stream_setup(wl, layers, n0, steps_seen=()):
+def _stream_setup(wl, layers, n0, export_w=False):
     cfg = _cfg(wl)
     B, A = wl.budget, wl.stream_append
     sc = StreamingCache(cfg, len(layers), max(n0 + A, B + A), B, A, wl.walk_iters, seed=0,
-                        device=DEV)
+                        device=DEV, export_w=export_w)
     q, k, v = gen_model(wl, device=DEV, n_tokens=n0, layers=layers)
     # The rows that arrive before the first event complete the initial cache.
     k0 = torch.empty(len(layers), wl.h_kv, n0 + A, wl.head_dim, dtype=k.dtype, device=DEV)
@@ -165,34 +180,41 @@ def _stream_inputs(sc, wl, layers, step):
 
 
 def test_streaming_100_events_teacher_forced():
-    """All 32 layers: 100 append-256 / evict-to-6554 events; the oracle re-runs
-    sampled events on the GPU's own pre-event caches."""
+    """All 32 layers: 100 append-256 / evict-to-6554 events; at sampled events
+    the oracle re-runs every KV head of two layers on the GPU's own pre-event
+    caches (teacher forcing), against the weights the batch exported."""
     wl = WORKLOADS["llama3_8b_stream32"]
     layers = list(range(wl.n_layers))
-    sc = _stream_setup(wl, layers, wl.n_tokens)
-    B, A = wl.budget, wl.stream_append
-    checked = {0: (0, 0), 1: (21, 3), 50: (9, 4), 99: (31, 7)}
+    sc = _stream_setup(wl, layers, wl.n_tokens, export_w=True)
+    B, A, G = wl.budget, wl.stream_append, wl.group
+    checked = {0: (0, 17), 1: (21, 3), 50: (9, 30), 99: (31, 7)}
     for step in range(wl.stream_steps):
         _stream_inputs(sc, wl, layers, step)
         pre = None
         if step in checked:
-            li, h = checked[step]
             k_pre, v_pre = sc.live()
-            pre = (li, h, sc.q[li].clone(), k_pre[li].clone(), v_pre[li].clone(), sc.n_tokens,
-                   sc.app_k[li].clone(), sc.app_v[li].clone())
+            pre = [(li, sc.q[li].clone(), k_pre[li].clone(), v_pre[li].clone(), sc.app_k[li].clone(),
+                    sc.app_v[li].clone()) for li in checked[step]]
+            n = sc.n_tokens
         sc.step()
         if pre is not None:
-            li, h, q, kp, vp, n, ak, av = pre
             nx.nx_read_device_status(sc.cfg, sc.ws)
             k_post, v_post = sc.live()
             assert sc.n_tokens == min(B, n) + A
-            keep = sc.keep[li]
-            _check_all_keeps(keep, n, B)
-            _check_unit(sc.cfg, wl, q, kp, vp, keep, k_post[li], v_post[li], n, B,
-                        wl.walk_iters, 0, layers[li], step, 0, [h])
             kept = min(B, n)
-            assert torch.equal(k_post[li][:, kept:].view(torch.int16), ak.view(torch.int16))
-            assert torch.equal(v_post[li][:, kept:].view(torch.int16), av.view(torch.int16))
+            jobs = []
+            for li, q, kp, vp, ak, av in pre:
+                keep = sc.keep[li]
+                _check_all_keeps(keep, n, B)
+                _check_rows(keep, k_post[li], v_post[li], kp, vp, kept)
+                qb, kb = bf16_bits(q), bf16_bits(kp)
+                w_h, keep_h = sc.weights(li).cpu().numpy(), keep.cpu().numpy()
+                jobs += [(f"event {step} layer {li} head {h}", qb[h * G:(h + 1) * G], kb[h], B,
+                          wl.walk_iters, 0, layers[li], step, h, w_h[h], keep_h[h, :kept])
+                         for h in range(wl.h_kv)]
+                assert torch.equal(k_post[li][:, kept:].view(torch.int16), ak.view(torch.int16))
+                assert torch.equal(v_post[li][:, kept:].view(torch.int16), av.view(torch.int16))
+            gc.oracle_map(_oracle_unit, jobs)
     nx.nx_read_device_status(sc.cfg, sc.ws)
 
 

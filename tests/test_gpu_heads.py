@@ -68,21 +68,20 @@ def _run_batch(cfg, wl, lay, n, budget, cap, walk, hb_in=None, seed=3):
           torch.tensor(hb_in, dtype=torch.int32, device=DEV))
     k = lay["k"][:, :n].contiguous()
     v = lay["v"][:, :n].contiguous()
+    w_sel = torch.full((H, cfg.units(n)), float("nan"), device=DEV)
     units = nx.make_units([dict(q=lay["q"], k=k, v=v, keep=keep, out_k=out_k, out_v=out_v,
                                 kv_head_stride=n * D, out_head_stride=rows * D, n_tokens=n,
-                                budget=budget, head_cap=cap, head_budget=hb, layer=5)],
+                                budget=budget, head_cap=cap, head_budget=hb, layer=5,
+                                out_w=w_sel)],
                           device=DEV)
     ws = nx.new_workspace(cfg, n, 1, walk, device=DEV)
     nx.nx_evict_batch(cfg, units, 1, n, walk, seed, workspace=ws, step=2, max_out_rows=rows)
     nx.nx_read_device_status(cfg, ws)
-    return k, v, keep, out_k, out_v, hb.cpu().numpy()
+    return k, v, keep, out_k, out_v, hb.cpu().numpy(), w_sel.cpu().numpy()
 
 
-def _check(cfg, wl, lay, k, v, keep, out_k, out_v, budgets, n, walk, seed=3):
-    wcfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=cfg.block)
-    ws = nx.new_workspace(wcfg, n, 1, walk, device=DEV)
-    w_gpu = nx.nx_nexus_weights(wcfg, lay["q"], k, n, walk, workspace=ws).cpu().numpy()
-    nx.nx_read_device_status(wcfg, ws)
+def _check(cfg, wl, lay, k, v, keep, out_k, out_v, budgets, n, walk, w_gpu, seed=3):
+    """w_gpu: the weights the batch exported (its selection's weights)."""
     _, on_gpu_w = nexus.select_from_weights(w_gpu, 0, seed, layer=5, step=2,
                                             head_budgets=budgets)
     qh, dt = gc.host(lay["q"])
@@ -97,7 +96,8 @@ def _check(cfg, wl, lay, k, v, keep, out_k, out_v, budgets, n, walk, seed=3):
         np.testing.assert_array_equal(keep[h, :kept], on_gpu_w[h], err_msg=f"head {h}")
         assert np.all(keep[h, kept:] == -1)
         gc.assert_weights_close(w_gpu[h], ref["w"][h], f"head {h}")
-        assert gc.overlap_fraction(keep[h, :kept], ref["keep"][h]) >= 0.999
+        gc.assert_kept_matches_oracle(keep[h, :kept], ref["keep"][h], ref["keys"][h], kept,
+                                      f"head {h}")
         rows = np.concatenate([np.arange(b * cfg.block, min((b + 1) * cfg.block, n))
                                for b in keep[h, :kept]])
         assert gc.rows_equal(out_k[h], k[h], rows)
@@ -113,9 +113,9 @@ def test_batch_with_given_budgets(n):
     B = n // 5
     cap = 2 * B + n // 2
     given = [B, 1, B // 3, 2 * B, B + 17, cap, 5, B // 2]
-    k, v, keep, ok, ov, hb = _run_batch(cfg, wl, lay, n, B, cap, wl.walk_iters, hb_in=given)
+    k, v, keep, ok, ov, hb, w = _run_batch(cfg, wl, lay, n, B, cap, wl.walk_iters, hb_in=given)
     np.testing.assert_array_equal(hb, given)
-    _check(cfg, wl, lay, k, v, keep, ok, ov, np.array(given), n, wl.walk_iters)
+    _check(cfg, wl, lay, k, v, keep, ok, ov, np.array(given), n, wl.walk_iters, w)
 
 
 @pytest.mark.parametrize("n,floor,cap_mult", [(4096, 0, 2), (4096, 100, 3), (40000, 800, 2),
@@ -126,8 +126,8 @@ def test_batch_with_allocated_budgets(n, floor, cap_mult):
                          head_alloc=nx.NX_HEADS_ALLOC, head_floor=floor)
     B = n // 5
     cap = cap_mult * B
-    k, v, keep, ok, ov, hb = _run_batch(cfg, wl, lay, n, B, cap, wl.walk_iters)
-    w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, wl.walk_iters)
+    k, v, keep, ok, ov, hb, w = _run_batch(cfg, wl, lay, n, B, cap, wl.walk_iters)
+    w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, wl.walk_iters, w)
     np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, floor, cap=cap))
     if cap_mult > 1:
         assert hb.sum() == wl.h_kv * B
@@ -140,8 +140,8 @@ def test_batch_allocated_budgets_with_blocks():
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16, block=b,
                          head_alloc=nx.NX_HEADS_ALLOC, head_floor=4)
     B = 51
-    k, v, keep, ok, ov, hb = _run_batch(cfg, wl, lay, n, B, 3 * B, wl.walk_iters)
-    w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, wl.walk_iters)
+    k, v, keep, ok, ov, hb, w = _run_batch(cfg, wl, lay, n, B, 3 * B, wl.walk_iters)
+    w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, wl.walk_iters, w)
     np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, 4, cap=3 * B))
 
 

@@ -108,6 +108,8 @@ def test_survival_events_teacher_forced(policy):
         k_post, v_post = sc.live()
         cfg = nx.NexusConfig(spec.h_q, spec.h_kv, spec.head_dim, spec.window, n_avg=n_avg)
         ws = nx.new_workspace(cfg, n, 1, walk, device=DEV)
+        # The 16-stream batch and this one-item call both score in 256-token tiles
+        # (too few head units for wider ones), so their fp32 sums run in the same order.
         w_gpu = nx.nx_nexus_weights(cfg, q[s], k[s], n, walk, workspace=ws).cpu().numpy()
         nx.nx_read_device_status(cfg, ws)
         w_ref = gc.oracle_weights(q[s], k[s], n, walk, spec.group, heads=[h])[h]
@@ -118,7 +120,8 @@ def test_survival_events_teacher_forced(policy):
         # pure oracle: its own weights, the same counters (head h of sequence 0)
         ref_keys = nexus.head_keys(w_ref, n, h, s, e, 0, n_avg)
         ref_keep = nexus.select_top(ref_keys, B)
-        assert gc.overlap_fraction(got, ref_keep) >= 0.999
+        gc.assert_kept_matches_oracle(got, ref_keep, ref_keys, B, f"event {e} stream {s} head {h}",
+                                      n_avg=max(n_avg, 1))
         assert gc.rows_equal(k_post[s, h], k[s, h], got)
         assert gc.rows_equal(v_post[s, h], v[s, h], got)
         assert torch.equal(k_post[s, h, B:].view(torch.int16),
