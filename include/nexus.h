@@ -215,6 +215,34 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
                         void* out_k, void* out_v);
 
 /*
+ * nx_evict_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels as nx_evict_step, but desc->workspace / workspace_bytes are
+ * ignored: the scratch is a static device array of NX_SCRATCH_BYTES inside
+ * the library, one per GPU, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipEventCreate; the stage profiler is off for it).
+ * The caller still passes every input and output, as for nx_evict_step.
+ *  - Shapes whose workspace (nx_evict_workspace_bytes with max_units = 1)
+ *    exceeds NX_SCRATCH_BYTES return NX_EWORKSPACE before anything is enqueued
+ *    (16 MiB holds, for example, 8 KV heads x 32768 tokens at walk depth 8).
+ *  - The first call on a device looks up the array's address and clears its
+ *    status word with a small kernel on desc->stream: make it outside graph
+ *    capture.  nx_read_device_status with desc->workspace == NULL reads (and
+ *    clears) that status word on the current device.
+ *  - Every call on one GPU uses the same array, which keeps the last call's
+ *    contents: calls that overlap in time on one GPU (other streams, other
+ *    threads) race and must be serialised by the caller.
+ * Errors: those of nx_evict_step, NX_EWORKSPACE as above, NX_EHIP when the
+ * set-up fails.
+ */
+#define NX_SCRATCH_BYTES (16u << 20)
+
+nx_status nx_evict_step_noalloc(const nx_desc* desc, const void* q_window, const void* k_cache,
+                                const void* v_cache, int32_t n_tokens, int32_t budget,
+                                int32_t walk_iters, uint64_t seed, int32_t* out_keep_idx,
+                                void* out_k, void* out_v);
+
+/*
  * The same event for `n_units` (sequence, layer) items in one launch per stage
  * (all layers of a model, or ragged sequences).  units_dev points to n_units
  * nx_unit records in device memory; desc supplies the shared shape, lambda,
@@ -265,9 +293,10 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
                         void* out_k, void* out_v);
 
 /*
- * Waits for desc->stream, reads and clears the workspace status word.
- * Returns NX_OK, NX_ENONFINITE or NX_EINVAL (a bad batch item), or NX_EHIP if
- * a HIP call failed.
+ * Waits for desc->stream, reads and clears the workspace status word (with
+ * desc->workspace == NULL: the status word of nx_evict_step_noalloc's static
+ * scratch on the current device).  Returns NX_OK, NX_ENONFINITE or NX_EINVAL
+ * (a bad batch item), or NX_EHIP if a HIP call failed.
  */
 nx_status nx_read_device_status(const nx_desc* desc);
 

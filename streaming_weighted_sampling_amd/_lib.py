@@ -19,6 +19,7 @@ NX_HEADS_UNIFORM = 0
 NX_HEADS_GIVEN = 1
 NX_HEADS_ALLOC = 2
 NX_MAX_ALLOC_HEADS = 256
+NX_SCRATCH_BYTES = 16 << 20
 NX_BF16 = 0
 NX_F32 = 1
 
@@ -83,6 +84,8 @@ SIGNATURES = {
     "nx_evict_workspace_bytes": (ctypes.c_size_t, [_P(NxDesc), _I32, _I32, _I32]),
     "nx_evict_step": (_I32, [_P(NxDesc), _VP, _VP, _VP, _I32, _I32, _I32, ctypes.c_uint64,
                              _VP, _VP, _VP]),
+    "nx_evict_step_noalloc": (_I32, [_P(NxDesc), _VP, _VP, _VP, _I32, _I32, _I32, ctypes.c_uint64,
+                                     _VP, _VP, _VP]),
     "nx_evict_batch": (_I32, [_P(NxDesc), _VP, _I32, _I32, _I32, ctypes.c_uint64]),
     "nx_nexus_weights": (_I32, [_P(NxDesc), _VP, _VP, _I32, _I32, _VP]),
     "nx_reservoir_select": (_I32, [_P(NxDesc), _VP, _I32, _I32, ctypes.c_uint64, _VP, _VP]),

@@ -159,6 +159,33 @@ def nx_evict_step(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, workspace
     return keep, out_k, out_v
 
 
+def nx_evict_step_noalloc(cfg, q, k, v, n_tokens, budget, walk_iters, seed, *, out_k, out_v,
+                          keep, layer=0, step=0, seq_id=0, out_w=None, stream=None):
+    """nx_evict_step on the library's static scratch (no workspace, nothing
+    allocated by the call); every output tensor is given by the caller."""
+    kst = _check_cache(cfg, k, "k")
+    if _check_cache(cfg, v, "v") != kst:
+        raise ValueError("k and v must share the head stride")
+    if q.dtype != cfg.dtype or not q.is_contiguous() or \
+            tuple(q.shape) != (cfg.n_q_heads, cfg.window, cfg.head_dim):
+        raise ValueError("q must be a contiguous [n_q_heads, window, head_dim] tensor")
+    ost = 0
+    if not cfg.compact:
+        ost = _check_cache(cfg, out_k, "out_k")
+        if _check_cache(cfg, out_v, "out_v") != ost:
+            raise ValueError("out_k and out_v must share the head stride")
+    if keep.dtype != torch.int32 or not keep.is_contiguous():
+        raise ValueError("keep must be a contiguous int32 tensor")
+    if out_w is not None:
+        _check_weights(cfg, out_w, n_tokens, "out_w")
+    d = cfg.desc(None, layer=layer, step=step, seq_id=seq_id, kv_head_stride=kst,
+                 out_head_stride=ost, stream=stream, out_w=out_w)
+    check(load().nx_evict_step_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), n_tokens,
+                                       budget, walk_iters, seed, _ptr(keep), _ptr(out_k),
+                                       _ptr(out_v)), "nx_evict_step_noalloc")
+    return keep, out_k, out_v
+
+
 def nx_nexus_weights(cfg, q, k, n_tokens, walk_iters, *, workspace, out_w=None, stream=None):
     """Nexus weights w [H_kv, units] fp32 (units = n_tokens, or blocks)."""
     kst = _check_cache(cfg, k, "k")
@@ -241,7 +268,8 @@ def nx_evict_batch(cfg, units_dev, n_units, max_tokens, walk_iters, seed, *, wor
 
 
 def nx_read_device_status(cfg, workspace, stream=None):
-    """Synchronises the stream and raises NexusError on a recorded device error."""
+    """Synchronises the stream and raises NexusError on a recorded device error
+    (workspace None: the status of nx_evict_step_noalloc calls on this device)."""
     d = cfg.desc(workspace, stream=stream)
     check(load().nx_read_device_status(ctypes.byref(d)), "device status")
 

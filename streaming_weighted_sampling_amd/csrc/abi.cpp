@@ -156,9 +156,9 @@ struct Profiler {
 Profiler& prof() { static Profiler p; return p; }
 
 template <typename F>
-hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
+hipError_t run_stage(int stage, hipStream_t s, F&& launch, bool profile = true) {
   Profiler& p = prof();
-  if (!((p.mask >> stage) & 1u)) return launch();
+  if (!profile || !((p.mask >> stage) & 1u)) return launch();
   std::lock_guard<std::mutex> lock(p.mu);
   hipEvent_t e0 = p.get(), e1 = p.get();
   if (e0) (void)hipEventRecord(e0, s);
@@ -173,8 +173,12 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch) {
 // + sample_select; held in the select kernel's registers up to
 // kFusedMaxTokens) when the call goes on to selection (not the weights-only
 // export): n >= 1 draws per token, or the top-B-by-weight limit.
-nx_status enqueue(const Args& a, hipStream_t s, int first, int last) {
+// profile = false keeps the HIP-event profiler (which creates events) out of the call.
+nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profile = true) {
   hipError_t err = hipSuccess;
+  auto run_stage = [profile](int stage, hipStream_t st, auto&& launch) {
+    return ::run_stage(stage, st, launch, profile);
+  };
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
   const bool fused = max_units <= kWideMaxTokens && !a.stop_after_weights &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
@@ -245,6 +249,39 @@ nx_unit single_unit(const nx_desc* d, const void* q, const void* k, const void* 
   return u;
 }
 
+// ---- the no-allocation variant of nx_evict_step ----
+// Its workspace is this file-scope device array, one copy per GPU that the
+// library runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current, and
+// only that address is ever handed to kernels or copies.
+constexpr size_t kScratchBytes = size_t(NX_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+__global__ __launch_bounds__(64) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
+// Device address of this device's scratch array (nullptr on a HIP error).  The
+// first call on a device looks it up and clears the status word with a fill
+// kernel on `s`; every later call returns the cached address.
+void* scratch_ptr(hipStream_t s) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, s, static_cast<uint32_t*>(p), 64);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,9 +293,10 @@ size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t
   return ws_layout(g).total;
 }
 
-nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,
-                        const void* v_cache, int32_t n_tokens, int32_t budget, int32_t walk_iters,
-                        uint64_t seed, int32_t* out_keep_idx, void* out_k, void* out_v) {
+static nx_status evict_step_impl(const nx_desc* desc, const void* q_window, const void* k_cache,
+                                 const void* v_cache, int32_t n_tokens, int32_t budget,
+                                 int32_t walk_iters, uint64_t seed, int32_t* out_keep_idx,
+                                 void* out_k, void* out_v, bool profile) {
   Geometry g{};
   nx_status st = make_geometry(desc, n_tokens, 1, walk_iters, &g);
   if (st != NX_OK) return st;
@@ -309,7 +347,31 @@ nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k
   Args a = base_args(desc, g, seed);
   if ((st = bind_workspace(desc, g, &a)) != NX_OK) return st;
   a.single = u;
-  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageKvCompact);
+  return enqueue(a, static_cast<hipStream_t>(desc->stream), kStageScoreStats, kStageKvCompact,
+                 profile);
+}
+
+nx_status nx_evict_step(const nx_desc* desc, const void* q_window, const void* k_cache,
+                        const void* v_cache, int32_t n_tokens, int32_t budget, int32_t walk_iters,
+                        uint64_t seed, int32_t* out_keep_idx, void* out_k, void* out_v) {
+  return evict_step_impl(desc, q_window, k_cache, v_cache, n_tokens, budget, walk_iters, seed,
+                         out_keep_idx, out_k, out_v, true);
+}
+
+nx_status nx_evict_step_noalloc(const nx_desc* desc, const void* q_window, const void* k_cache,
+                                const void* v_cache, int32_t n_tokens, int32_t budget,
+                                int32_t walk_iters, uint64_t seed, int32_t* out_keep_idx,
+                                void* out_k, void* out_v) {
+  if (desc == nullptr) return NX_EINVAL;
+  void* ws = scratch_ptr(static_cast<hipStream_t>(desc->stream));
+  if (ws == nullptr) return NX_EHIP;
+  nx_desc d = *desc;
+  d.workspace = ws;
+  d.workspace_bytes = kScratchBytes;
+  // The shape's workspace must fit the static scratch: NX_EWORKSPACE otherwise
+  // (bind_workspace), before anything is enqueued.
+  return evict_step_impl(&d, q_window, k_cache, v_cache, n_tokens, budget, walk_iters, seed,
+                         out_keep_idx, out_k, out_v, false);
 }
 
 nx_status nx_evict_batch(const nx_desc* desc, const nx_unit* units_dev, int32_t n_units,
@@ -428,16 +490,21 @@ nx_status nx_kv_compact(const nx_desc* desc, const void* k_cache, const void* v_
 }
 
 nx_status nx_read_device_status(const nx_desc* desc) {
-  if (desc == nullptr || desc->workspace == nullptr || desc->workspace_bytes < 256) return NX_EINVAL;
+  if (desc == nullptr) return NX_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(desc->stream);
+  void* ws = desc->workspace;
+  if (ws == nullptr) {
+    ws = scratch_ptr(s);   // the status of nx_evict_step_noalloc calls on this device
+    if (ws == nullptr) return NX_EHIP;
+  } else if (desc->workspace_bytes < 256) {
+    return NX_EINVAL;
+  }
   if (hipStreamSynchronize(s) != hipSuccess) return NX_EHIP;
   uint32_t word = 0;
-  if (hipMemcpy(&word, desc->workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
-    return NX_EHIP;
+  if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return NX_EHIP;
   if (word != 0) {
     const uint32_t zero = 0;
-    if (hipMemcpy(desc->workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
-      return NX_EHIP;
+    if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return NX_EHIP;
   }
   if (word & kStatusNonFinite) return NX_ENONFINITE;
   if (word & kStatusBadItem) return NX_EINVAL;

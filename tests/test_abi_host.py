@@ -184,3 +184,14 @@ def test_stage_entry_points_validate(lib):
     wide = _desc(head_alloc=_lib.NX_HEADS_ALLOC, n_q_heads=512, n_kv_heads=512)
     assert lib.nx_head_budgets(ctypes.byref(wide), FAKE, 4096, 10, 0, FAKE) == \
         _lib.NX_EUNSUPPORTED
+
+
+def test_static_scratch_holds_the_stated_shape(lib):
+    """The no-allocation entry point's scratch covers 8 KV heads x 32768 tokens at
+    walk depth 8 (the header's example), and that call rejects larger shapes
+    before any launch (no GPU is touched: validation fails first)."""
+    d = _desc(window=32)
+    assert lib.nx_evict_workspace_bytes(ctypes.byref(d), 32768, 1, 8) <= _lib.NX_SCRATCH_BYTES
+    assert lib.nx_evict_workspace_bytes(ctypes.byref(d), 131072, 1, 3) > _lib.NX_SCRATCH_BYTES
+    assert lib.nx_evict_step_noalloc(None, FAKE, FAKE, FAKE, 4096, 819, 3, 0, FAKE, FAKE,
+                                     FAKE) == _lib.NX_EINVAL
