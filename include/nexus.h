@@ -307,7 +307,8 @@ const char* nx_status_str(nx_status status);
  * Read-bandwidth probe (a measurement aid, not part of an eviction event): reads
  * `bytes` bytes at `src` (device memory, 16-B aligned, bytes a multiple of 256)
  * `passes` times, one kernel launch per pass, on `stream` (a hipStream_t), with
- * the score sweeps' access pattern: 256-B rows, 512 KB per workgroup.
+ * the score sweeps' access pattern: 256-B rows, up to 512 KB per workgroup (less for
+ * small buffers, which still get >= 2048 workgroups when they hold >= 64K rows).
  *   mode 0: global -> LDS copies through the sweeps' ring of LDS slots
  *   mode 1: plain 16-byte vector loads into registers
  * sink: >= 1 KB of device memory that the kernels may write (it keeps the loads

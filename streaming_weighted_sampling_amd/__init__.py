@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     NX_OK, NX_EINVAL, NX_EALIAS, NX_EWORKSPACE, NX_EUNSUPPORTED, NX_ENONFINITE, NX_EHIP,
     NX_BF16, NX_F32, NX_COMPACT_COPY, NX_COMPACT_INPLACE, NX_HEADS_UNIFORM, NX_HEADS_GIVEN,
     NX_HEADS_ALLOC, NX_MAX_ALLOC_HEADS, NX_SCRATCH_BYTES, NxDesc, NxUnit, NexusError, LIB_PATH,
-    load, status_str,
+    load, status_str, check,
 )
 from .api import (  # noqa: F401
     NexusConfig, TOPK, workspace_bytes, new_workspace, nx_evict_step, nx_evict_step_noalloc, nx_nexus_weights,

@@ -801,8 +801,8 @@ hipError_t launch_pass(const Args& a, hipStream_t s) {
 // Read-ceiling probe (measurement only): streams a buffer the way the score
 // sweeps stream K.  The buffer is cut into "heads" of up to 2^22 rows of 256 B
 // (1 GiB, so 32-bit buffer offsets address them); one workgroup reads
-// kProbeRows consecutive rows, the same span as a score workgroup at 2048
-// tokens.  Mode 0 copies through the sweeps' LDS ring (global -> LDS, four
+// `span` consecutive rows: 2048 (a score workgroup at 2048 tokens) for large
+// buffers, fewer for small ones so that every buffer gets >= 2048 workgroups.  Mode 0 copies through the sweeps' LDS ring (global -> LDS, four
 // slots of 8 KB, every wavefront a loader) and reads each slot back as MFMA
 // fragments; mode 1 issues plain 16-B vector loads, eight in flight per lane.
 // Every value read is folded into an XOR that is stored only if it equals an
@@ -812,12 +812,12 @@ constexpr int64_t kProbeHeadRows = int64_t(1) << 22;
 
 template <int kMode>
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, int64_t rows,
-                                                               uint32_t* sink) {
+                                                               int span, uint32_t* sink) {
   using GE = Geo<uint16_t, 128>;
   __shared__ __align__(16) char smem[GE::kSlotsStats * GE::kTileBytes];
   const int64_t head_row0 = int64_t(blockIdx.y) * kProbeHeadRows;
   const int64_t head_rows = min(kProbeHeadRows, rows - head_row0);
-  const int t0 = int(blockIdx.x) * kProbeRows;
+  const int t0 = int(blockIdx.x) * span;
   if (t0 >= head_rows) return;
   const int n = int(head_rows);
   const char* base = src + head_row0 * GE::kRowBytes;
@@ -827,7 +827,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, 
     HeadUnit u{};
     u.k = base;
     u.n = n;
-    const int n_sub = (min(t0 + kProbeRows, n) - t0 + 31) / 32;
+    const int n_sub = (min(t0 + span, n) - t0 + 31) / 32;
     sweep_tiles<uint16_t, 128, GE::kSlotsStats, kWaves, kWaves>(u, t0, n_sub, smem, wave, false,
                                                                 [&](int, const char* cur) {
       uint4 kf[GE::kChunks];
@@ -836,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* src, 
       for (int c = 0; c < GE::kChunks; ++c) acc ^= kf[c].x ^ kf[c].y ^ kf[c].z ^ kf[c].w;
     });
   } else {
-    const int t1 = min(t0 + kProbeRows, n);
+    const int t1 = min(t0 + span, n);
     const Buf b(base + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes));
     const uint32_t bytes = uint32_t((t1 - t0) * GE::kRowBytes);
     constexpr int kInFlight = 8;
@@ -866,13 +866,15 @@ hipError_t launch_stream_read(const void* src, int64_t rows, int mode, uint32_t*
                               hipStream_t s) {
   const int64_t heads = (rows + kProbeHeadRows - 1) / kProbeHeadRows;
   const int64_t per_head = rows < kProbeHeadRows ? rows : kProbeHeadRows;
-  const dim3 grid(unsigned((per_head + kProbeRows - 1) / kProbeRows), unsigned(heads));
+  int span = kProbeRows;
+  while (span > 32 && rows / span < 2048) span /= 2;
+  const dim3 grid(unsigned((per_head + span - 1) / span), unsigned(heads));
   if (mode == 0)
     hipLaunchKernelGGL(stream_read_kernel<0>, grid, dim3(kThreads), 0, s,
-                       static_cast<const char*>(src), rows, sink);
+                       static_cast<const char*>(src), rows, span, sink);
   else
     hipLaunchKernelGGL(stream_read_kernel<1>, grid, dim3(kThreads), 0, s,
-                       static_cast<const char*>(src), rows, sink);
+                       static_cast<const char*>(src), rows, span, sink);
   return hipGetLastError();
 }
 
