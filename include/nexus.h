@@ -37,6 +37,12 @@
  *    [kept, head_dim] rows, kept = min(budget, n_tokens).
  *  - Element types: NX_BF16 (bfloat16) or NX_F32, shared by Q, K, V and the
  *    outputs; head_dim 64 or 128.
+ *  - Debugging: with the environment variable NX_DEBUG set to a non-empty value
+ *    other than "0" (read at every call), each call is synchronous -- after
+ *    every kernel stage the stream is synchronised and the HIP error state and
+ *    the device status word are checked; the first failure is returned by the
+ *    call itself (NX_EHIP, NX_ENONFINITE, NX_EINVAL) and the stage named on
+ *    stderr.  The checks are skipped while desc->stream is being captured.
  */
 #ifndef NEXUS_H
 #define NEXUS_H
@@ -107,8 +113,10 @@ typedef struct nx_desc {
                                rows at or past position kept move, the j-th of them
                                (ascending) into the j-th evicted slot below kept, and the
                                appended rows go to kept, kept + 1, ...; out_k / out_v must be
-                               NULL and kv_head_stride must hold kept + n_append rows; tokens
-                               only (block <= 1).  Other values: NX_EINVAL. */
+                               NULL and kv_head_stride must hold kept + n_append rows.  With
+                               blocks the same holds for the kept blocks' rows (row i of the
+                               kept rows is row i % b of block keep[i / b]), so aligned blocks
+                               move whole.  Other values: NX_EINVAL. */
   int32_t head_alloc;       /* per-head budgets (appendix 10: a layer budget shared unevenly by
                                the heads), nx_evict_batch and nx_head_budgets only:
                                NX_HEADS_UNIFORM (0): every head keeps min(budget, units).

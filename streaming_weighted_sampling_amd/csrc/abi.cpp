@@ -5,6 +5,8 @@
 // Eviction Under Fixed Budgets" (academ.us article page).
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -32,7 +34,6 @@ nx_status check_desc(const nx_desc* d) {
   if (d->compact != NX_COMPACT_COPY && d->compact != NX_COMPACT_INPLACE) return NX_EINVAL;
   if (d->head_alloc < NX_HEADS_UNIFORM || d->head_alloc > NX_HEADS_ALLOC || d->head_floor < 0)
     return NX_EINVAL;
-  if (d->compact == NX_COMPACT_INPLACE && d->block > 1) return NX_EUNSUPPORTED;
   if (d->block > 1 && (d->block > 32 || (d->block & (d->block - 1)) != 0)) return NX_EUNSUPPORTED;
   if (d->dtype != NX_BF16 && d->dtype != NX_F32) return NX_EUNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return NX_EUNSUPPORTED;
@@ -168,6 +169,38 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch, bool profile = true) 
   return err;
 }
 
+// NX_DEBUG (environment, read at every call): a non-empty value other than
+// "0" makes each call synchronous -- after every stage the stream is
+// synchronised, the HIP error state and the device status word are checked,
+// and the first failure is returned by the entry point itself (the stage is
+// named on stderr).  Skipped while the stream is being captured into a graph.
+bool debug_mode() {
+  const char* e = std::getenv("NX_DEBUG");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+nx_status debug_check(const Args& a, hipStream_t s, int stage) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return NX_EHIP;
+  if (cap != hipStreamCaptureStatusNone) return NX_OK;
+  const char* name = nx_stage_name(stage);
+  hipError_t err = hipStreamSynchronize(s);
+  if (err == hipSuccess) err = hipGetLastError();
+  if (err != hipSuccess) {
+    std::fprintf(stderr, "nexus debug: stage %s: %s\n", name, hipGetErrorString(err));
+    return NX_EHIP;
+  }
+  uint32_t word = 0;
+  if (a.status != nullptr &&
+      hipMemcpy(&word, a.status, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return NX_EHIP;
+  const nx_status st = (word & kStatusNonFinite) ? NX_ENONFINITE
+                       : (word & kStatusBadItem) ? NX_EINVAL
+                                                 : NX_OK;
+  if (st != NX_OK) std::fprintf(stderr, "nexus debug: stage %s: %s\n", name, nx_status_str(st));
+  return st;
+}
+
 // Enqueue stages [first, last] in order.
 // Items of up to kWideMaxTokens units select on estimate codes (estimate_keys
 // + sample_select; held in the select kernel's registers up to
@@ -176,6 +209,7 @@ hipError_t run_stage(int stage, hipStream_t s, F&& launch, bool profile = true) 
 // profile = false keeps the HIP-event profiler (which creates events) out of the call.
 nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profile = true) {
   hipError_t err = hipSuccess;
+  const bool debug = debug_mode();
   auto run_stage = [profile](int stage, hipStream_t st, auto&& launch) {
     return ::run_stage(stage, st, launch, profile);
   };
@@ -224,6 +258,10 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profil
       case kStageKvCompact: err = run_stage(st, s, [&] { return launch_kv_compact(live, s); }); break;
       case kStageHeadBudget: err = run_stage(st, s, [&] { return launch_head_budget(a, s); }); break;
       default: break;
+    }
+    if (err == hipSuccess && debug) {
+      const nx_status dst = debug_check(a, s, st);
+      if (dst != NX_OK) return dst;
     }
   }
   return err == hipSuccess ? NX_OK : NX_EHIP;

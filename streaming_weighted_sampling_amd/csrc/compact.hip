@@ -85,7 +85,10 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
 }
 
 // In-place compaction (hole filling) for streaming.  With kept rows in
-// ascending keep[0..kept), let c = #{keep[i] < kept}: rows keep[c..kept) are
+// ascending keep[0..kept) (with blocks of b tokens: the kept blocks' rows,
+// row i = keep[i / b] * b + i % b, kept = the kept rows; hole filling at row
+// level moves whole aligned blocks whenever kept is a multiple of b, and a
+// short last block splits no other block), let c = #{keep[i] < kept}: rows keep[c..kept) are
 // the movers (kept rows at or past position kept) and the evicted positions
 // below kept are the holes, equally many.  The j-th mover goes to the j-th
 // hole; since keep[i] - i counts the holes before keep[i], the j-th hole is
@@ -102,10 +105,9 @@ constexpr int kLdsKeep = 12288;   // keep entries staged in LDS for the searches
 // pointer (a flat access whose base register lies outside the LDS aperture
 // faults even when the immediate offset would bring it back inside).
 template <int kRowBytes, typename Keep>
-__device__ __forceinline__ bool fill_holes(const HeadUnit& u, Keep keep) {
+__device__ __forceinline__ bool fill_holes(const HeadUnit& u, int kept, Keep keep) {
   constexpr int kPerRow = kRowBytes / 16;
   constexpr int kRowsPerPass = kThreads / kPerRow;
-  const int kept = u.kept;
   // c = #{keep[i] < kept}: the entries are ascending, so a binary search.
   int lo = 0, hi = kept;
   while (lo < hi) {
@@ -148,19 +150,26 @@ __global__ __launch_bounds__(kThreads) void kv_fill_holes_kernel(const Args a) {
   const int hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid || u.keep == nullptr) return;
-  const int kept = u.kept;
+  const int b = a.g.block;
+  const int kept = min(u.kept * b, u.n);   // kept rows
   // Movers are kept rows at or past kept, so at most n - kept of them; the
   // whole workgroup leaves together.
   if (int(blockIdx.x) * kCompactRows >= u.n - kept) return;
   bool bad;
-  if (kept <= kLdsKeep) {
+  if (u.kept <= kLdsKeep) {
     // The searches read the keep array many times: stage it in LDS once.
-    for (int i = threadIdx.x; i < kept; i += kThreads) s_keep[i] = u.keep[i];
+    for (int i = threadIdx.x; i < u.kept; i += kThreads) s_keep[i] = u.keep[i];
     __syncthreads();
-    bad = fill_holes<kRowBytes>(u, [](int i) { return s_keep[i]; });
+    if (b == 1)
+      bad = fill_holes<kRowBytes>(u, kept, [](int i) { return s_keep[i]; });
+    else
+      bad = fill_holes<kRowBytes>(u, kept, [b](int i) { return s_keep[i / b] * b + (i & (b - 1)); });
   } else {
     const int32_t* keep = u.keep;
-    bad = fill_holes<kRowBytes>(u, [keep](int i) { return keep[i]; });
+    if (b == 1)
+      bad = fill_holes<kRowBytes>(u, kept, [keep](int i) { return keep[i]; });
+    else
+      bad = fill_holes<kRowBytes>(u, kept, [keep, b](int i) { return keep[i / b] * b + (i & (b - 1)); });
   }
   if (__syncthreads_or(bad) && threadIdx.x == 0) raise_status(a, kStatusBadItem);
 }
@@ -172,7 +181,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
   const int hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (!u.valid || u.keep == nullptr || u.n_append == 0) return;
-  const uint32_t head_bytes = uint32_t(u.kept + u.n_append) * kRowBytes;
+  // Appended rows follow the kept rows (with blocks, n % b == 0 then holds).
+  const int kept = min(u.kept * a.g.block, u.n);
+  const uint32_t head_bytes = uint32_t(kept + u.n_append) * kRowBytes;
   const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
   const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);
   const Buf kab(u.app_k, app_bytes), vab(u.app_v, app_bytes);
@@ -182,8 +193,8 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
       const uint32_t off = uint32_t((r0 + r) * kRowBytes + 16 * col);
       const uint4 xk = kab.ld16<kNonTemporal>(off);
       const uint4 xv = vab.ld16<kNonTemporal>(off);
-      kb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xk);
-      vb.st16<kNonTemporal>(uint32_t(u.kept * kRowBytes) + off, xv);
+      kb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xk);
+      vb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xv);
     }
   }
 }

@@ -58,6 +58,21 @@ struct LdsDma {
                 __builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32) & 0xFFFF)),
                 __builtin_amdgcn_readfirstlane(int(bytes)), kRsrcWord3};
   }
+  // The same copy with the hint fixed at compile time (no branch per copy).
+  template <bool kNT>
+  __device__ void load16_t(uint32_t lds_addr, uint32_t voff) const {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    if constexpr (kNT)
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(r)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+  }
   // lds_addr: wave-uniform LDS byte address of this wavefront's 1 KB block.
   __device__ void load16(uint32_t lds_addr, uint32_t voff) const {
 #pragma clang diagnostic push

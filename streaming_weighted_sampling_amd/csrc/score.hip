@@ -161,15 +161,15 @@ __device__ inline floatx16_t mfma_tile(const uint4 (&qf)[Geo<T, D>::kChunks],
 // barrier (everyone's copies landed, everyone is done with the slot about to
 // be refilled), refill, body(st, lds).  Rows past the cache end read as zero.
 // Ends on a barrier.
-template <typename T, int D, int kSlots, int kLoaders, int NW, typename Body>
-__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role, bool nt,
-                                   Body&& body) {
+template <typename T, int D, int kSlots, int kLoaders, int NW, bool kNT, typename Body>
+__device__ inline void sweep_tiles_impl(const HeadUnit& u, int t0, int n_sub, char* ring, int role,
+                                        Body&& body) {
   using GE = Geo<T, D>;
   constexpr int kPerWave = GE::kTileBytes / (1024 * kLoaders);   // copies per loader per tile
   static_assert(kPerWave >= 1 && kPerWave * 1024 * kLoaders == GE::kTileBytes, "tile split");
   static_assert((kSlots - 2) * kPerWave < 64, "vmcnt range");
   const int t1 = min(t0 + 32 * n_sub, u.n);
-  const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes), nt);
+  const LdsDma dma(u.k + int64_t(t0) * GE::kRowBytes, uint32_t((t1 - t0) * GE::kRowBytes), kNT);
   const int lw = role - (NW - kLoaders);   // loader index, < 0: not a loader
   const bool loader = lw >= 0;
   const int lane = threadIdx.x & 63;
@@ -187,7 +187,7 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* r
     const uint32_t dst = ring_lds + uint32_t((st % kSlots) * GE::kTileBytes);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
-      dma.load16(dst + uint32_t(i * kLoaders * 1024), voff[i] + uint32_t(st * GE::kTileBytes));
+      dma.template load16_t<kNT>(dst + uint32_t(i * kLoaders * 1024), voff[i] + uint32_t(st * GE::kTileBytes));
   };
 #pragma unroll
   for (int r = 0; r < kSlots - 1; ++r)
@@ -209,6 +209,17 @@ __device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* r
     body(st, ring + (st % kSlots) * GE::kTileBytes);
   }
   __syncthreads();
+}
+
+// The sweep, unswitched on the non-temporal hint of the K copies (wave-uniform):
+// the copy issue inside the loop then carries no branch.
+template <typename T, int D, int kSlots, int kLoaders, int NW, typename Body>
+__device__ inline void sweep_tiles(const HeadUnit& u, int t0, int n_sub, char* ring, int role, bool nt,
+                                   Body&& body) {
+  if (nt)
+    sweep_tiles_impl<T, D, kSlots, kLoaders, NW, true>(u, t0, n_sub, ring, role, body);
+  else
+    sweep_tiles_impl<T, D, kSlots, kLoaders, NW, false>(u, t0, n_sub, ring, role, body);
 }
 
 // Pass 1 over the block's tokens.  kExact = false keeps one shift per row (the
@@ -378,6 +389,8 @@ constexpr int kWalkLds = 3;     // any other shape: walk rows through LDS
 constexpr int kWalkFast4Deep = 4;   // G = 4, 6 < H <= 8
 constexpr int kWalkFast4Mid = 5;    // G = 4, 4 < H <= 6 (fewer Gram pairs per lane than Deep,
                                     // which keeps the kernel within 128 VGPRs)
+constexpr int kWalkFast4H3 = 6;     // G = 4, H = 3 exactly (no per-row depth tests)
+constexpr int kWalkFast8H3 = 7;     // G = 8, H = 3 exactly
 
 // Pass 2 on one (head unit, tile) item.
 //
@@ -413,9 +426,12 @@ template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   constexpr bool kHasWalk = kWalk != kWalkNone;
+  constexpr int kExactH = kWalk == kWalkFast4H3 || kWalk == kWalkFast8H3 ? 3 : 0;
+  constexpr bool kG8 = kWalk == kWalkFast8 || kWalk == kWalkFast8H3;   // walk rows span 8 output rows
   constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep ||
-                             kWalk == kWalkFast4Mid;
-  constexpr int kMaxT = kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4
+                             kWalk == kWalkFast4Mid || kExactH > 0;
+  constexpr int kMaxT = kExactH > 0                                ? kExactH
+                        : kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4
                         : kWalk == kWalkFast4Mid                   ? 6
                                                                    : kMaxWalk;   // deepest walk
   constexpr int kHalfWaves = 2 * NW;
@@ -435,7 +451,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   const int n_mt = g.rows_pad / 32;
   const int row_roles = min(n_mt, NW);
   const float c = a.c_log2;
-  const int walk = min(g.walk, kMaxT);          // == g.walk for the mode the host picked
+  // == g.walk for the mode the host picked (a constant for the exact-depth modes)
+  const int walk = kExactH > 0 ? kExactH : min(g.walk, kMaxT);
   const int n_pairs = walk * (walk + 1) / 2;
   const int pg = kHalfWaves - 1 - (2 * role + hh);   // first Gram pair of this half-wave
 
@@ -648,7 +665,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
               float pt[kMaxT];
 #pragma unroll
               for (int t = 0; t < kMaxT; ++t)
-                pt[t] = wf * (kWalk != kWalkFast8 ? grp[t] : grp[2 * t] + grp[2 * t + 1]);
+                pt[t] = wf * (!kG8 ? grp[t] : grp[2 * t] + grp[2 * t + 1]);
               put_walk(st, pt);
             }
           }
@@ -735,6 +752,8 @@ void score_probs_kernel(const Args a) {
 
 int walk_mode(const Geometry& g) {
   if (g.walk == 0) return kWalkNone;
+  if (g.walk == 3 && g.group == 4) return kWalkFast4H3;
+  if (g.walk == 3 && g.group == 8) return kWalkFast8H3;
   if (g.walk <= 4 && g.group == 4) return kWalkFast4;
   if (g.walk <= 4 && g.group == 8) return kWalkFast8;
   if (g.walk <= 6 && g.group == 4) return kWalkFast4Mid;
@@ -757,6 +776,12 @@ void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
       break;
     case kWalkFast8:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast8, kBlocks>), grid, dim3(64 * NW), 0, s, a);
+      break;
+    case kWalkFast4H3:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4H3, kBlocks>), grid, dim3(64 * NW), 0, s, a);
+      break;
+    case kWalkFast8H3:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast8H3, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkFast4Deep:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4Deep, kBlocks>), grid, dim3(64 * NW), 0, s, a);

@@ -487,6 +487,95 @@ def test_inplace_streaming_events_match_oracle():
                                               exp_v[:B + A])
 
 
+def _block_rows(blocks, b, n):
+    return np.concatenate([np.arange(k * b, min(k * b + b, n)) for k in blocks])
+
+
+@pytest.mark.parametrize("block,n", [(32, 4096), (32, 4001), (8, 1000)])
+def test_inplace_blocks_step_matches_copy_and_oracle_layout(block, n):
+    """In-place compaction of kept blocks (a short last block when b does not
+    divide N): the same kept blocks and weights as the copy mode, and the caches
+    afterwards equal the oracle's hole filling of the kept blocks' rows."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    d = gen_layer(wl, device=DEV, n_tokens=n)
+    cfg_copy = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=block)
+    cfg_in = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=block, compact=nx.NX_COMPACT_INPLACE)
+    nu = cfg_copy.units(n)
+    B = max(1, round(nu / 5))
+    ws = _ws(cfg_copy, n, 1, wl.walk_iters)
+    w_c = torch.empty(wl.h_kv, nu, device=DEV)
+    w_i = torch.empty_like(w_c)
+    keep_c, ok, ov = nx.nx_evict_step(cfg_copy, d["q"], d["k"], d["v"], n, B, wl.walk_iters, 3,
+                                      workspace=ws, layer=2, step=1, out_w=w_c)
+    k_in, v_in = d["k"].clone(), d["v"].clone()
+    keep_i, k_out, v_out = nx.nx_evict_step(cfg_in, d["q"], k_in, v_in, n, B, wl.walk_iters, 3,
+                                            workspace=ws, layer=2, step=1, out_w=w_i)
+    nx.nx_read_device_status(cfg_in, ws)
+    assert k_out.data_ptr() == k_in.data_ptr()
+    assert torch.equal(keep_c, keep_i)
+    assert torch.equal(w_c.view(torch.int32), w_i.view(torch.int32))
+    kh = d["k"].view(torch.int16).cpu().numpy()
+    vh = d["v"].view(torch.int16).cpu().numpy()
+    kept_rows = cfg_in.kept_rows(n, B)
+    for h in range(wl.h_kv):
+        rows = _block_rows(keep_i[h].cpu().numpy(), block, n)
+        assert len(rows) == kept_rows
+        exp_k = nexus.compact_inplace(kh[h], rows)
+        exp_v = nexus.compact_inplace(vh[h], rows)
+        np.testing.assert_array_equal(k_in[h].view(torch.int16).cpu().numpy()[:kept_rows], exp_k[:kept_rows])
+        np.testing.assert_array_equal(v_in[h].view(torch.int16).cpu().numpy()[:kept_rows], exp_v[:kept_rows])
+        pos = nexus.inplace_layout(rows, n)
+        np.testing.assert_array_equal(exp_k[pos], ok[h][:kept_rows].view(torch.int16).cpu().numpy())
+
+
+def test_inplace_blocks_streaming_events_match_oracle():
+    """Four append-256 / evict-to-26-blocks events with blocks of 32, in place,
+    on two layers: each event's kept blocks equal the oracle's selection on the
+    exported block weights and share the stated bar with the pure oracle, and
+    the cache equals the oracle's hole filling with the new rows after it."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    wl = WORKLOADS["llama3_8b_layer"]
+    b = 32
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=b)
+    L, A, B, n0 = 2, 256, 26, 4096
+    sc = StreamingCache(cfg, L, n0, B, A, wl.walk_iters, seed=12, device=DEV, inplace=True,
+                        export_w=True)
+    g = torch.Generator(device="cpu").manual_seed(21)
+    k0 = torch.randn(L, wl.h_kv, n0, wl.head_dim, generator=g).to(torch.bfloat16).to(DEV)
+    v0 = torch.randn(L, wl.h_kv, n0, wl.head_dim, generator=g).to(torch.bfloat16).to(DEV)
+    sc.load(k0, v0, n0)
+    for step in range(4):
+        sc.q.copy_(torch.randn(sc.q.shape, generator=g).to(torch.bfloat16))
+        sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g).to(torch.bfloat16))
+        sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g).to(torch.bfloat16))
+        kp, vp = (t.clone() for t in sc.live())
+        n_pre = sc.n_tokens
+        sc.step()
+        nx.nx_read_device_status(sc.cfg, sc.ws)
+        assert sc.n_tokens == B * b + A
+        kl, vl = sc.live()
+        for l in range(L):
+            keep = sc.keep[l].cpu().numpy()
+            w_gpu = sc.weights(l).cpu().numpy()
+            qh, dt = gc.host(sc.q[l])
+            kh, _ = gc.host(kp[l])
+            vh, _ = gc.host(vp[l])
+            ref = nexus.evict_step(qh, kh, vh, B, wl.walk_iters, 12, dtype=dt, layer=l, step=step,
+                                   block=b)
+            _, on_gpu_w = nexus.select_from_weights(w_gpu, B, 12, layer=l, step=step)
+            for h in range(wl.h_kv):
+                gc.assert_weights_close(w_gpu[h], ref["w"][h], f"step {step} layer {l} head {h}")
+                np.testing.assert_array_equal(keep[h], on_gpu_w[h])
+                gc.assert_kept_matches_oracle(keep[h], ref["keep"][h], ref["keys"][h], B,
+                                              f"step {step} layer {l} head {h}")
+                rows = _block_rows(keep[h], b, n_pre)
+                for src, dst, app in ((kp, kl, sc.app_k), (vp, vl, sc.app_v)):
+                    exp = nexus.compact_inplace(src[l, h].view(torch.int16).cpu().numpy(), rows,
+                                                app[l, h].view(torch.int16).cpu().numpy())
+                    np.testing.assert_array_equal(dst[l, h].view(torch.int16).cpu().numpy(),
+                                                  exp[:B * b + A])
+
+
 # --------------------------------------------------------------- compaction --
 
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 64)])

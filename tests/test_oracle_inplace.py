@@ -11,6 +11,7 @@ enumeration on tiny caches.
 import itertools
 
 import numpy as np
+import pytest
 
 from oracle import nexus
 
@@ -72,3 +73,33 @@ def test_brute_force_tiny():
             for i in keep:
                 if i < kept:
                     assert out[i, 0] == rows[i, 0]
+
+
+def _block_rows(blocks, b, n):
+    return np.concatenate([np.arange(k * b, min(k * b + b, n)) for k in blocks]).astype(np.int64)
+
+
+@pytest.mark.parametrize("n,b,seed", [(4096, 32, 1), (1088, 32, 2), (100, 32, 3), (4001, 16, 4),
+                                      (257, 8, 5)])
+def test_block_hole_filling_moves_aligned_blocks_whole(n, b, seed):
+    """With blocks the kept rows are the kept blocks' rows; row-level hole
+    filling then moves every aligned block whole: each kept block lands as b
+    consecutive rows starting at a multiple of b (a short last block, if kept,
+    lands on consecutive rows too)."""
+    rng = np.random.default_rng(seed)
+    nu = -(-n // b)
+    blocks = np.sort(rng.choice(nu, size=max(1, nu // 4), replace=False))
+    rows = _block_rows(blocks, b, n)
+    cache = np.arange(n)[:, None] * 10 + np.arange(3)[None, :]
+    out = nexus.compact_inplace(cache, rows)
+    kept = len(rows)
+    got_rows = out[:kept, 0] // 10                # which original row sits in each slot
+    assert sorted(got_rows.tolist()) == rows.tolist()
+    full = [k for k in blocks if k * b + b <= n]
+    for k in full:
+        pos = np.flatnonzero(got_rows == k * b)
+        assert len(pos) == 1
+        p = int(pos[0])
+        if kept % b == 0:
+            assert p % b == 0, "an aligned block must land on a block boundary"
+        np.testing.assert_array_equal(got_rows[p:p + b], np.arange(k * b, k * b + b))
