@@ -28,8 +28,9 @@
 // l % 32; its half l / 32 supplies the contraction slots of head dims
 // [half*D/2, half*D/2 + D/2), the same dims for A and B, so every lane reads
 // one contiguous half-row of 16-B chunks.  Output register v of lane l is
-// C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Each wavefront owns one 32-row tile:
-// workgroups of 4 wavefronts up to 128 rows, of 16 above (up to 512 rows).
+// C[8*(v/4) + 4*(l/32) + v%4][l % 32].  Workgroups of 4 wavefronts owning one
+// 32-row tile each up to 128 rows; above, 8 wavefronts owning two tiles each
+// (up to 512 rows).
 
 #include "nx_device.hpp"
 
@@ -605,8 +606,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     // now, ahead of the K fragment reads; the sums after the MFMA issue.
     // (The LDS walk mode keeps its lagged work in one piece, ahead of the
     // fragment reads: splitting it costs it occupancy.)
-    // With 16 wavefronts the lagged work also stays in one piece: holding
-    // sixteen a_j partials across the MFMA chain would spill.
+    // With 8 wavefronts the lagged work also stays in one piece: holding
+    // eight a_j partials across the MFMA chains would spill.
     constexpr bool kSplitLag = kWalk != kWalkLds && NW == kWaves;
     const bool lag = st > 0;
     float la[NW], gx[kPairsPerLane], gy[kPairsPerLane];
@@ -715,9 +716,10 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 }
 
 // Pass 1: one workgroup per (tile, head unit).
-// NW wavefronts per workgroup (4, or 16 for more than 4 row tiles): one row
-// tile per wavefront keeps its query fragments and row statistics within 128
-// VGPRs, four wavefronts per SIMD (four tiles per wavefront took 252-256).
+// NW wavefronts of MPW row tiles per workgroup (4 x 1, or 8 x 2 above 4 row
+// tiles): one tile per wavefront keeps its query fragments and row statistics
+// within 128 VGPRs, four wavefronts per SIMD; two tiles take ~232 VGPRs, two
+// wavefronts per SIMD (four tiles per wavefront took 252-256, one).
 template <typename T, int D, int MPW, int NW>
 __global__ __launch_bounds__(64 * NW) void score_stats_kernel(const Args a) {
   __shared__ __align__(16) char smem[Geo<T, D>::kSlotsStats * Geo<T, D>::kTileBytes];
@@ -735,14 +737,14 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 // bf16 without blocks and with a register-lean walk form is held to 128 VGPRs
 // (4 wavefronts per SIMD), which it reaches without spilling; fp32, blocks and
 // the LDS and deep walk forms need more and run at 2-3.
-template <typename T, int kWalk, bool kBlocks>
+template <typename T, int kWalk, bool kBlocks, int MPW>
 constexpr int probs_min_waves() {
-  return sizeof(T) == 2 && !kBlocks && kWalk != kWalkLds && kWalk != kWalkFast4Deep ? 4 : 1;
+  return MPW == 1 && sizeof(T) == 2 && !kBlocks && kWalk != kWalkLds && kWalk != kWalkFast4Deep ? 4 : 1;
 }
 
 template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
 __global__ __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(probs_min_waves<T, kWalk, kBlocks>())))
+__attribute__((amdgpu_waves_per_eu(probs_min_waves<T, kWalk, kBlocks, MPW>())))
 void score_probs_kernel(const Args a) {
   __shared__ __align__(16) char smem[probs_smem_bytes<T, D, kWalk, NW>()];
   const int tile = blockIdx.x, hu = blockIdx.y;
@@ -761,9 +763,9 @@ int walk_mode(const Geometry& g) {
   return kWalkLds;
 }
 
-// Wavefronts per workgroup, one row tile each: 4 up to 4 row tiles, else 16
-// (the host allows at most 16: G*W <= 512).
-int waves_per_group(const Geometry& g) { return g.rows_pad / 32 <= 4 ? 4 : 16; }
+// Wavefronts per workgroup: 4 (one row tile each) up to 4 row tiles, else 8
+// (two row tiles each; the host allows at most 16 tiles: G*W <= 512).
+int waves_per_group(const Geometry& g) { return g.rows_pad / 32 <= 4 ? 4 : 8; }
 
 template <int MPW, int NW, typename T, int D, bool kBlocks>
 void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
@@ -794,14 +796,23 @@ void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
   }
 }
 
+// NW wavefronts of MPW row tiles each per workgroup: up to 4 row tiles, four
+// wavefronts of one tile; above, eight wavefronts of two tiles (16 tiles: G*W
+// up to 512 rows).  Two tiles per wavefront read each K fragment from LDS once
+// for both MFMA chains (the 16 one-tile wavefronts of a 512-row workgroup
+// re-read every sub-tile 16 times, as much LDS time as the MFMA work) and give
+// each wavefront two independent chains; measured on the 70B-shaped share
+// against sixteen one-tile wavefronts: 1.40 -> 1.31 ms (pass 1), 1.45 -> 1.32 ms
+// (pass 2), three interleaved rounds.
 template <bool kProbs, int NW, typename T, int D>
 hipError_t launch_t(const Args& a, hipStream_t s) {
+  constexpr int MPW = NW == 8 ? 2 : 1;
   const dim3 grid(a.g.n_tmax, a.g.n_hu);
   if constexpr (kProbs) {
-    if (a.g.block > 1) launch_probs<1, NW, T, D, true>(a, grid, s);
-    else launch_probs<1, NW, T, D, false>(a, grid, s);
+    if (a.g.block > 1) launch_probs<MPW, NW, T, D, true>(a, grid, s);
+    else launch_probs<MPW, NW, T, D, false>(a, grid, s);
   } else {
-    hipLaunchKernelGGL((score_stats_kernel<T, D, 1, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((score_stats_kernel<T, D, MPW, NW>), grid, dim3(64 * NW), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -812,7 +823,7 @@ hipError_t launch_pass(const Args& a, hipStream_t s) {
   const int nw = waves_per_group(g);
 #define NX_MPW(T, D)                                            \
   if (nw == 4) return launch_t<kProbs, 4, T, D>(a, s);          \
-  return launch_t<kProbs, 16, T, D>(a, s);
+  return launch_t<kProbs, 8, T, D>(a, s);
   if (g.dtype == NX_BF16) {
     if (g.head_dim == 128) { NX_MPW(uint16_t, 128) }
     NX_MPW(uint16_t, 64)
