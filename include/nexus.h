@@ -131,8 +131,14 @@ typedef struct nx_desc {
                                appendix 10 cites; then every head keeps its allocation.
                                With 1 or 2: cap = the item's head_cap (0: budget), keep rows
                                hold cap entries (entries past a head's kept count are set to
-                               -1), out_head_stride >= cap rows (cap * block with blocks),
-                               n_append must be 0, and head_budget must be non-NULL.  A
+                               -1), out_head_stride >= cap rows (cap * block with blocks) plus
+                               n_append (appended rows follow each head's own kept rows: the
+                               decode regime, with nx_unit.head_tokens / head_tokens_out
+                               carrying the per-head counts to the next event), and
+                               head_budget must be non-NULL.  With per-head resident counts
+                               the allocation takes Bbar = min(budget, the largest head's
+                               units) and counts the largest weights over all heads' units;
+                               each allocation is capped by its own head's units.  A
                                violation on the device marks the item bad.  Other values:
                                NX_EINVAL; nx_evict_step, nx_reservoir_select and
                                nx_kv_compact need 0. */
@@ -186,8 +192,18 @@ typedef struct nx_unit {
   int32_t head_cap;         /* per-head capacity with desc->head_alloc != 0 (0: budget) */
   int32_t* head_budget;     /* [n_kv_heads] int32 device array with desc->head_alloc != 0:
                                read (NX_HEADS_GIVEN) or written (NX_HEADS_ALLOC); else ignored */
-  float* out_w;             /* nullable: [n_kv_heads][units] fp32 (units = ceil(n_tokens / block)),
-                               the Nexus weights w (section 2.2 Eq. 5) the item's selection used */
+  float* out_w;             /* nullable: [n_kv_heads][units] fp32 (units = ceil(n_tokens_h / block)
+                               of each head, row stride as for n_tokens), the Nexus weights w
+                               (section 2.2 Eq. 5) the item's selection used */
+  const int32_t* head_tokens;   /* nullable: [n_kv_heads] int32 device array of per-head resident
+                               counts 1 <= n_tokens_h <= n_tokens (after per-head budgets the
+                               heads of a streaming cache hold different numbers of rows);
+                               NULL: every head holds n_tokens.  n_tokens bounds them (strides,
+                               max_tokens); with blocks and appended rows each must be a multiple
+                               of the block size */
+  int32_t* head_tokens_out; /* nullable: [n_kv_heads] int32, written with each head's row count
+                               after the event (kept rows + n_append), the head_tokens of the next
+                               event; must not overlap head_tokens */
 } nx_unit;
 
 /*

@@ -256,18 +256,22 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
     out_k / out_v are the rows of the kept blocks in ascending block order.
     Per-head budgets (appendix 10): head_budgets gives head h's kept count;
     ada_floor = f (not None) computes them with ada_head_budgets from the
-    weights of all heads (capacity head_cap, default budget).
+    weights of all heads (capacity head_cap, default budget).  k and v may
+    also be lists of per-head [N_h, D] arrays: after per-head budgets the
+    heads of a streaming cache hold different numbers of rows.
     Returns dict with per-head lists: w, keys, keep (ascending), out_k, out_v,
     and "budgets" (the per-head kept counts used).
     """
     q = np.asarray(q)
-    k = np.asarray(k)
-    v = np.asarray(v)
+    k = [np.asarray(x) for x in k]
+    v = [np.asarray(x) for x in v]
     h_q, W, d = q.shape
-    h_kv, n, _ = k.shape
-    if h_q % h_kv:
+    h_kv = len(k)
+    if len(v) != h_kv or any(len(kh) != len(vh) for kh, vh in zip(k, v)):
+        raise ValueError("k and v must hold the same rows")
+    if h_kv == 0 or h_q % h_kv:
         raise ValueError("H_q must be a multiple of H_kv")
-    if budget < 1 or n < 1:
+    if budget < 1 or min(len(x) for x in k) < 1:
         raise ValueError("budget and n_tokens must be >= 1")
     if n_sink + n_recent > budget:
         raise ValueError("forced slots exceed the budget")
@@ -281,11 +285,12 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
         q_grp = as_f64(q[h * g:(h + 1) * g], dtype)
         weights[h] = head_weights(q_grp, as_f64(k[h], dtype), walk_iters, lam, eps, block)["w"]
     if ada_floor is not None:
-        head_budgets = ada_head_budgets(np.stack([weights[h] for h in range(h_kv)]), budget,
-                                        ada_floor, budget if head_cap is None else head_cap)
+        head_budgets = ada_head_budgets([weights[h] for h in range(h_kv)], budget, ada_floor,
+                                        budget if head_cap is None else head_cap)
     for h in heads:
         w = weights[h]
         nu = w.shape[-1]
+        n = len(k[h])
         b_h = budget if head_budgets is None else int(head_budgets[h])
         if n_sink + n_recent > b_h:
             raise ValueError("forced slots exceed the head's budget")
@@ -304,21 +309,24 @@ def evict_step(q, k, v, budget, walk_iters, seed, *, dtype="bf16", layer=0,
 
 def select_from_weights(w, budget, seed, *, layer=0, step=0, seq_id=0,
                         n_sink=0, n_recent=0, n_avg=1, head_budgets=None):
-    """Reservoir selection on given weights w: [H_kv, N] (any precision).
+    """Reservoir selection on given weights w: [H_kv, N] (any precision), or a
+    list of per-head weight vectors of their own lengths.
 
     The oracle run on someone else's scores: same Philox stream, fp64 keys,
-    full sort.  Returns (keys [H_kv, N], list of ascending keep arrays).
+    full sort.  Returns (keys: [H_kv, N], or a list for ragged heads; list of
+    ascending keep arrays).
     """
-    w = np.asarray(w, dtype=np.float64)
-    h_kv, n = w.shape
-    keys = np.empty((h_kv, n))
+    rows = [np.asarray(x, dtype=np.float64).ravel() for x in w]
+    h_kv = len(rows)
+    ragged = len({len(x) for x in rows}) > 1
+    keys = [None] * h_kv
     keeps = []
     for h in range(h_kv):
-        keys[h] = head_keys(w[h], n, seq_id * h_kv + h, layer, step, seed, n_avg, n_sink,
-                            n_recent)
+        keys[h] = head_keys(rows[h], len(rows[h]), seq_id * h_kv + h, layer, step, seed, n_avg,
+                            n_sink, n_recent)
         keeps.append(select_top(keys[h], budget if head_budgets is None else
                                 int(head_budgets[h])))
-    return keys, keeps
+    return (keys if ragged else np.stack(keys)), keeps
 
 
 # ------------------------------------------------- per-head budgets ----
@@ -330,29 +338,36 @@ def ada_head_budgets(w, budget, floor, cap=None):
     that aim; this is the allocation of Ada-KV itself, a top-K over the
     scores of all heads together, on the Nexus weights, with a per-head floor:
 
-      Bbar = min(budget, N), f = min(floor, Bbar), K = H (Bbar - f);
+      N_h = head h's units, Bbar = min(budget, max_h N_h), f = min(floor, Bbar),
+      K = H (Bbar - f);
       order all (head h, unit j) by weight, largest first (weights <= 0 all
       count as 0), equal weights: the smaller head first;
       c_h = how many of the first K belong to head h;
-      B_h = min(f + c_h, cap, N)   (cap: the per-head capacity, default budget).
+      B_h = min(f + c_h, cap, N_h)   (cap: the per-head capacity, default budget).
 
-    w: [H, N] weights of the item's KV heads (any precision).  Returns int64 [H].
+    w: [H, N] weights of the item's KV heads (any precision), or a list of H
+    per-head weight vectors of their own lengths N_h (a streaming cache after
+    earlier per-head budgets: each head holds its own number of rows).
+    Returns int64 [H].
     """
-    w = np.asarray(w, dtype=np.float64)
-    h_kv, n = w.shape
+    rows = [np.asarray(x, dtype=np.float64).ravel() for x in w]
+    h_kv = len(rows)
+    sizes = np.array([len(x) for x in rows], dtype=np.int64)
     if budget < 1 or floor < 0:
         raise ValueError("budget must be >= 1 and floor >= 0")
-    if not np.all(np.isfinite(w)):
+    if h_kv == 0 or sizes.min() < 1:
+        raise ValueError("every head needs at least one unit")
+    if not all(np.all(np.isfinite(x)) for x in rows):
         raise ValueError("non-finite Nexus weight")
     cap = budget if cap is None else cap
-    bbar = min(budget, n)
+    bbar = min(budget, int(sizes.max()))
     f = min(floor, bbar)
     k = h_kv * (bbar - f)
-    val = np.where(w > 0, w, 0.0).ravel()
-    head = np.repeat(np.arange(h_kv), n)
+    val = np.concatenate([np.where(x > 0, x, 0.0) for x in rows])
+    head = np.repeat(np.arange(h_kv), sizes)
     order = np.lexsort((head, -val))          # weight descending, then head ascending
     counts = np.bincount(head[order[:k]], minlength=h_kv)
-    return np.minimum(np.minimum(f + counts, cap), n).astype(np.int64)
+    return np.minimum(np.minimum(f + counts, cap), sizes).astype(np.int64)
 
 
 # ------------------------------------------------- in-place compaction ----

@@ -73,6 +73,8 @@ class NxUnit(ctypes.Structure):
         ("head_cap", ctypes.c_int32),
         ("head_budget", ctypes.c_void_p),
         ("out_w", ctypes.c_void_p),
+        ("head_tokens", ctypes.c_void_p),
+        ("head_tokens_out", ctypes.c_void_p),
     ]
 
 

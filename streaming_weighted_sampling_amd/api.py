@@ -245,7 +245,8 @@ def make_units(items, device="cuda"):
     """Device array of nx_unit records from a list of dicts (see nx_unit in nexus.h)."""
     arr = (NxUnit * len(items))()
     for rec, it in zip(arr, items):
-        for key in ("q", "k", "v", "keep", "out_k", "out_v", "app_k", "app_v", "out_w"):
+        for key in ("q", "k", "v", "keep", "out_k", "out_v", "app_k", "app_v", "out_w",
+                    "head_tokens", "head_tokens_out"):
             setattr(rec, key, _ptr(it.get(key)))
         rec.kv_head_stride = it["kv_head_stride"]
         rec.out_head_stride = it["out_head_stride"]

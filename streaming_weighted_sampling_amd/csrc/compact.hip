@@ -36,6 +36,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(const Args a) {
   const int b = a.g.block;
   const int kept_rows = min(u.kept * b, u.n);
   const int rows = kept_rows + u.n_append;
+  // The head's row count after the event (the next event's resident count).
+  if (blockIdx.x == 0 && threadIdx.x == 0 && u.tokens_out != nullptr) *u.tokens_out = rows;
   const uint32_t src_bytes = uint32_t(u.n) * kRowBytes;
   const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
   const Buf kb(u.k, src_bytes), vb(u.v, src_bytes);
@@ -180,9 +182,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
   constexpr int kRowsPerPass = kThreads / kPerRow;
   const int hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
-  if (!u.valid || u.keep == nullptr || u.n_append == 0) return;
+  if (!u.valid || u.keep == nullptr) return;
   // Appended rows follow the kept rows (with blocks, n % b == 0 then holds).
   const int kept = min(u.kept * a.g.block, u.n);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && u.tokens_out != nullptr) *u.tokens_out = kept + u.n_append;
+  if (u.n_append == 0) return;
   const uint32_t head_bytes = uint32_t(kept + u.n_append) * kRowBytes;
   const uint32_t app_bytes = uint32_t(u.n_append) * kRowBytes;
   const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);

@@ -113,6 +113,7 @@ struct HeadUnit {
   const char* app_k;
   const char* app_v;
   float* w_out;        // nullable: this head's weight export row (nu entries)
+  int32_t* tokens_out; // nullable: where this head's row count after the event goes
   int32_t n, budget, kept, n_append;
   int32_t nu;          // selection units: ceil(n / block); kept = min(budget, nu) of them
   int32_t cap;         // keep row length: budget, or the per-head capacity
@@ -136,7 +137,9 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   const int64_t d = g.head_dim;
   HeadUnit r;
   r.h = h;
-  r.n = u.n_tokens;
+  // Per-head resident counts (decode with per-head budgets), bounded by the
+  // item's n_tokens.
+  r.n = u.head_tokens != nullptr ? u.head_tokens[h] : u.n_tokens;
   // Per-head budgets: keep rows of `cap` entries; the head's own budget (given
   // ones at every stage, allocated ones once this call's allocation is in
   // place; before that, the capacity).
@@ -145,7 +148,7 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   r.cap = per_head && u.head_cap > 0 ? u.head_cap : u.budget;
   r.budget = !per_head ? u.budget
              : (budgets_in && u.head_budget != nullptr) ? u.head_budget[h] : r.cap;
-  r.nu = (u.n_tokens + g.block - 1) / g.block;
+  r.nu = (r.n + g.block - 1) / g.block;
   r.kept = r.budget < r.nu ? r.budget : r.nu;
   r.n_append = u.n_append;
   r.layer = u.layer;
@@ -158,19 +161,25 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   r.out_v = u.out_v ? static_cast<char*>(u.out_v) + int64_t(h) * u.out_head_stride * esz : nullptr;
   r.app_k = u.app_k ? static_cast<const char*>(u.app_k) + int64_t(h) * u.n_append * d * esz : nullptr;
   r.app_v = u.app_v ? static_cast<const char*>(u.app_v) + int64_t(h) * u.n_append * d * esz : nullptr;
-  r.w_out = u.out_w ? u.out_w + int64_t(h) * r.nu : nullptr;
-  bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && u.budget >= 1 &&
+  // The weight export keeps the item's row stride (units of n_tokens).
+  r.w_out = u.out_w ? u.out_w + int64_t(h) * ((u.n_tokens + g.block - 1) / g.block) : nullptr;
+  r.tokens_out = u.head_tokens_out ? u.head_tokens_out + h : nullptr;
+  bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && r.n >= 1 && r.n <= u.n_tokens &&
+            u.budget >= 1 &&
             u.n_append >= 0 && r.budget >= 1 && r.budget <= r.cap &&
             (a.n_sink + a.n_recent <= r.budget || r.budget >= r.nu) &&
             u.kv_head_stride >= int64_t(u.n_tokens) * d && u.q != nullptr && u.k != nullptr;
-  if (per_head) ok = ok && u.head_cap >= 0 && u.n_append == 0 && u.head_budget != nullptr;
+  if (per_head) ok = ok && u.head_cap >= 0 && u.head_budget != nullptr;
+  // The counts written after the event must not change the ones this event reads.
+  if (u.head_tokens != nullptr && u.head_tokens_out != nullptr)
+    ok = ok && (u.head_tokens_out + g.h_kv <= u.head_tokens || u.head_tokens + g.h_kv <= u.head_tokens_out);
   // Rows of the kept units (whole blocks; a short last block only shortens it),
   // at most the capacity's.
-  const int64_t kept_rows = min(int64_t(min(r.cap, r.nu)) * g.block, int64_t(u.n_tokens));
+  const int64_t kept_rows = min(int64_t(min(r.cap, r.nu)) * g.block, int64_t(r.n));
   if (u.out_k || u.out_v)
     ok = ok && u.out_head_stride >= (kept_rows + u.n_append) * d &&
          (kept_rows + u.n_append) * d * esz <= INT32_MAX;
-  if (g.block > 1 && u.n_append > 0) ok = ok && u.n_tokens % g.block == 0;
+  if (g.block > 1 && u.n_append > 0) ok = ok && r.n % g.block == 0;
   if (g.inplace)   // k / v are compacted in place and must hold the appended rows too
     ok = ok && u.out_k == nullptr && u.out_v == nullptr && u.v != nullptr &&
          u.kv_head_stride >= (kept_rows + u.n_append) * d &&

@@ -1147,15 +1147,32 @@ __global__ __launch_bounds__(kKeysThreads) void head_codes_kernel(const Args a) 
     if (s_hist[b] != 0u) atomicAdd(&gh[b], s_hist[b]);
 }
 
-// Allocation sizes of one item: Bbar = min(budget, units), f = min(floor,
-// Bbar), k = H (Bbar - f) codes to take out of total = H * units.
+// Selection units of head h of an item (its resident count, per head when
+// the item carries head_tokens; clamped into [0, n_tokens] so that indexing
+// stays inside the item's arrays even for a bad count, which head_unit
+// rejects).
+__device__ inline int alloc_head_units(const Args& a, const nx_unit& it, int h) {
+  int n = it.head_tokens != nullptr ? it.head_tokens[h] : it.n_tokens;
+  n = min(max(n, 0), it.n_tokens);
+  return (n + a.g.block - 1) / a.g.block;
+}
+
+// Allocation sizes of one item: Bbar = min(budget, units of its largest
+// head), f = min(floor, Bbar), k = H (Bbar - f) codes to take out of all the
+// heads' total units.
 struct AllocSizes {
   int f, k, total;
 };
-__device__ inline AllocSizes alloc_sizes(const Args& a, const nx_unit& it, int nu) {
-  const int bbar = min(it.budget, nu);
+__device__ inline AllocSizes alloc_sizes(const Args& a, const nx_unit& it) {
+  int numax = 0, total = 0;
+  for (int h = 0; h < a.g.h_kv; ++h) {
+    const int nu = alloc_head_units(a, it, h);
+    numax = max(numax, nu);
+    total += nu;   // < 2^31: H * n_tokens is checked on the host
+  }
+  const int bbar = min(it.budget, numax);
   const int f = min(a.head_floor, bbar);
-  return {f, a.g.h_kv * (bbar - f), a.g.h_kv * nu};   // total < 2^31 (checked on the host)
+  return {f, a.g.h_kv * (bbar - f), total};
 }
 
 // The bin of the item's histogram (in LDS) that holds the k-th largest code.
@@ -1205,7 +1222,7 @@ __global__ __launch_bounds__(kSelThreads) void head_count_kernel(const Args a) {
   if (!u.valid) return;
   const nx_unit it = load_item(a, item);
   const int nu = u.nu;
-  const AllocSizes z = alloc_sizes(a, it, nu);
+  const AllocSizes z = alloc_sizes(a, it);
   if (!(z.k > 0 && z.k < z.total)) return;
   __shared__ uint32_t s_hist[kAllocBins];
   __shared__ uint32_t s_wsum[kSelWaves];
@@ -1285,17 +1302,30 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
   const nx_unit it = load_item(a, item);
   const HeadUnit u0 = head_unit(a, item * H);
   if (!u0.valid) return;
-  const int cap = u0.cap, nu = u0.nu;
+  const int cap = u0.cap;
   if (it.keep != nullptr)
     for (int64_t i = tid; i < int64_t(H) * cap; i += kSelThreads) it.keep[i] = -1;
   if (g.head_alloc != NX_HEADS_ALLOC) return;
   __shared__ SelCore sh;
   __shared__ int s_gt[NX_MAX_ALLOC_HEADS], s_eq[NX_MAX_ALLOC_HEADS], s_off[NX_MAX_ALLOC_HEADS];
+  // Units of every head and their exclusive prefix (the flat code index of
+  // head h starts at s_pre[h]).
+  __shared__ int s_nu[NX_MAX_ALLOC_HEADS], s_pre[NX_MAX_ALLOC_HEADS + 1];
+  if (tid == 0) {
+    int acc = 0;
+    for (int h = 0; h < H; ++h) {
+      s_nu[h] = alloc_head_units(a, it, h);
+      s_pre[h] = acc;
+      acc += s_nu[h];
+    }
+    s_pre[H] = acc;
+  }
+  __syncthreads();
   __shared__ uint32_t s_hist[kAllocBins];
   __shared__ uint32_t s_cand[kAllocCand];
   __shared__ uint32_t s_wsum[kSelWaves];
   __shared__ int s_bstar, s_krem, s_above, s_ncand, s_fallback;
-  const AllocSizes z = alloc_sizes(a, it, nu);
+  const AllocSizes z = alloc_sizes(a, it);
   const int f = z.f, k = z.k, total = z.total;
   const uint32_t* base =
       reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens) + a.wcode_off;
@@ -1389,9 +1419,18 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
         s_gt[h] = 0;
         s_eq[h] = 0;
       }
+      // Head of flat code index idx: the last h with s_pre[h] <= idx.
+      auto head_of = [&](int idx) {
+        int lo = 0, hi = H - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= idx) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+      };
       auto code_at = [&](int idx) -> uint64_t {
-        const int h = idx / nu;
-        return uint64_t(base[size_t(h) * hstride + (idx - h * nu)]) | 0xFFFFFFFF00000000ull;
+        const int h = head_of(idx);
+        return uint64_t(base[size_t(h) * hstride + (idx - s_pre[h])]) | 0xFFFFFFFF00000000ull;
       };
       uint32_t o = 0u, an = ~0u;
       for (int idx = tid; idx < total; idx += kSelThreads) {
@@ -1424,7 +1463,7 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
       const uint64_t prefix = sh.prefix, mask = sh.mask;
       int cur = -1, gt = 0, eq = 0;
       for (int idx = tid; idx < total; idx += kSelThreads) {
-        const int h = idx / nu;
+        const int h = head_of(idx);
         if (h != cur) {
           if (cur >= 0) {
             atomicAdd(&s_gt[cur], gt);
@@ -1457,17 +1496,17 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
       if (k == 0) {
         ch = 0;
       } else if (k >= total) {
-        ch = nu;
+        ch = s_nu[h];
       } else {
         const int take = all ? s_eq[h] : min(s_eq[h], need);
         if (!all) need -= take;
         ch = s_gt[h] + take;
       }
-      const int bh = min(min(f + ch, cap), nu);
+      const int bh = min(min(f + ch, cap), s_nu[h]);
       it.head_budget[h] = bh;
       // A budget that cannot hold the forced slots makes the head invalid for
       // the stages that follow: report it.
-      if (bh < a.n_sink + a.n_recent && bh < nu) raise_status(a, kStatusBadItem);
+      if (bh < a.n_sink + a.n_recent && bh < s_nu[h]) raise_status(a, kStatusBadItem);
     }
   }
 }

@@ -8,6 +8,9 @@ cited Ada-KV, as the oracle states it).
   set equals the oracle's selection on those weights with its budget, at least
   99.9% of it is shared with the pure-oracle result, keep entries past a head's
   count are -1, and the compacted rows are the gathered rows.
+* Per-head resident counts (head_tokens / head_tokens_out): one event on
+  ragged heads, and streaming decode with allocated budgets (copy and in
+  place), every event against the oracle on the device's pre-event cache.
 """
 
 import numpy as np
@@ -153,3 +156,155 @@ def test_given_budget_above_capacity_marks_the_item_bad():
     with pytest.raises(nx.NexusError) as e:
         _run_batch(cfg, wl, lay, n, 400, 400, wl.walk_iters, hb_in=[400] * 7 + [401])
     assert e.value.code == nx.NX_EINVAL
+
+
+# ------------------------------------------------ per-head resident counts --
+
+
+def test_uniform_budget_on_ragged_heads():
+    """One event on heads of different lengths (head_tokens): each head's
+    weights, selection and rows follow the oracle on its own rows, and
+    head_tokens_out holds min(B, n_h) + n_append."""
+    n, B, A = 4096, 700, 64
+    wl, lay = _layer(n)
+    H, D = wl.h_kv, wl.head_dim
+    cfg = nx.NexusConfig(wl.h_q, H, D, wl.window, torch.bfloat16)
+    counts = [4096, 3000, 701, 700, 1, 2048, 4095, 1500]
+    tin = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    tout = torch.full((H,), -7, dtype=torch.int32, device=DEV)
+    keep = torch.full((H, B), 12345, dtype=torch.int32, device=DEV)
+    out_k = torch.zeros(H, B + A, D, dtype=cfg.dtype, device=DEV)
+    out_v = torch.zeros_like(out_k)
+    app_k = torch.randn(H, A, D, device=DEV).to(cfg.dtype)
+    app_v = torch.randn_like(app_k)
+    w_sel = torch.full((H, n), float("nan"), device=DEV)
+    units = nx.make_units([dict(q=lay["q"], k=lay["k"], v=lay["v"], keep=keep, out_k=out_k,
+                                out_v=out_v, app_k=app_k, app_v=app_v, kv_head_stride=n * D,
+                                out_head_stride=(B + A) * D, n_tokens=n, budget=B, n_append=A,
+                                layer=1, out_w=w_sel, head_tokens=tin, head_tokens_out=tout)],
+                          device=DEV)
+    ws = nx.new_workspace(cfg, n, 1, wl.walk_iters, device=DEV)
+    nx.nx_evict_batch(cfg, units, 1, n, wl.walk_iters, 11, workspace=ws, step=3,
+                      max_out_rows=B + A)
+    nx.nx_read_device_status(cfg, ws)
+    np.testing.assert_array_equal(tout.cpu().numpy(), [min(B, c) + A for c in counts])
+    qh, dt = gc.host(lay["q"])
+    kh, _ = gc.host(lay["k"])
+    vh, _ = gc.host(lay["v"])
+    ref = nexus.evict_step(qh, [kh[h, :c] for h, c in enumerate(counts)],
+                           [vh[h, :c] for h, c in enumerate(counts)], B, wl.walk_iters, 11,
+                           dtype=dt, layer=1, step=3)
+    w = w_sel.cpu().numpy()
+    keep = keep.cpu().numpy()
+    _, on_gpu_w = nexus.select_from_weights([w[h, :c] for h, c in enumerate(counts)], B, 11,
+                                            layer=1, step=3)
+    for h, c in enumerate(counts):
+        kept = min(B, c)
+        assert np.all(np.isnan(w[h, c:])), f"head {h}: weights written past its count"
+        gc.assert_weights_close(w[h, :c], ref["w"][h], f"head {h}")
+        np.testing.assert_array_equal(keep[h, :kept], on_gpu_w[h], err_msg=f"head {h}")
+        gc.assert_kept_matches_oracle(keep[h, :kept], ref["keep"][h], ref["keys"][h], kept,
+                                      f"head {h}")
+        assert gc.rows_equal(out_k[h, :kept], lay["k"][h], keep[h, :kept])
+        assert gc.rows_equal(out_v[h, :kept], lay["v"][h], keep[h, :kept])
+        assert torch.equal(out_k[h, kept:kept + A].view(torch.int16), app_k[h].view(torch.int16))
+        assert torch.equal(out_v[h, kept:kept + A].view(torch.int16), app_v[h].view(torch.int16))
+
+
+@pytest.mark.parametrize("bad", ["same_array", "above_n_tokens", "zero"])
+def test_bad_head_tokens_mark_the_item_bad(bad):
+    n, B = 1024, 200
+    wl, lay = _layer(n)
+    H, D = wl.h_kv, wl.head_dim
+    cfg = nx.NexusConfig(wl.h_q, H, D, wl.window, torch.bfloat16)
+    vals = [n] * H
+    if bad == "above_n_tokens":
+        vals[3] = n + 1
+    if bad == "zero":
+        vals[5] = 0
+    tin = torch.tensor(vals, dtype=torch.int32, device=DEV)
+    tout = tin if bad == "same_array" else torch.zeros(H, dtype=torch.int32, device=DEV)
+    keep = torch.zeros(H, B, dtype=torch.int32, device=DEV)
+    out_k = torch.zeros(H, B, D, dtype=cfg.dtype, device=DEV)
+    out_v = torch.zeros_like(out_k)
+    units = nx.make_units([dict(q=lay["q"], k=lay["k"], v=lay["v"], keep=keep, out_k=out_k,
+                                out_v=out_v, kv_head_stride=n * D, out_head_stride=B * D,
+                                n_tokens=n, budget=B, head_tokens=tin, head_tokens_out=tout)],
+                          device=DEV)
+    ws = nx.new_workspace(cfg, n, 1, wl.walk_iters, device=DEV)
+    with pytest.raises(nx.NexusError) as e:
+        nx.nx_evict_batch(cfg, units, 1, n, wl.walk_iters, 1, workspace=ws, max_out_rows=B)
+        nx.nx_read_device_status(cfg, ws)
+    assert e.value.code == nx.NX_EINVAL
+    if bad == "same_array":
+        np.testing.assert_array_equal(tin.cpu().numpy(), vals)
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+def test_streaming_decode_with_allocated_budgets(inplace):
+    """Four append-128 / evict events on two layers with allocated per-head
+    budgets (floor 32, capacity 2B): the heads' row counts drift apart and
+    travel on the device from one event to the next.  Every event is checked
+    against the oracle on the device's pre-event cache: the allocation exactly
+    on the device's weights, the selection exactly on them, the weights and
+    kept sets against the pure oracle, the new counts and the new rows."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    wl = WORKLOADS["llama3_8b_layer"]
+    L, n0, A, B, floor, seed = 2, 2048, 128, 400, 32, 5
+    cap = 2 * B
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
+                         head_alloc=nx.NX_HEADS_ALLOC, head_floor=floor)
+    sc = StreamingCache(cfg, L, max(n0, cap + A), B, A, wl.walk_iters, seed=seed, device=DEV,
+                        inplace=inplace, export_w=True, head_cap=cap)
+    g = torch.Generator(device="cpu").manual_seed(23)
+    k0 = torch.randn((L, wl.h_kv, n0, wl.head_dim), generator=g).to(torch.bfloat16)
+    # Heads with different spreads so that the allocation moves budget between them.
+    k0 = k0 * torch.linspace(0.3, 3.0, wl.h_kv).view(1, -1, 1, 1).to(torch.bfloat16)
+    sc.load(k0.to(DEV), torch.randn_like(k0).to(DEV), n0)
+    drift = False
+    for step in range(4):
+        sc.q.copy_(torch.randn(sc.q.shape, generator=g).to(torch.bfloat16))
+        sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g).to(torch.bfloat16))
+        sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g).to(torch.bfloat16))
+        pre = sc.head_tokens().numpy()
+        kp, vp = (gc.host(t)[0] for t in sc.live())
+        sc.step()
+        nx.nx_read_device_status(sc.cfg, sc.ws)
+        post = sc.head_tokens().numpy()
+        hb_all = sc.head_budget.cpu().numpy()
+        kl, vl = (gc.host(t)[0] for t in sc.live())
+        app_k, app_v = gc.host(sc.app_k)[0], gc.host(sc.app_v)[0]
+        for l in range(L):
+            what = f"step {step} layer {l}"
+            counts = pre[l]
+            hb = hb_all[l]
+            w_all = sc.weights(l).cpu().numpy()
+            w_gpu = [w_all[h, :c] for h, c in enumerate(counts)]
+            np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, floor, cap=cap),
+                                          err_msg=what)
+            _, on_gpu_w = nexus.select_from_weights(w_gpu, 0, seed, layer=l, step=step,
+                                                    head_budgets=hb)
+            qh, dt = gc.host(sc.q[l])
+            ref = nexus.evict_step(qh, [kp[l, h, :c] for h, c in enumerate(counts)],
+                                   [vp[l, h, :c] for h, c in enumerate(counts)], B,
+                                   wl.walk_iters, seed, dtype=dt, layer=l, step=step,
+                                   head_budgets=hb)
+            keep = sc.keep[l].cpu().numpy()
+            for h, c in enumerate(counts):
+                kept = min(int(hb[h]), int(c))
+                np.testing.assert_array_equal(keep[h, :kept], on_gpu_w[h], err_msg=f"{what} head {h}")
+                assert np.all(keep[h, kept:] == -1)
+                gc.assert_weights_close(w_gpu[h], ref["w"][h], f"{what} head {h}")
+                gc.assert_kept_matches_oracle(keep[h, :kept], ref["keep"][h], ref["keys"][h],
+                                              kept, f"{what} head {h}")
+                assert post[l, h] == kept + A
+                if inplace:   # all pre-event rows of the buffer: they hold kept + A
+                    exp_k = nexus.compact_inplace(kp[l, h], keep[h, :kept], app_k[l, h])
+                    exp_v = nexus.compact_inplace(vp[l, h], keep[h, :kept], app_v[l, h])
+                else:
+                    exp_k = np.concatenate([kp[l, h][keep[h, :kept]], app_k[l, h]])
+                    exp_v = np.concatenate([vp[l, h][keep[h, :kept]], app_v[l, h]])
+                np.testing.assert_array_equal(kl[l, h, :kept + A], exp_k[:kept + A])
+                np.testing.assert_array_equal(vl[l, h, :kept + A], exp_v[:kept + A])
+        drift = drift or len(set(post.ravel().tolist())) > 1
+    assert drift, "the allocation never moved budget between heads"

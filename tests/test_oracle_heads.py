@@ -122,3 +122,63 @@ def test_evict_step_with_head_budgets():
     # The kept set of each head is the selection on its keys with its own budget.
     for h in range(h_kv):
         np.testing.assert_array_equal(ada["keep"][h], nexus.select_top(ada["keys"][h], want[h]))
+
+
+def test_hand_computed_ragged_heads():
+    # After earlier per-head budgets the heads hold different unit counts:
+    # head 0 has 2 units, head 1 has 4.  Bbar = min(budget, 4).
+    w = [np.array([0.5, 0.1]), np.array([0.4, 0.3, 0.2, 0.05])]
+    # B = 2, floor 0: K = 4 -> 0.5 (h0), 0.4, 0.3, 0.2 (h1).
+    np.testing.assert_array_equal(nexus.ada_head_budgets(w, 2, 0, cap=10), [1, 3])
+    # Floor 1: K = 2 -> 0.5 (h0), 0.4 (h1); plus 1 each.
+    np.testing.assert_array_equal(nexus.ada_head_budgets(w, 2, 1, cap=10), [2, 2])
+    # B = 3: K = 6 = all units -> every head keeps everything.
+    np.testing.assert_array_equal(nexus.ada_head_budgets(w, 3, 0, cap=10), [2, 4])
+    # Capacity 3 cuts head 1.
+    np.testing.assert_array_equal(nexus.ada_head_budgets(w, 3, 0, cap=3), [2, 3])
+    # B = 4, floor 3: K = 2 -> 0.5 (h0), 0.4 (h1); head 0's 3 + 1 is cut to its 2 units.
+    np.testing.assert_array_equal(nexus.ada_head_budgets(w, 4, 3, cap=10), [2, 4])
+
+
+def test_brute_force_ragged_heads():
+    """Ragged heads against Python's sort: (weight or 0) descending, head ascending."""
+    rng = np.random.default_rng(8)
+    for _ in range(300):
+        h = int(rng.integers(1, 6))
+        ns = rng.integers(1, 12, size=h)
+        w = [rng.choice([0.5, 0.25, 0.125, 0.0, -1.0], size=int(m)) for m in ns]
+        b = int(rng.integers(1, 14))
+        f = int(rng.integers(0, b + 1))
+        cap = int(rng.integers(1, 20))
+        items = sorted(((max(w[i][j], 0.0), i) for i in range(h) for j in range(ns[i])),
+                       key=lambda t: (-t[0], t[1]))
+        bbar = min(b, int(ns.max()))
+        ff = min(f, bbar)
+        k = h * (bbar - ff)
+        c = np.zeros(h, dtype=int)
+        for _, i in items[:k]:
+            c[i] += 1
+        want = np.minimum(np.minimum(ff + c, cap), ns)
+        np.testing.assert_array_equal(nexus.ada_head_budgets(w, b, f, cap=cap), want)
+
+
+def test_evict_step_ragged_heads_are_independent_but_for_the_budgets():
+    """Each ragged head's result is the one-head event on its own rows with the
+    same Philox unit (seq_id' = seq_id * H + h) and its allocated budget."""
+    rng = np.random.default_rng(9)
+    h_q, h_kv, W, d = 8, 4, 4, 16
+    ns = [40, 64, 17, 33]
+    q = rng.standard_normal((h_q, W, d)).astype(np.float32)
+    k = [rng.standard_normal((m, d)).astype(np.float32) for m in ns]
+    v = [rng.standard_normal((m, d)).astype(np.float32) for m in ns]
+    out = nexus.evict_step(q, k, v, 16, 2, 9, dtype="f32", layer=3, step=5, seq_id=2,
+                           ada_floor=4, head_cap=40)
+    want = nexus.ada_head_budgets([out["w"][h] for h in range(h_kv)], 16, 4, cap=40)
+    g = h_q // h_kv
+    for h in range(h_kv):
+        assert out["budgets"][h] == want[h] and len(out["w"][h]) == ns[h]
+        one = nexus.evict_step(q[h * g:(h + 1) * g], [k[h]], [v[h]], 16, 2, 9, dtype="f32",
+                               layer=3, step=5, seq_id=2 * h_kv + h, head_budgets=[want[h]])
+        np.testing.assert_array_equal(out["keep"][h], one["keep"][0])
+        np.testing.assert_array_equal(out["out_k"][h], k[h][out["keep"][h]])
+        np.testing.assert_array_equal(out["out_v"][h], v[h][out["keep"][h]])
