@@ -652,16 +652,46 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   const bool estimate = uses_estimate(a, u);
   uint32_t* codes = reinterpret_cast<uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
   constexpr int kPer = kKeysPerBlock / kKeysThreads;
+  static_assert(kPer == 4, "one 16-byte vector per array and thread");
+  // Computed weights in rows of a multiple of 4 floats: thread t takes tokens
+  // j0 + 4t .. +3 with one 16-byte load per array (and one 16-byte code
+  // store); otherwise tokens j0 + t + kKeysThreads i, one float at a time.
+  const bool vec = a.w_in == nullptr && (g.max_tokens & 3) == 0;
+  auto tok = [&](int i) {
+    return vec ? j0 + 4 * int(threadIdx.x) + i : j0 + int(threadIdx.x) + kKeysThreads * i;
+  };
   float w[kPer];
+  if (vec) {
+    const int jv = j0 + 4 * int(threadIdx.x);
+    const int jl = jv < n ? jv : j0;   // rows hold max_tokens >= n rounded up to 4 floats
+    const float4 av = *reinterpret_cast<const float4*>(ws.a_in + jl);
+    float4 pv[kMaxWalk];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int j = j0 + threadIdx.x + kKeysThreads * i;
-    w[i] = ws(a, s_coef, j < n ? j : j0);
+    for (int t = 0; t < kMaxWalk; ++t)
+      pv[t] = t < g.walk ? *reinterpret_cast<const float4*>(ws.p_in + size_t(t) * g.max_tokens + jl)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float ae[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pe[kMaxWalk];
+#pragma unroll
+      for (int t = 0; t < kMaxWalk; ++t)
+        pe[t] = e == 0 ? pv[t].x : e == 1 ? pv[t].y : e == 2 ? pv[t].z : pv[t].w;
+      w[e] = combine_weight(a, s_coef, ae[e], pe, jl + e, ws.ramp);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tok(i);
+      w[i] = ws(a, s_coef, j < n ? j : j0);
+    }
   }
   bool nonfinite = false;
+  uint32_t cv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int j = j0 + threadIdx.x + kKeysThreads * i;
+    const int j = tok(i);
+    cv[i] = 0u;
     if (j < n) {
       nonfinite |= !isfinite(w[i]);
       if (u.w_out != nullptr) u.w_out[j] = w[i];
@@ -670,16 +700,25 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
         if (a.n_avg == NX_TOPK) {
           // The key is w itself (appendix 8.2 limit): code of log2(w), same
           // order, within an ulp of the log, and exact keys (w) in the band.
-          codes[j] = forced ? 0xFFFFFFFFu
-                     : !(w[i] > 0.f) ? 0u
-                     : min(max(f32_code(__builtin_amdgcn_logf(w[i])), 1u), 0xFFFFFFFEu);
+          cv[i] = forced ? 0xFFFFFFFFu
+                  : !(w[i] > 0.f) ? 0u
+                  : min(max(f32_code(__builtin_amdgcn_logf(w[i])), 1u), 0xFFFFFFFEu);
         } else if (a.n_avg <= 1) {
           const uint4 x = philox4x32_10(make_uint4(uint32_t(j), u.unit_id, u.layer, a.step), k0, k1);
-          codes[j] = estimate_code(x.x, x.y, w[i], forced);
+          cv[i] = estimate_code(x.x, x.y, w[i], forced);
         } else {
-          codes[j] = estimate_code_avg(a, u, j, w[i], forced, k0, k1);
+          cv[i] = estimate_code_avg(a, u, j, w[i], forced, k0, k1);
         }
       }
+    }
+  }
+  if (estimate) {
+    if (vec && tok(kPer - 1) < n) {
+      *reinterpret_cast<uint4*>(codes + tok(0)) = make_uint4(cv[0], cv[1], cv[2], cv[3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (tok(i) < n) codes[tok(i)] = cv[i];
     }
   }
   if (a.est_wcodes) {
@@ -691,7 +730,7 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
     uint32_t* wc = codes + a.wcode_off;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int j = j0 + threadIdx.x + kKeysThreads * i;
+      const int j = tok(i);
       if (j < n) {
         const uint32_t c = (w[i] > 0.f && w[i] < INFINITY) ? __float_as_uint(w[i]) : 0u;
         wc[j] = c;
