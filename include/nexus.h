@@ -224,8 +224,12 @@ size_t nx_evict_workspace_bytes(const nx_desc* desc, int32_t max_tokens, int32_t
  *   k_cache      [n_kv_heads][kv_head_stride]; v_cache likewise
  *   n_tokens     N >= 1 resident tokens per head
  *   budget       B >= 1 kept tokens per head (B >= N keeps all)
- *   walk_iters   H in [0, min(window, 8)]: the H most recent window rows, oldest
- *                first, feed the walk; H = 0 gives plain direct attention
+ *   walk_iters   H in [0, window] (H > window: NX_EINVAL): the H most recent window
+ *                rows, oldest first, feed the walk (section 2.2 Eq. 4); H = 0 gives
+ *                plain direct attention.  Built for H <= 64; above 8 (or above 64
+ *                walk rows G * H) only with G = n_q_heads / n_kv_heads <= 32, where
+ *                the walk rows take a separate Gram pass; other shapes:
+ *                NX_EUNSUPPORTED
  *   seed         64-bit Philox key
  *   out_keep_idx [n_kv_heads, budget] int32, ascending; entries past `kept` untouched
  *   out_k, out_v [n_kv_heads][out_head_stride], must not overlap k_cache / v_cache;

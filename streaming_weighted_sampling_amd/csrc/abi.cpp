@@ -48,15 +48,17 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   if (max_tokens < 1 || max_tokens > kMaxTokens || n_items < 1) return NX_EINVAL;
   // One KV head's rows (and each per-head workspace array) stay below 2 GB so
   // 32-bit buffer offsets address them.
-  if (int64_t(max_tokens) * d->head_dim * elem_size(d->dtype) > (int64_t(1) << 31) ||
-      int64_t(max_tokens) * kMaxWalk * 4 > (int64_t(1) << 31))
-    return NX_EUNSUPPORTED;
   if (walk < 0 || walk > d->window) return NX_EINVAL;
+  if (int64_t(max_tokens) * d->head_dim * elem_size(d->dtype) > (int64_t(1) << 31) ||
+      int64_t(max_tokens) * (walk > kMaxWalk ? walk : kMaxWalk) * 4 > (int64_t(1) << 31))
+    return NX_EUNSUPPORTED;
   const int32_t group = d->n_q_heads / d->n_kv_heads;
   const int64_t rows = int64_t(group) * d->window;
   const int64_t rows_pad = (rows + 31) / 32 * 32;
-  if (walk > kMaxWalk || int64_t(group) * walk > kMaxWalkRows || rows_pad > kMaxRowsPad)
-    return NX_EUNSUPPORTED;
+  if (rows_pad > kMaxRowsPad) return NX_EUNSUPPORTED;
+  // Deep walks take one row tile per G rows of a window slot (G <= 32).
+  const bool deep = walk > kMaxWalk || int64_t(group) * walk > kMaxWalkRows;
+  if (deep && (walk > kMaxWalkDeep || group > 32)) return NX_EUNSUPPORTED;
   const int64_t n_hu = int64_t(n_items) * d->n_kv_heads;
   if (n_hu > 65535) return NX_EUNSUPPORTED;     // grid y dimension of the token stages
   g->h_q = d->n_q_heads;
@@ -89,6 +91,8 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->tok_per_block = tpb;
   g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
+  g->deep = deep ? 1 : 0;
+  g->n_gc = (max_tokens + kGramChunk - 1) / kGramChunk;
   return NX_OK;
 }
 

@@ -28,8 +28,14 @@
 
 namespace nx {
 
-constexpr int kMaxWalk = 8;          // walk depth H supported by the kernels
-constexpr int kMaxWalkRows = 64;     // G * H window rows feeding the walk
+constexpr int kMaxWalk = 8;          // walk depth H of the register-held walk forms
+constexpr int kMaxWalkRows = 64;     // G * H window rows feeding those forms
+// Deeper walks (H > kMaxWalk or G * H > kMaxWalkRows, up to kMaxWalkDeep with
+// G <= 32): the second sweep writes every walk row P_t, a separate pass forms
+// their Gram matrix, and the recurrence runs in LDS.
+constexpr int kMaxWalkDeep = 64;
+constexpr int kMaxCoef = kMaxWalkDeep;   // walk coefficient slots per head unit
+constexpr int kGramChunk = 2048;     // units per Gram workgroup of the deep walk
 constexpr int kMaxRows = 1024;       // G * W rows per head unit
 constexpr int kMinTokPerBlock = 256;   // smallest token range of a score workgroup
 constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two)
@@ -70,6 +76,8 @@ struct Geometry {
   int32_t block;         // tokens per selection unit (1, or a block size up to 32)
   int32_t inplace;       // 1: compaction rearranges k / v in place (hole filling)
   int32_t head_alloc;    // NX_HEADS_UNIFORM / _GIVEN / _ALLOC
+  int32_t deep;          // 1: deep walk (walk rows stored whole, Gram in its own pass)
+  int32_t n_gc;          // Gram chunks per head unit (deep walk)
 };
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
@@ -88,8 +96,12 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
   L.a = off;      off = align256(off + hu * nm * sizeof(float));
   L.p = off;      off = align256(off + hu * size_t(g.walk > 0 ? g.walk : 1) * nm * sizeof(float));
-  L.gram = off;   off = align256(off + hu * g.n_t2 * kMaxWalk * kMaxWalk * sizeof(float));
-  L.coef = off;   off = align256(off + hu * kMaxWalk * sizeof(float));
+  // Gram partials: per score tile [kMaxWalk][kMaxWalk]; deep walk: per Gram
+  // chunk [H][H].
+  const size_t gram_floats = g.deep ? size_t(g.n_gc) * g.walk * g.walk
+                                    : size_t(g.n_t2) * kMaxWalk * kMaxWalk;
+  L.gram = off;   off = align256(off + hu * gram_floats * sizeof(float));
+  L.coef = off;   off = align256(off + hu * kMaxCoef * sizeof(float));
   L.keys = off;   off = align256(off + hu * nm * sizeof(uint64_t));
   L.selp = off;   off = align256(off + hu * g.n_kc * 2 * sizeof(uint64_t));
   // per-item histogram of the per-head allocation (left zeroed by every call)

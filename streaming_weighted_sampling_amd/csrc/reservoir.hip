@@ -82,8 +82,108 @@ __global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
     }
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t)
-      a.coef[size_t(hu) * kMaxWalk + t] = (t < g.walk) ? gam[t] / norm : 0.f;
+      a.coef[size_t(hu) * kMaxCoef + t] = (t < g.walk) ? gam[t] / norm : 0.f;
   }
+}
+
+// ---- deep walks (H > kMaxWalk or G * H > kMaxWalkRows) --------------------
+//
+// Gram partials of the stored walk rows: one workgroup per (chunk of
+// kGramChunk units, head unit) sums P_t[j] P_t'[j] (t' < t) and, on the
+// diagonal, P_t[j] (the row's L1 norm: the rows are non-negative) over its
+// units in ascending order, as the second sweep's own partials hold them; 64
+// units at a time staged in LDS (row stride 65 floats: the lanes of a
+// wavefront, on different rows t, read different banks).
+constexpr int kGramStage = 64;
+__global__ __launch_bounds__(256) void gram_deep_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.y, chunk = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int j0 = chunk * kGramChunk;
+  if (j0 >= u.nu) return;
+  const int j1 = min(j0 + kGramChunk, u.nu);
+  const int H = g.walk, n_pairs = H * (H + 1) / 2;
+  constexpr int kPairs = (kMaxWalkDeep * (kMaxWalkDeep + 1) / 2 + 255) / 256;
+  __shared__ float s_p[kMaxWalkDeep][kGramStage + 1];
+  const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
+  int pt[kPairs], pt2[kPairs];
+  float acc[kPairs];
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int p = threadIdx.x + 256 * k;
+    int t = 0;
+    while ((t + 1) * (t + 2) / 2 <= p) ++t;
+    pt[k] = t;
+    pt2[k] = p - t * (t + 1) / 2;
+    acc[k] = 0.f;
+  }
+  for (int c0 = j0; c0 < j1; c0 += kGramStage) {
+    const int cn = min(kGramStage, j1 - c0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < H * kGramStage; i += 256) {
+      const int t = i / kGramStage, jj = i - t * kGramStage;
+      s_p[t][jj] = jj < cn ? p_in[size_t(t) * g.max_tokens + c0 + jj] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      if (threadIdx.x + 256 * k < n_pairs) {
+        const float* x = s_p[pt[k]];
+        const float* y = s_p[pt2[k]];
+        float s0 = acc[k];
+        if (pt[k] == pt2[k]) {
+          for (int jj = 0; jj < cn; ++jj) s0 += x[jj];
+        } else {
+          for (int jj = 0; jj < cn; ++jj) s0 = fmaf(x[jj], y[jj], s0);
+        }
+        acc[k] = s0;
+      }
+    }
+  }
+  float* out = a.gram + (size_t(hu) * g.n_gc + chunk) * H * H;
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k)
+    if (threadIdx.x + 256 * k < n_pairs) out[pt[k] * H + pt2[k]] = acc[k];
+}
+
+// Walk coefficients of a deep walk, one workgroup per head unit: the chunk
+// partials summed in chunk order (one thread per Gram entry), then the walk
+// recurrence of section 2.2 Eq. (4) in its rank-1 form by one thread, with
+// the same fused multiply-adds as walk_coef_kernel.
+__global__ __launch_bounds__(256) void walk_coef_deep_kernel(const Args a) {
+  const Geometry& g = a.g;
+  const int hu = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  const int H = g.walk, n_pairs = H * (H + 1) / 2;
+  const int n_chunks = (u.nu + kGramChunk - 1) / kGramChunk;
+  __shared__ float s_gm[kMaxWalkDeep][kMaxWalkDeep + 1];
+  const float* gp = a.gram + size_t(hu) * g.n_gc * H * H;
+  for (int p = threadIdx.x; p < n_pairs; p += 256) {
+    int t = 0;
+    while ((t + 1) * (t + 2) / 2 <= p) ++t;
+    const int t2 = p - t * (t + 1) / 2;
+    float sum = 0.f;
+    for (int c = 0; c < n_chunks; ++c) sum += gp[size_t(c) * H * H + t * H + t2];
+    s_gm[t][t2] = sum;
+  }
+  __syncthreads();
+  __shared__ float s_gam[kMaxWalkDeep];
+  __shared__ float s_norm;
+  if (threadIdx.x == 0) {
+    float norm = 0.f;
+    for (int t = 0; t < H; ++t) {
+      float x = 1.f;
+      for (int t2 = 0; t2 < t; ++t2) x = fmaf(s_gam[t2], s_gm[t][t2], x);
+      s_gam[t] = x;
+      norm = fmaf(x, s_gm[t][t], norm);
+    }
+    s_norm = norm;
+  }
+  __syncthreads();
+  if (threadIdx.x < kMaxCoef)
+    a.coef[size_t(hu) * kMaxCoef + threadIdx.x] = int(threadIdx.x) < H ? s_gam[threadIdx.x] / s_norm : 0.f;
 }
 
 // w_j = a_j + lambda c~_j + eps r_j (section 2.2 Eqs. 2 and 5) with
@@ -98,6 +198,24 @@ __device__ __attribute__((always_inline)) inline float combine_weight(
     if (t < a.g.walk) cj = fmaf(s_coef[t], pv[t], cj);
   const float r = float(j) * ramp;
   return fmaf(a.eps_tie, r, fmaf(a.lambda, cj, aj));
+}
+
+// The same weight for walks deeper than kMaxWalk: the walk rows are read
+// eight at a time, and the multiply-adds run in the same order.
+__device__ inline float deep_weight(const Args& a, const float* s_coef, const float* a_in,
+                                    const float* p_in, float ramp, int j) {
+  float cj = 0.f;
+  for (int t0 = 0; t0 < a.g.walk; t0 += 8) {
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pv[i] = t0 + i < a.g.walk ? p_in[size_t(t0 + i) * a.g.max_tokens + j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (t0 + i < a.g.walk) cj = fmaf(s_coef[t0 + i], pv[i], cj);
+  }
+  const float r = float(j) * ramp;
+  return fmaf(a.eps_tie, r, fmaf(a.lambda, cj, a_in[j]));
 }
 
 // The fp64 key of token j with weight w (section 2.3 Eq. 6).  n = 1: ln(u)/w
@@ -149,11 +267,11 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
   if (!u.valid) return;
   const int j0 = chunk * kKeysPerBlock;
   if (j0 >= u.nu) return;
-  __shared__ float s_coef[kMaxWalk];
+  __shared__ float s_coef[kMaxCoef];
   __shared__ uint64_t s_or[kKeysThreads / 64], s_and[kKeysThreads / 64];
 
-  if (threadIdx.x < kMaxWalk)
-    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
+  if (threadIdx.x < kMaxCoef)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
   __syncthreads();
 
   const float* a_in = a.a + size_t(hu) * g.max_tokens;
@@ -177,6 +295,8 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     const int jc = in[i] ? j : j0;   // a valid token for the lanes past the end
     if (a.w_in != nullptr) {
       w[i] = a.w_in[ext + jc];
+    } else if (g.walk > kMaxWalk) {
+      w[i] = deep_weight(a, s_coef, a_in, p_in, ramp, jc);
     } else {
       // The same arithmetic as token_weight, loads first.
       float pv[kMaxWalk];
@@ -490,7 +610,7 @@ constexpr float kLn2f = 0.693147180559945309f;
 
 struct SelShared {
   SelCore core;
-  float coef[kMaxWalk];
+  float coef[kMaxCoef];
   int n_band, n_above;
   uint32_t cb;
   uint32_t band_idx[kBandCap];
@@ -503,6 +623,7 @@ struct SelShared {
 // serves the direct score and every walk row.)
 __device__ __attribute__((always_inline)) inline float token_weight(
     const Args& a, const float* s_coef, const float* a_in, const float* p_in, float ramp, int j) {
+  if (a.g.walk > kMaxWalk) return deep_weight(a, s_coef, a_in, p_in, ramp, j);
   float pv[kMaxWalk];
 #pragma unroll
   for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < a.g.walk ? p_in[size_t(t) * a.g.max_tokens + j] : 0.f;
@@ -640,9 +761,9 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   if (!u.valid) return;
   const int j0 = chunk * kKeysPerBlock;
   if (j0 >= u.nu) return;
-  __shared__ float s_coef[kMaxWalk];
-  if (threadIdx.x < kMaxWalk)
-    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
+  __shared__ float s_coef[kMaxCoef];
+  if (threadIdx.x < kMaxCoef)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
   __syncthreads();
   const int n = u.nu;
   const size_t ext = size_t(u.h) * n;
@@ -656,7 +777,7 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   // Computed weights in rows of a multiple of 4 floats: thread t takes tokens
   // j0 + 4t .. +3 with one 16-byte load per array (and one 16-byte code
   // store); otherwise tokens j0 + t + kKeysThreads i, one float at a time.
-  const bool vec = a.w_in == nullptr && (g.max_tokens & 3) == 0;
+  const bool vec = a.w_in == nullptr && g.walk <= kMaxWalk && (g.max_tokens & 3) == 0;
   auto tok = [&](int i) {
     return vec ? j0 + 4 * int(threadIdx.x) + i : j0 + int(threadIdx.x) + kKeysThreads * i;
   };
@@ -755,7 +876,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   SelCore& core = sh.core;
   const int tid = threadIdx.x;
 
-  if (tid < kMaxWalk) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
+  if (tid < kMaxCoef) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + tid] : 0.f;
   __syncthreads();
 
   const size_t ext = size_t(u.h) * u.nu;   // row of head h in [h_kv, n] exports
@@ -974,7 +1095,7 @@ __device__ __forceinline__ void for_codes(const uint32_t* codes, int n, int slot
 
 struct WideShared {
   SelCore core;
-  float coef[kMaxWalk];
+  float coef[kMaxCoef];
   int n_band, n_above;
   uint32_t cb;
   uint32_t band_idx[kBandCap];
@@ -991,7 +1112,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
   __shared__ WideShared sh;
   SelCore& core = sh.core;
   const int tid = threadIdx.x;
-  if (tid < kMaxWalk) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + tid] : 0.f;
+  if (tid < kMaxCoef) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + tid] : 0.f;
   __syncthreads();
   const size_t ext = size_t(u.h) * u.nu;
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
@@ -1129,7 +1250,14 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
 }  // namespace
 
 hipError_t launch_walk_coef(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(walk_coef_kernel, dim3(a.g.n_hu), dim3(64), 0, s, a);
+  if (a.g.deep) {
+    hipLaunchKernelGGL(gram_deep_kernel, dim3(a.g.n_gc, a.g.n_hu), dim3(256), 0, s, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(walk_coef_deep_kernel, dim3(a.g.n_hu), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(walk_coef_kernel, dim3(a.g.n_hu), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -1158,11 +1286,11 @@ __global__ __launch_bounds__(kKeysThreads) void head_codes_kernel(const Args a) 
   if (!u.valid) return;
   const int j0 = chunk * kKeysPerBlock;
   if (j0 >= u.nu) return;
-  __shared__ float s_coef[kMaxWalk];
+  __shared__ float s_coef[kMaxCoef];
   __shared__ uint32_t s_hist[kAllocBins];
   for (int b = threadIdx.x; b < kAllocBins; b += kKeysThreads) s_hist[b] = 0u;
-  if (threadIdx.x < kMaxWalk)
-    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxWalk + threadIdx.x] : 0.f;
+  if (threadIdx.x < kMaxCoef)
+    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
   __syncthreads();
   const int n = u.nu;
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + size_t(u.h) * n : nullptr,

@@ -392,6 +392,7 @@ constexpr int kWalkFast4Mid = 5;    // G = 4, 4 < H <= 6 (fewer Gram pairs per l
                                     // which keeps the kernel within 128 VGPRs)
 constexpr int kWalkFast4H3 = 6;     // G = 4, H = 3 exactly (no per-row depth tests)
 constexpr int kWalkFast8H3 = 7;     // G = 8, H = 3 exactly
+constexpr int kWalkGlobal = 8;      // deep walks: every row tile stores its P_t rows (no Gram here)
 
 // Pass 2 on one (head unit, tile) item.
 //
@@ -427,6 +428,8 @@ template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
 __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int tile, char* smem) {
   using GE = Geo<T, D>;
   constexpr bool kHasWalk = kWalk != kWalkNone;
+  constexpr bool kGlobal = kWalk == kWalkGlobal;
+  constexpr bool kHasGram = kHasWalk && !kGlobal;   // Gram partials formed in this pass
   constexpr int kExactH = kWalk == kWalkFast4H3 || kWalk == kWalkFast8H3 ? 3 : 0;
   constexpr bool kG8 = kWalk == kWalkFast8 || kWalk == kWalkFast8H3;   // walk rows span 8 output rows
   constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep ||
@@ -600,6 +603,62 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     }
   };
 
+  // Deep walks: P_t = W * (sum of its G rows) for the tokens of sub-tile st.
+  // Lane (nn, hh) holds rows 8q + 4hh + r (q, r < 4) in e[4q + r] and their
+  // quad sums in sq[q]; a group of G rows is then a sum of e's (G <= 2), a
+  // quad sum (G = 4), or quad sums of both halves (G >= 8, one swap).
+  auto store_walk_rows = [&](int mt, int st, const float (&e)[16], const float (&sq)[4]) {
+    const int G = g.group;
+    const int tok = t0 + 32 * st + nn;
+    const bool ok = tok < u.n;
+    // Group of rows rho0 .. rho0 + G - 1; every lane takes part (the block
+    // sums move values across lanes), lanes with mine set store.
+    auto put = [&](int rho0, float sum, bool mine) {
+      const int t = rho0 / G;
+      float v = wf * sum;
+      if (blk == 1) {
+        if (mine && ok && t < g.walk) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), v);
+      } else {
+        v = group_sum(ok ? v : 0.f, blk);
+        if (mine && lead && ok && t < g.walk)
+          p_out.stf(uint32_t((t * g.max_tokens + tok / blk) * 4), v);
+      }
+    };
+    if (G <= 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = mt * 32 + 8 * q + 4 * hh;
+        if (G == 4) {
+          put(r0, sq[q], true);
+        } else if (G == 2) {
+          put(r0, e[4 * q] + e[4 * q + 1], true);
+          put(r0 + 2, e[4 * q + 2] + e[4 * q + 3], true);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) put(r0 + r, e[4 * q + r], true);
+        }
+      }
+    } else {
+      // Sums of G / 8 consecutive quads (rows 8q .. 8q + 8 G/8 - 1 of one
+      // half), then the two halves added by one swap (both halves then hold
+      // the same sum, half 0 + half 1); half 0 stores.
+      const int span = G / 8;   // 1, 2 or 4 quads
+      float part[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[q] = sq[q];
+      if (span >= 2) { part[0] += part[1]; part[2] += part[3]; }
+      if (span >= 4) part[0] += part[2];
+#pragma unroll
+      for (int q = 0; q < 4; q += 1) {
+        if (q % span != 0) continue;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[q]),
+                                                         __float_as_uint(part[q]), false, false);
+        const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        put(mt * 32 + 8 * q, sum, hh == 0);
+      }
+    }
+  };
+
   sweep_tiles<T, D, GE::kSlotsProbs, 2, NW>(u, t0, n_sub, smem, role, a.k_stream_nt != 0,
                                            [&](int st, const char* cur) {
     // Lagged work on slots the previous barrier made visible: the LDS reads
@@ -670,6 +729,11 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
               put_walk(st, pt);
             }
           }
+        } else if constexpr (kGlobal) {
+          // Walk rows are rows 0 .. G*H - 1, G consecutive rows per window
+          // slot t (G <= 32 divides the tile's 32 rows): a tile that holds
+          // some of them sums each group and stores P_t of its 32 tokens.
+          if (mt * 32 < g.walk_rows) store_walk_rows(mt, st, e, sq);
         } else if constexpr (kWalk == kWalkLds) {
           // Walk rows are rows 0 .. G*H - 1: every row tile that holds some
           // of them (G*H may exceed one tile's 32 rows) leaves their values.
@@ -691,7 +755,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   });
   // Drain the lagged work (the sweep ends on a barrier).
   a_final(n_sub - 1);
-  if constexpr (kHasWalk) {
+  if constexpr (kHasGram) {
     if constexpr (kWalk == kWalkLds) {
       if (n_sub > 1) gram_step(n_sub - 2);
       walk_lds(n_sub - 1);
@@ -736,10 +800,13 @@ __global__ __launch_bounds__(kThreads) void score_combine_kernel(const Args a) {
 // Pass 2: one workgroup per (tile, head unit).
 // bf16 without blocks and with a register-lean walk form is held to 128 VGPRs
 // (4 wavefronts per SIMD), which it reaches without spilling; fp32, blocks and
-// the LDS and deep walk forms need more and run at 2-3.
+// the LDS, deep and global walk forms need more and run at 2-3.
 template <typename T, int kWalk, bool kBlocks, int MPW>
 constexpr int probs_min_waves() {
-  return MPW == 1 && sizeof(T) == 2 && !kBlocks && kWalk != kWalkLds && kWalk != kWalkFast4Deep ? 4 : 1;
+  return MPW == 1 && sizeof(T) == 2 && !kBlocks && kWalk != kWalkLds && kWalk != kWalkFast4Deep &&
+                 kWalk != kWalkGlobal
+             ? 4
+             : 1;
 }
 
 template <typename T, int D, int MPW, int NW, int kWalk, bool kBlocks>
@@ -754,6 +821,7 @@ void score_probs_kernel(const Args a) {
 
 int walk_mode(const Geometry& g) {
   if (g.walk == 0) return kWalkNone;
+  if (g.deep) return kWalkGlobal;
   if (g.walk == 3 && g.group == 4) return kWalkFast4H3;
   if (g.walk == 3 && g.group == 8) return kWalkFast8H3;
   if (g.walk <= 4 && g.group == 4) return kWalkFast4;
@@ -790,6 +858,9 @@ void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
       break;
     case kWalkFast4Mid:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4Mid, kBlocks>), grid, dim3(64 * NW), 0, s, a);
+      break;
+    case kWalkGlobal:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkGlobal, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     default:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkLds, kBlocks>), grid, dim3(64 * NW), 0, s, a);

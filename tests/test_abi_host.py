@@ -136,7 +136,11 @@ def test_host_validation_codes(lib):
     assert _step(lib, _desc(), q=None) == _lib.NX_EINVAL
     assert _step(lib, _desc(head_dim=96)) == _lib.NX_EUNSUPPORTED
     assert _step(lib, _desc(dtype=7)) == _lib.NX_EUNSUPPORTED
-    assert _step(lib, _desc(), h=9) == _lib.NX_EUNSUPPORTED              # walk depth > 8
+    assert _step(lib, _desc(window=80), h=65) == _lib.NX_EUNSUPPORTED    # walk depth > 64
+    # deep walks (H > 8) need G <= 32: 64 query heads on one KV head is G = 64
+    assert _step(lib, _desc(n_q_heads=64, n_kv_heads=1, window=12), h=9) == _lib.NX_EUNSUPPORTED
+    assert _step(lib, _desc(), h=9) == _lib.NX_EWORKSPACE                 # deep walk: valid
+    assert _step(lib, _desc(), h=32) == _lib.NX_EWORKSPACE                # H = W
     assert _step(lib, _desc(n_q_heads=64, n_kv_heads=2)) == _lib.NX_EUNSUPPORTED  # 1024 rows
     assert _step(lib, _desc(kv_head_stride=100)) == _lib.NX_EINVAL       # stride < N*D
     # outputs overlapping inputs

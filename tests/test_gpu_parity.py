@@ -632,6 +632,17 @@ SCORE_CASES = [
     ("one_token", 4, 2, 128, 4, torch.bfloat16, 1, 2),
     # 64 KV heads x 3 tiles of 2048 tokens, ragged tail: many workgroups per head unit
     ("many_heads_ragged", 256, 64, 128, 32, torch.bfloat16, 5000, 3),
+    # deep walks (section 2.2 Eq. 4 with any H <= W): walk rows stored by the
+    # second sweep, Gram in its own pass
+    ("deep_g4_h12", 32, 8, 128, 32, torch.bfloat16, 3000, 12),
+    ("deep_g4_h32_every_row", 32, 8, 128, 32, torch.bfloat16, 2100, 32),
+    ("deep_g8_h16", 64, 8, 128, 32, torch.bfloat16, 1800, 16),
+    ("deep_g16_h5_80_walk_rows", 128, 8, 128, 8, torch.bfloat16, 1500, 5),
+    ("deep_g1_h40", 8, 8, 128, 48, torch.bfloat16, 2600, 40),
+    ("deep_g2_h64", 16, 8, 64, 64, torch.bfloat16, 2000, 64),
+    ("deep_g32_h9", 32, 1, 128, 16, torch.bfloat16, 1000, 9),
+    ("deep_f32_g4_h10", 8, 2, 64, 16, torch.float32, 1500, 10),
+    ("deep_ragged_many_chunks", 32, 8, 128, 32, torch.bfloat16, 9001, 20),
 ]
 
 
@@ -729,6 +740,43 @@ def test_evict_step_forced_slots_and_edges():
     _end_to_end("llama3_8b_layer", n=1, budget=1)
     _end_to_end("llama3_8b_layer", n=999, budget=1)
     _end_to_end("tiny_mha_f32", walk=0)
+
+
+@pytest.mark.parametrize("walk", [12, 32])
+def test_evict_step_deep_walk(walk):
+    """Walks deeper than the register-held forms (H = 12, and H = W = 32: every
+    window row), end to end."""
+    _end_to_end("llama3_8b_layer", n=4096, walk=walk, seed=13, layer=2, step=4)
+
+
+@pytest.mark.parametrize("block,walk,n", [(32, 16, 4096), (8, 24, 3001)])
+def test_block_mode_deep_walk(block, walk, n):
+    """Blocks with a deep walk: the stored walk rows are block sums, the Gram
+    pass runs over block units."""
+    wl = WORKLOADS["llama3_8b_layer"]
+    cfg = _cfg(wl.h_q, wl.h_kv, wl.head_dim, wl.window, block=block)
+    d = gen_layer(wl, device=DEV, n_tokens=n)
+    nu = cfg.units(n)
+    budget = max(1, round(nu / 5))
+    ws = _ws(cfg, n, 1, walk)
+    w_gpu = torch.full((wl.h_kv, nu), float("nan"), device=DEV)
+    keep, ok, ov = nx.nx_evict_step(cfg, d["q"], d["k"], d["v"], n, budget, walk, 6,
+                                    workspace=ws, layer=1, step=3, out_w=w_gpu)
+    nx.nx_read_device_status(cfg, ws)
+    qh, dt = gc.host(d["q"])
+    kh, _ = gc.host(d["k"])
+    vh, _ = gc.host(d["v"])
+    ref = nexus.evict_step(qh, kh, vh, budget, walk, 6, dtype=dt, layer=1, step=3, block=block)
+    _, on_gpu_w = nexus.select_from_weights(w_gpu.cpu().numpy(), budget, 6, layer=1, step=3)
+    for h in range(wl.h_kv):
+        gc.assert_weights_close(w_gpu[h].cpu().numpy(), ref["w"][h], f"block {block} head {h}")
+        got = gc.check_keep_valid(keep[h].cpu().numpy(), nu, budget)
+        np.testing.assert_array_equal(got, on_gpu_w[h])
+        gc.assert_kept_matches_oracle(got, ref["keep"][h], ref["keys"][h], min(budget, nu),
+                                      f"block {block} head {h}")
+        rows = np.concatenate([np.arange(b * block, min(b * block + block, n)) for b in got])
+        assert gc.rows_equal(ok[h][:len(rows)], d["k"][h], rows)
+        assert gc.rows_equal(ov[h][:len(rows)], d["v"][h], rows)
 
 
 def test_evict_step_is_deterministic():
