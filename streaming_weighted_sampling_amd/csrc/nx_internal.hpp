@@ -95,7 +95,7 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
   L.a = off;      off = align256(off + hu * nm * sizeof(float));
-  L.p = off;      off = align256(off + hu * size_t(g.walk > 0 ? g.walk : 1) * nm * sizeof(float));
+  L.p = off;      off = align256(off + hu * size_t(g.walk) * nm * sizeof(float));   // none for H = 0
   // Gram partials: per score tile [kMaxWalk][kMaxWalk]; deep walk: per Gram
   // chunk [H][H].
   const size_t gram_floats = g.deep ? size_t(g.n_gc) * g.walk * g.walk
