@@ -866,7 +866,11 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   if (__syncthreads_or(nonfinite) && threadIdx.x == 0) raise_status(a, kStatusNonFinite);
 }
 
+// kPer codes per lane (1024 kPer >= the call's units): small head units take
+// fewer register slots, and every per-slot loop and the write scan shrink.
+template <int kPer>
 __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a) {
+  static_assert(kPer >= 4 && kPer <= kPer && (kPer * kSelWaves) % 64 == 0, "slot count");
   const Geometry& g = a.g;
   const int hu = blockIdx.x;
   const HeadUnit u = head_unit(a, hu);
@@ -889,11 +893,11 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     return;
   }
   // This lane's estimate codes (written by estimate_keys_kernel).
-  uint32_t code[kFusedPer];
+  uint32_t code[kPer];
   if (estimate) {
     const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
 #pragma unroll
-    for (int i = 0; i < kFusedPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int j = tid + kSelThreads * i;
       code[i] = j < n ? codes[j] : 0u;
     }
@@ -906,7 +910,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     // Radix select on the estimate codes.
     uint32_t v_or = 0, v_and = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < kFusedPer; ++i)
+    for (int i = 0; i < kPer; ++i)
       if (tid + kSelThreads * i < n) { v_or |= code[i]; v_and &= code[i]; }
 #pragma unroll
     for (int mm = 32; mm >= 1; mm >>= 1) {
@@ -925,7 +929,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
       sh.cb = 0xFFFFFFFFu;
     }
     __syncthreads();
-    sel_passes(core, kFusedPer, [&](int i) { return uint64_t(code[i]) | 0xFFFFFFFF00000000ull; },
+    sel_passes(core, kPer, [&](int i) { return uint64_t(code[i]) | 0xFFFFFFFF00000000ull; },
                [&](int i) { return tid + kSelThreads * i < n; });
     if (!core.done) {
       if (tid == 0) raise_status(a, kStatusBadItem);
@@ -938,7 +942,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
       uint32_t mn = 0xFFFFFFFFu;
       const uint64_t prefix = core.prefix, mask = core.mask;
 #pragma unroll
-      for (int i = 0; i < kFusedPer; ++i)
+      for (int i = 0; i < kPer; ++i)
         if (tid + kSelThreads * i < n && ((uint64_t(code[i]) | 0xFFFFFFFF00000000ull) & mask) == prefix)
           mn = min(mn, code[i]);
 #pragma unroll
@@ -958,7 +962,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     }
     int above = 0;
 #pragma unroll
-    for (int i = 0; i < kFusedPer; ++i) {
+    for (int i = 0; i < kPer; ++i) {
       const int j = tid + kSelThreads * i;
       if (j < n) {
         if (code[i] > hi) {
@@ -969,7 +973,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
         }
       }
     }
-    for (int c = tid; c < kFusedMaxTokens / 32; c += kSelThreads) sh.chosen[c] = 0;
+    for (int c = tid; c < kPer * kSelThreads / 32; c += kSelThreads) sh.chosen[c] = 0;
     atomicAdd(&sh.n_above, above);
     __syncthreads();
     m = sh.n_band;
@@ -1030,21 +1034,21 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   // per (round, wave) counts, one exclusive scan over them in token order.
   uint32_t kmask = 0;
 #pragma unroll
-  for (int r = 0; r < kFusedPer; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const int j = r * kSelThreads + tid;
     if (j < n && (code[r] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u))) kmask |= 1u << r;
   }
   const int lane = tid & 63, wave = tid >> 6;
   const uint64_t below_lane = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int r = 0; r < kFusedPer; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const uint64_t bal = __ballot((kmask >> r) & 1u);
     if (lane == 0) sh.round_cnt[r * kSelWaves + wave] = __popcll(bal);
   }
   __syncthreads();
   if (tid < 64) {
     // 512 counts in (round, wave) order, eight per lane: exclusive scan.
-    constexpr int kPerLane = kFusedPer * kSelWaves / 64;
+    constexpr int kPerLane = kPer * kSelWaves / 64;
     int loc[kPerLane], sum = 0;
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += sh.round_cnt[lane * kPerLane + q]; }
@@ -1060,7 +1064,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   }
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kFusedPer; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     const uint64_t bal = __ballot((kmask >> r) & 1u);
     if ((kmask >> r) & 1u) {
       const int pos = sh.round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
@@ -1700,8 +1704,14 @@ hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
 
 hipError_t launch_sample_select(const Args& a, hipStream_t s) {
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
-  if (max_units <= kFusedMaxTokens)
-    hipLaunchKernelGGL(sample_select_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  if (max_units <= 4 * kSelThreads)
+    hipLaunchKernelGGL(sample_select_kernel<4>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  else if (max_units <= 8 * kSelThreads)
+    hipLaunchKernelGGL(sample_select_kernel<8>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  else if (max_units <= 16 * kSelThreads)
+    hipLaunchKernelGGL(sample_select_kernel<16>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  else if (max_units <= kFusedMaxTokens)
+    hipLaunchKernelGGL(sample_select_kernel<kFusedPer>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   else
     hipLaunchKernelGGL(sample_select_wide_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
