@@ -308,3 +308,68 @@ def test_streaming_decode_with_allocated_budgets(inplace):
                 np.testing.assert_array_equal(vl[l, h, :kept + A], exp_v[:kept + A])
         drift = drift or len(set(post.ravel().tolist())) > 1
     assert drift, "the allocation never moved budget between heads"
+
+
+def test_allocated_budgets_with_a_deep_walk():
+    """Allocated per-head budgets on the weights of a deep walk (H = 16: walk
+    rows stored by the second sweep, Gram pass): the budgets equal the
+    oracle's allocation on the exported weights, the kept sets the oracle's
+    selection on them, and the weights the pure oracle's within 1e-3."""
+    n = 4096
+    wl, lay = _layer(n)
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
+                         head_alloc=nx.NX_HEADS_ALLOC, head_floor=40)
+    B = n // 5
+    k, v, keep, ok, ov, hb, w = _run_batch(cfg, wl, lay, n, B, 2 * B, 16)
+    w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, 16, w)
+    np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, 40, cap=2 * B))
+
+
+def test_streaming_decode_deep_walk_inplace():
+    """Three in-place append-64 / evict events with a deep walk (H = 12) and
+    allocated per-head budgets: every event against the oracle on the
+    device's pre-event cache."""
+    from streaming_weighted_sampling_amd.stream import StreamingCache
+    wl = WORKLOADS["llama3_8b_layer"]
+    L, n0, A, B, floor, seed, walk = 1, 1500, 64, 300, 20, 9, 12
+    cap = 2 * B
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
+                         head_alloc=nx.NX_HEADS_ALLOC, head_floor=floor)
+    sc = StreamingCache(cfg, L, max(n0, cap + A), B, A, walk, seed=seed, device=DEV,
+                        inplace=True, export_w=True, head_cap=cap)
+    g = torch.Generator(device="cpu").manual_seed(31)
+    k0 = torch.randn((L, wl.h_kv, n0, wl.head_dim), generator=g).to(torch.bfloat16)
+    k0 = k0 * torch.linspace(0.4, 2.5, wl.h_kv).view(1, -1, 1, 1).to(torch.bfloat16)
+    sc.load(k0.to(DEV), torch.randn_like(k0).to(DEV), n0)
+    for step in range(3):
+        sc.q.copy_(torch.randn(sc.q.shape, generator=g).to(torch.bfloat16))
+        sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g).to(torch.bfloat16))
+        sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g).to(torch.bfloat16))
+        pre = sc.head_tokens().numpy()
+        kp, vp = (gc.host(t)[0] for t in sc.live())
+        sc.step()
+        nx.nx_read_device_status(sc.cfg, sc.ws)
+        post = sc.head_tokens().numpy()
+        hb = sc.head_budget.cpu().numpy()[0]
+        kl, _ = (gc.host(t)[0] for t in sc.live())
+        app_k = gc.host(sc.app_k)[0]
+        counts = pre[0]
+        w_all = sc.weights(0).cpu().numpy()
+        w_gpu = [w_all[h, :c] for h, c in enumerate(counts)]
+        np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, floor, cap=cap))
+        _, on_gpu_w = nexus.select_from_weights(w_gpu, 0, seed, layer=0, step=step,
+                                                head_budgets=hb)
+        qh, dt = gc.host(sc.q[0])
+        ref = nexus.evict_step(qh, [kp[0, h, :c] for h, c in enumerate(counts)],
+                               [vp[0, h, :c] for h, c in enumerate(counts)], B, walk, seed,
+                               dtype=dt, layer=0, step=step, head_budgets=hb)
+        keep = sc.keep[0].cpu().numpy()
+        for h, c in enumerate(counts):
+            kept = min(int(hb[h]), int(c))
+            what = f"step {step} head {h}"
+            np.testing.assert_array_equal(keep[h, :kept], on_gpu_w[h], err_msg=what)
+            gc.assert_weights_close(w_gpu[h], ref["w"][h], what)
+            gc.assert_kept_matches_oracle(keep[h, :kept], ref["keep"][h], ref["keys"][h], kept, what)
+            assert post[0, h] == kept + A
+            exp_k = nexus.compact_inplace(kp[0, h], keep[h, :kept], app_k[0, h])
+            np.testing.assert_array_equal(kl[0, h, :kept + A], exp_k[:kept + A])
