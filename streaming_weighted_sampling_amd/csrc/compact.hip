@@ -11,6 +11,8 @@
 // Loads and stores go through buffer resources sized to the head's rows.
 // Loads and stores are non-temporal: every source row is read once, and the
 // compacted cache is consumed by later decode steps, not by this event.
+#include <algorithm>
+
 #include "nx_device.hpp"
 
 namespace nx {
@@ -123,24 +125,48 @@ __device__ __forceinline__ bool fill_holes(const HeadUnit& u, int kept, Keep kee
   const uint32_t head_bytes = uint32_t(max(u.n, kept + u.n_append)) * kRowBytes;
   const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);
   const int col = threadIdx.x % kPerRow;
+  constexpr int kPasses = kCompactRows / kRowsPerPass;
+  static_assert(kPasses * kRowsPerPass == kCompactRows, "whole passes");
   bool bad = false;
   for (int m0 = blockIdx.x * kCompactRows; m0 < movers; m0 += gridDim.x * kCompactRows) {
-    for (int r = threadIdx.x / kPerRow; r < kCompactRows; r += kRowsPerPass) {
-      const int j = m0 + r;
-      if (j >= movers) break;
-      const int src = keep(c + j);
-      // last i < c with keep[i] - i <= j
-      int l = 0, h = c;
-      while (l < h) {
-        const int mid = (l + h) >> 1;
-        if (keep(mid) - mid <= j) l = mid + 1; else h = mid;
+    // Every pass's source and hole first (LDS searches), then all loads, then
+    // all stores: one memory round trip per block instead of one per pass.
+    int src[kPasses], hole[kPasses];
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+      const int j = m0 + int(threadIdx.x) / kPerRow + q * kRowsPerPass;
+      src[q] = -1;
+      if (j < movers) {
+        const int sr = keep(c + j);
+        // last i < c with keep[i] - i <= j
+        int l = 0, h = c;
+        while (l < h) {
+          const int mid = (l + h) >> 1;
+          if (keep(mid) - mid <= j) l = mid + 1; else h = mid;
+        }
+        const int ho = j + l;
+        if (sr < kept || sr >= u.n || ho >= kept) {
+          bad = true;
+        } else {
+          src[q] = sr;
+          hole[q] = ho;
+        }
       }
-      const int hole = j + l;
-      if (src < kept || src >= u.n || hole >= kept) { bad = true; continue; }
-      const uint4 xk = kb.ld16<kNonTemporal>(uint32_t(src * kRowBytes + 16 * col));
-      const uint4 xv = vb.ld16<kNonTemporal>(uint32_t(src * kRowBytes + 16 * col));
-      kb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xk);
-      vb.st16<kNonTemporal>(uint32_t(hole * kRowBytes + 16 * col), xv);
+    }
+    uint4 xk[kPasses], xv[kPasses];
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+      if (src[q] >= 0) {
+        xk[q] = kb.ld16<kNonTemporal>(uint32_t(src[q] * kRowBytes + 16 * col));
+        xv[q] = vb.ld16<kNonTemporal>(uint32_t(src[q] * kRowBytes + 16 * col));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+      if (src[q] >= 0) {
+        kb.st16<kNonTemporal>(uint32_t(hole[q] * kRowBytes + 16 * col), xk[q]);
+        vb.st16<kNonTemporal>(uint32_t(hole[q] * kRowBytes + 16 * col), xv[q]);
+      }
     }
   }
   return bad;
@@ -160,7 +186,20 @@ __global__ __launch_bounds__(kThreads) void kv_fill_holes_kernel(const Args a) {
   bool bad;
   if (u.kept <= kLdsKeep) {
     // The searches read the keep array many times: stage it in LDS once.
-    for (int i = threadIdx.x; i < u.kept; i += kThreads) s_keep[i] = u.keep[i];
+    // (eight loads per thread in flight per round)
+    for (int i0 = threadIdx.x; i0 < u.kept; i0 += 8 * kThreads) {
+      int32_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q * kThreads;
+        v[q] = i < u.kept ? u.keep[i] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q * kThreads;
+        if (i < u.kept) s_keep[i] = v[q];
+      }
+    }
     __syncthreads();
     if (b == 1)
       bad = fill_holes<kRowBytes>(u, kept, [](int i) { return s_keep[i]; });
@@ -192,13 +231,26 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const Args a) {
   const Buf kb(u.k, head_bytes), vb(u.v, head_bytes);
   const Buf kab(u.app_k, app_bytes), vab(u.app_v, app_bytes);
   const int col = threadIdx.x % kPerRow;
+  constexpr int kPasses = kCompactRows / kRowsPerPass;
   for (int r0 = blockIdx.x * kCompactRows; r0 < u.n_append; r0 += gridDim.x * kCompactRows) {
-    for (int r = threadIdx.x / kPerRow; r < kCompactRows && r0 + r < u.n_append; r += kRowsPerPass) {
-      const uint32_t off = uint32_t((r0 + r) * kRowBytes + 16 * col);
-      const uint4 xk = kab.ld16<kNonTemporal>(off);
-      const uint4 xv = vab.ld16<kNonTemporal>(off);
-      kb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xk);
-      vb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xv);
+    uint4 xk[kPasses], xv[kPasses];
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+      const int r = r0 + int(threadIdx.x) / kPerRow + q * kRowsPerPass;
+      if (r < u.n_append) {
+        const uint32_t off = uint32_t(r * kRowBytes + 16 * col);
+        xk[q] = kab.ld16<kNonTemporal>(off);
+        xv[q] = vab.ld16<kNonTemporal>(off);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kPasses; ++q) {
+      const int r = r0 + int(threadIdx.x) / kPerRow + q * kRowsPerPass;
+      if (r < u.n_append) {
+        const uint32_t off = uint32_t(r * kRowBytes + 16 * col);
+        kb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xk[q]);
+        vb.st16<kNonTemporal>(uint32_t(kept * kRowBytes) + off, xv[q]);
+      }
     }
   }
 }
@@ -217,10 +269,16 @@ hipError_t launch_kv_compact(const Args& a, hipStream_t s) {
   }
   if (a.g.inplace) {
     // Movers are at most the kept rows; the appended rows are max_out_rows - kept.
-    NX_LAUNCH(kv_fill_holes_kernel, grid)
+    // Both kernels stride their row blocks by the grid, and in the streaming
+    // steady state only a few blocks per head unit hold work (the rows past
+    // the kept count): about 2048 workgroups in all, not one per possible row
+    // block, whose launch alone cost more than the moves.
+    const int per_hu = std::max(1, std::min<int>(grid.x, 2048 / std::max(1, a.g.n_hu)));
+    const dim3 g2(per_hu, a.g.n_hu);
+    NX_LAUNCH(kv_fill_holes_kernel, g2)
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    NX_LAUNCH(kv_append_kernel, grid)
+    NX_LAUNCH(kv_append_kernel, g2)
   } else {
     NX_LAUNCH(kv_compact_kernel, grid)
   }
