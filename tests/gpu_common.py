@@ -120,11 +120,6 @@ def oracle_map(fn, jobs, workers=None):
             return list(ex.map(fn, jobs))
 
 
-def overlap_fraction(keep_a, keep_b):
-    a, b = set(np.asarray(keep_a).tolist()), set(np.asarray(keep_b).tolist())
-    return len(a & b) / max(len(b), 1)
-
-
 def check_keep_valid(keep, n_tokens, budget):
     keep = np.asarray(keep)
     kept = min(budget, n_tokens)
