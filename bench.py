@@ -237,16 +237,17 @@ def roofline_obj(amount, unit, peak, bound, kernel_ms, launches, kernel, traffic
             "traffic_source": None if traffic is None else traffic["source"]}
 
 
-def steady(wl, args):
+def steady_run(wl, compact, steps, warmup):
     """Streaming steady state: every event holds N = B + A rows per head, keeps
-    B and appends A new rows (queries and new rows synthetic, fixed)."""
+    B and appends A new rows (queries and new rows synthetic, fixed).  Returns
+    (ms per event, per-stage ms per launch, rows per head)."""
     from streaming_weighted_sampling_amd.stream import StreamingCache
     dev = "cuda"
     L, B, A = wl.n_layers, wl.budget, wl.stream_append
     n = B + A
     cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16)
     sc = StreamingCache(cfg, L, n, B, A, wl.walk_iters, seed=0, device=dev,
-                        inplace=args.compact == "inplace")
+                        inplace=compact == "inplace")
     q32 = torch.empty(wl.h_q, wl.window, wl.head_dim, device=dev)
     k32 = torch.empty(wl.h_kv, n, wl.head_dim, device=dev)
     v32 = torch.empty(wl.h_kv, n, wl.head_dim, device=dev)
@@ -258,23 +259,31 @@ def steady(wl, args):
         k0[layer].copy_(k32)
         v0[layer].copy_(v32)
     sc.load(k0, v0, n)
+    del k0, v0
     g = torch.Generator(device=dev).manual_seed(5)
     sc.app_k.copy_(torch.randn(sc.app_k.shape, generator=g, device=dev).to(torch.bfloat16))
     sc.app_v.copy_(torch.randn(sc.app_v.shape, generator=g, device=dev).to(torch.bfloat16))
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         sc.step()
     torch.cuda.synchronize()
     nx.profile_enable(True)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         sc.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     nx.profile_enable(False)
     stages = nx.profile_read()
     nx.nx_read_device_status(sc.cfg, sc.ws)
-    ms = (t1 - t0) * 1e3 / args.steps
-    units = L * wl.h_kv
+    ms = (t1 - t0) * 1e3 / steps
+    return ms, {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items() if v[1]}, n
+
+
+def steady(wl, args):
+    """The streaming steady state as its own JSON line (--steady)."""
+    ms, stages, n = steady_run(wl, args.compact, args.steps, args.warmup)
+    units = wl.n_layers * wl.h_kv
+    B, A = wl.budget, wl.stream_append
     print(json.dumps({
         "metric": METRIC, "value": round(units * n / (ms * 1e-3), 1), "unit": "KV tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -282,7 +291,7 @@ def steady(wl, args):
         "data": "synthetic",
         "config": {"workload": f"llama3_8b_stream32 steady-state event N={n} -> {B} + {A} "
                                f"appended, 32 layers x 8 KV heads", "compact": args.compact},
-        "stage_ms_per_launch": {k: round(v[0] / max(v[1], 1), 4) for k, v in stages.items() if v[1]},
+        "stage_ms_per_launch": stages,
     }))
 
 
@@ -406,6 +415,19 @@ def headline(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg, args.block)
+    if args.n_avg == 1 and args.block == 1 and args.heads == "uniform":
+        # Context, not the metric: the same model's streaming steady state (every
+        # later event of the streaming workload), N = B + A -> B kept + A appended.
+        del data
+        torch.cuda.empty_cache()
+        st = {}
+        for mode in ("copy", "inplace"):
+            ms, stages, _ = steady_run(wl, mode, 10, 2)
+            st[mode] = {"ms_per_event": round(ms, 4), "kv_compact_ms": stages.get("kv_compact")}
+        out["streaming_steady_state"] = {
+            "events": f"N={wl.budget + wl.stream_append} -> {wl.budget} kept + {wl.stream_append} "
+                      f"appended per KV head, 32 layers x 8 KV heads, 10 timed events each",
+            **st}
     print(json.dumps(out))
 
 
