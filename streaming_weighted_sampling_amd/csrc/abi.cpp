@@ -46,6 +46,11 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   nx_status st = check_desc(d);
   if (st != NX_OK) return st;
   if (max_tokens < 1 || max_tokens > kMaxTokens || n_items < 1) return NX_EINVAL;
+  // The per-head workspace rows (a, the walk rows, the keys) hold max_tokens
+  // rounded up to a multiple of 4, so that every row starts 16-B aligned and
+  // the token passes read them 16 bytes at a time whatever N the call has.
+  g->max_n = max_tokens;
+  max_tokens = (max_tokens + 3) & ~3;
   // One KV head's rows (and each per-head workspace array) stay below 2 GB so
   // 32-bit buffer offsets address them.
   if (walk < 0 || walk > d->window) return NX_EINVAL;

@@ -164,7 +164,7 @@ __device__ inline HeadUnit head_unit(const Args& a, int hu) {
   // The weight export keeps the item's row stride (units of n_tokens).
   r.w_out = u.out_w ? u.out_w + int64_t(h) * ((u.n_tokens + g.block - 1) / g.block) : nullptr;
   r.tokens_out = u.head_tokens_out ? u.head_tokens_out + h : nullptr;
-  bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_tokens && r.n >= 1 && r.n <= u.n_tokens &&
+  bool ok = u.n_tokens >= 1 && u.n_tokens <= g.max_n && r.n >= 1 && r.n <= u.n_tokens &&
             u.budget >= 1 &&
             u.n_append >= 0 && r.budget >= 1 && r.budget <= r.cap &&
             (a.n_sink + a.n_recent <= r.budget || r.budget >= r.nu) &&

@@ -67,7 +67,8 @@ struct Geometry {
   int32_t h_q, h_kv, group, head_dim, window, walk, rows, rows_pad, walk_rows;
   int32_t dtype;
   int32_t n_hu;          // head units = n_items * h_kv
-  int32_t max_tokens;
+  int32_t max_tokens;    // workspace row length: the call's max_tokens rounded up to 4
+  int32_t max_n;         // the call's max_tokens (bound on every item's n_tokens)
   int32_t max_out_rows;  // compaction grid rows per head unit
   int32_t tok_per_block; // tokens per score workgroup for this call
   int32_t n_tmax;        // score tiles per head unit at tok_per_block (for max_tokens)
