@@ -340,6 +340,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
 
 // Exclusive prefix count of `flag` over the block (ascending thread order);
 // returns the block total in *total.  Uses s_cnt[kSelWaves].
+template <int kThr = kSelThreads>
 __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t m = __ballot(flag);
@@ -347,7 +348,7 @@ __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
   if (lane == 0) s_cnt[wave] = __popcll(m);
   __syncthreads();
   int off = 0, tot = 0;
-  for (int w = 0; w < kSelWaves; ++w) {
+  for (int w = 0; w < (kThr / 64); ++w) {
     const int c = s_cnt[w];
     off += w < wave ? c : 0;
     tot += c;
@@ -362,28 +363,28 @@ __device__ inline int block_rank(bool flag, int* s_cnt, int* total) {
 // (r0 + r) * kSelThreads + tid), with per-lane keep masks, per (round,
 // wavefront) counts and one exclusive scan per group.  round_cnt holds
 // kFusedPer * kSelWaves ints; every thread of the block calls this.
-template <typename KeepAt>
+template <int kThr = kSelThreads, typename KeepAt>
 __device__ inline void write_ascending(int n, int budget, int32_t* keep, int* round_cnt,
                                        int* group_total, KeepAt&& keep_at) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below_lane = (1ull << lane) - 1ull;
-  const int slots = (n + kSelThreads - 1) / kSelThreads;
+  const int slots = (n + kThr - 1) / kThr;
   int base = 0;
   for (int r0 = 0; r0 < slots; r0 += kFusedPer) {
     uint32_t kmask = 0;
 #pragma unroll
     for (int r = 0; r < kFusedPer; ++r) {
-      const int j = (r0 + r) * kSelThreads + tid;
+      const int j = (r0 + r) * kThr + tid;
       if (j < n && keep_at(j)) kmask |= 1u << r;
     }
 #pragma unroll
     for (int r = 0; r < kFusedPer; ++r) {
       const uint64_t bal = __ballot((kmask >> r) & 1u);
-      if (lane == 0) round_cnt[r * kSelWaves + wave] = __popcll(bal);
+      if (lane == 0) round_cnt[r * (kThr / 64) + wave] = __popcll(bal);
     }
     __syncthreads();
     if (tid < 64) {
-      constexpr int kPerLane = kFusedPer * kSelWaves / 64;
+      constexpr int kPerLane = kFusedPer * (kThr / 64) / 64;
       int loc[kPerLane], sum = 0;
 #pragma unroll
       for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += round_cnt[lane * kPerLane + q]; }
@@ -403,8 +404,8 @@ __device__ inline void write_ascending(int n, int budget, int32_t* keep, int* ro
     for (int r = 0; r < kFusedPer; ++r) {
       const uint64_t bal = __ballot((kmask >> r) & 1u);
       if ((kmask >> r) & 1u) {
-        const int pos = base + round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
-        if (pos < budget) keep[pos] = (r0 + r) * kSelThreads + tid;
+        const int pos = base + round_cnt[r * (kThr / 64) + wave] + __popcll(bal & below_lane);
+        if (pos < budget) keep[pos] = (r0 + r) * kThr + tid;
       }
     }
     base += *group_total;
@@ -528,18 +529,19 @@ __device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Vali
 
 // Selection over codes in global memory (keys[j], j < n): the common prefix
 // from (o, an), the radix passes, then the kept indices in ascending order.
+template <int kThr = kSelThreads>
 __device__ inline void select_global(const Args& a, const HeadUnit& u, const uint64_t* keys,
                                      uint64_t o, uint64_t an, SelCore& sh) {
   const int n = u.nu, tid = threadIdx.x;
   if (tid == 0) sel_init(sh, o, an, n, u.budget);
   __syncthreads();
-  const int slots = (n + kSelThreads - 1) / kSelThreads;
-  sel_passes<8>(sh, slots, [&](int i) { return keys[tid + kSelThreads * i]; },
-             [&](int i) { return tid + kSelThreads * i < n; });
+  const int slots = (n + kThr - 1) / kThr;
+  sel_passes<8>(sh, slots, [&](int i) { return keys[tid + kThr * i]; },
+             [&](int i) { return tid + kThr * i < n; });
   if (!sh.done) {
     // Unreachable with consistent inputs; report and keep the oldest tokens.
     if (tid == 0) raise_status(a, kStatusBadItem);
-    for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+    for (int j = tid; j < u.budget; j += kThr) u.keep[j] = j;
     return;
   }
   const uint64_t prefix = sh.prefix, mask = sh.mask;
@@ -552,10 +554,10 @@ __device__ inline void select_global(const Args& a, const HeadUnit& u, const uin
     // scan rounds from the end and find the index where the count reaches need.
     int seen = 0;
     for (int r = slots - 1; r >= 0; --r) {
-      const int j = r * kSelThreads + tid;
+      const int j = r * kThr + tid;
       const bool eq = j < n && (keys[j] & mask) == prefix;
       int tot;
-      const int below = block_rank(eq, sh.cnt, &tot);
+      const int below = block_rank<kThr>(eq, sh.cnt, &tot);
       const int above = tot - below - (eq ? 1 : 0);   // ties at larger j in this round
       if (eq && seen + above + 1 == need) sh.cut = j;
       seen += tot;
@@ -564,7 +566,7 @@ __device__ inline void select_global(const Args& a, const HeadUnit& u, const uin
     __syncthreads();
   }
   const int cut = sh.cut;
-  write_ascending(n, u.budget, u.keep, sh.round_cnt, &sh.group_total, [&](int j) {
+  write_ascending<kThr>(n, u.budget, u.keep, sh.round_cnt, &sh.group_total, [&](int j) {
     const uint64_t top = keys[j] & mask;
     return top > prefix || (top == prefix && (!ties || j >= cut));
   });
@@ -866,11 +868,15 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   if (__syncthreads_or(nonfinite) && threadIdx.x == 0) raise_status(a, kStatusNonFinite);
 }
 
-// kPer codes per lane (1024 kPer >= the call's units): small head units take
-// fewer register slots, and every per-slot loop and the write scan shrink.
-template <int kPer>
-__global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a) {
-  static_assert(kPer >= 4 && kPer <= kPer && (kPer * kSelWaves) % 64 == 0, "slot count");
+// kPer codes per lane on kThr lanes (kThr kPer >= the call's units): small
+// head units take fewer register slots, and every per-slot loop and the write
+// scan shrink; 512 lanes let two workgroups share a CU.
+template <int kPer, int kThr = kSelThreads>
+__global__ __launch_bounds__(kThr) __attribute__((amdgpu_waves_per_eu(4)))
+void sample_select_kernel(const Args a) {
+  static_assert(kPer >= 4 && kPer <= kFusedPer && kThr >= 256 && kThr <= kSelThreads &&
+                    (kPer * (kThr / 64)) % 64 == 0,
+                "slot count");
   const Geometry& g = a.g;
   const int hu = blockIdx.x;
   const HeadUnit u = head_unit(a, hu);
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   const bool estimate = uses_estimate(a, u);
   if (u.keep != nullptr && u.budget >= n && a.keys_out == nullptr) {
-    for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+    for (int j = tid; j < n; j += kThr) u.keep[j] = j;
     return;
   }
   // This lane's estimate codes (written by estimate_keys_kernel).
@@ -898,7 +904,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int j = tid + kSelThreads * i;
+      const int j = tid + kThr * i;
       code[i] = j < n ? codes[j] : 0u;
     }
   }
@@ -911,7 +917,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     uint32_t v_or = 0, v_and = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (tid + kSelThreads * i < n) { v_or |= code[i]; v_and &= code[i]; }
+      if (tid + kThr * i < n) { v_or |= code[i]; v_and &= code[i]; }
 #pragma unroll
     for (int mm = 32; mm >= 1; mm >>= 1) {
       v_or |= uint32_t(__shfl_xor(int(v_or), mm, 64));
@@ -921,7 +927,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     __syncthreads();
     if (tid == 0) {
       uint64_t o = 0, an = 0xFFFFFFFFull;
-      for (int w = 0; w < kSelWaves; ++w) { o |= core.red_or[w]; an &= core.red_and[w]; }
+      for (int w = 0; w < (kThr / 64); ++w) { o |= core.red_or[w]; an &= core.red_and[w]; }
       // The codes enter the 64-bit passes with their upper 32 bits set.
       sel_init(core, o | 0xFFFFFFFF00000000ull, an | 0xFFFFFFFF00000000ull, n, u.budget);
       sh.n_band = 0;
@@ -930,10 +936,10 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     }
     __syncthreads();
     sel_passes(core, kPer, [&](int i) { return uint64_t(code[i]) | 0xFFFFFFFF00000000ull; },
-               [&](int i) { return tid + kSelThreads * i < n; });
+               [&](int i) { return tid + kThr * i < n; });
     if (!core.done) {
       if (tid == 0) raise_status(a, kStatusBadItem);
-      for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
+      for (int j = tid; j < u.budget; j += kThr) u.keep[j] = j;
       return;
     }
     // The B-th largest estimate is the smallest code of the boundary bin
@@ -943,7 +949,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
       const uint64_t prefix = core.prefix, mask = core.mask;
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (tid + kSelThreads * i < n && ((uint64_t(code[i]) | 0xFFFFFFFF00000000ull) & mask) == prefix)
+        if (tid + kThr * i < n && ((uint64_t(code[i]) | 0xFFFFFFFF00000000ull) & mask) == prefix)
           mn = min(mn, code[i]);
 #pragma unroll
       for (int mm = 32; mm >= 1; mm >>= 1) mn = min(mn, uint32_t(__shfl_xor(int(mn), mm, 64)));
@@ -963,7 +969,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     int above = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int j = tid + kSelThreads * i;
+      const int j = tid + kThr * i;
       if (j < n) {
         if (code[i] > hi) {
           ++above;
@@ -973,7 +979,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
         }
       }
     }
-    for (int c = tid; c < kPer * kSelThreads / 32; c += kSelThreads) sh.chosen[c] = 0;
+    for (int c = tid; c < kPer * kThr / 32; c += kThr) sh.chosen[c] = 0;
     atomicAdd(&sh.n_above, above);
     __syncthreads();
     m = sh.n_band;
@@ -985,7 +991,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     // Exact keys of every token into the workspace, then the global selection.
     uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
     uint64_t o = 0, an = ~0ull;
-    for (int j = tid; j < n; j += kSelThreads) {
+    for (int j = tid; j < n; j += kThr) {
       const double key = exact_key(a, u, j, ws(a, sh.coef, j), k0, k1);
       if (a.keys_out != nullptr) a.keys_out[ext + j] = key;
       const uint64_t c = key_code(key);
@@ -995,7 +1001,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     }
     if (u.keep == nullptr) return;
     if (u.budget >= n) {
-      for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
+      for (int j = tid; j < n; j += kThr) u.keep[j] = j;
       return;
     }
 #pragma unroll
@@ -1006,20 +1012,20 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
     if ((tid & 63) == 0) { core.red_or[tid >> 6] = o; core.red_and[tid >> 6] = an; }
     __syncthreads();
     uint64_t ob = 0, anb = ~0ull;
-    for (int w = 0; w < kSelWaves; ++w) { ob |= core.red_or[w]; anb &= core.red_and[w]; }
+    for (int w = 0; w < (kThr / 64); ++w) { ob |= core.red_or[w]; anb &= core.red_and[w]; }
     __syncthreads();
-    select_global(a, u, keys, ob, anb, core);
+    select_global<kThr>(a, u, keys, ob, anb, core);
     return;
   }
 
   // Exact keys of the band, one list entry per lane, then the exact order
   // inside the band ((code, index) descending): the first need2 win.
-  for (int t = tid; t < m; t += kSelThreads) {
+  for (int t = tid; t < m; t += kThr) {
     const int j = int(sh.band_idx[t]);
     sh.band_code[t] = key_code(exact_key(a, u, j, ws(a, sh.coef, j), k0, k1));
   }
   __syncthreads();
-  for (int t = tid; t < m; t += kSelThreads) {
+  for (int t = tid; t < m; t += kThr) {
     const uint64_t ct = sh.band_code[t];
     const uint32_t it = sh.band_idx[t];
     int rank = 0;
@@ -1035,7 +1041,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   uint32_t kmask = 0;
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
-    const int j = r * kSelThreads + tid;
+    const int j = r * kThr + tid;
     if (j < n && (code[r] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u))) kmask |= 1u << r;
   }
   const int lane = tid & 63, wave = tid >> 6;
@@ -1043,12 +1049,12 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const uint64_t bal = __ballot((kmask >> r) & 1u);
-    if (lane == 0) sh.round_cnt[r * kSelWaves + wave] = __popcll(bal);
+    if (lane == 0) sh.round_cnt[r * (kThr / 64) + wave] = __popcll(bal);
   }
   __syncthreads();
   if (tid < 64) {
     // 512 counts in (round, wave) order, eight per lane: exclusive scan.
-    constexpr int kPerLane = kPer * kSelWaves / 64;
+    constexpr int kPerLane = kPer * (kThr / 64) / 64;
     int loc[kPerLane], sum = 0;
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += sh.round_cnt[lane * kPerLane + q]; }
@@ -1067,8 +1073,8 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_kernel(const Args a
   for (int r = 0; r < kPer; ++r) {
     const uint64_t bal = __ballot((kmask >> r) & 1u);
     if ((kmask >> r) & 1u) {
-      const int pos = sh.round_cnt[r * kSelWaves + wave] + __popcll(bal & below_lane);
-      if (pos < u.budget) u.keep[pos] = r * kSelThreads + tid;
+      const int pos = sh.round_cnt[r * (kThr / 64) + wave] + __popcll(bal & below_lane);
+      if (pos < u.budget) u.keep[pos] = r * kThr + tid;
     }
   }
 }
@@ -1704,6 +1710,18 @@ hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
 
 hipError_t launch_sample_select(const Args& a, hipStream_t s) {
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
+  // Many head units of up to 16384 units: 512-lane workgroups with twice the
+  // codes per lane, so that two share a CU and hide each other's latency.
+  constexpr int kHalf = kSelThreads / 2;
+  if (a.g.n_hu >= 512 && max_units <= kFusedPer * kHalf) {
+    if (max_units <= 8 * kHalf)
+      hipLaunchKernelGGL((sample_select_kernel<8, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
+    else if (max_units <= 16 * kHalf)
+      hipLaunchKernelGGL((sample_select_kernel<16, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
+    else
+      hipLaunchKernelGGL((sample_select_kernel<kFusedPer, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
+    return hipGetLastError();
+  }
   if (max_units <= 4 * kSelThreads)
     hipLaunchKernelGGL(sample_select_kernel<4>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   else if (max_units <= 8 * kSelThreads)

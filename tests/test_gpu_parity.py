@@ -812,3 +812,50 @@ def test_stats_overflow_fallback():
     nx.nx_read_device_status(cfg, ws)
     ref = gc.oracle_weights(q, k, n, 2, 4)
     gc.assert_weights_close(w[0].cpu().numpy(), ref[0], "overflow fallback")
+
+
+@pytest.mark.parametrize("n_hi", [4000, 8000, 16000])
+def test_many_small_head_units_select(n_hi):
+    """Batches of 512 head units (64 items x 8 KV heads) with ragged N up to
+    4000, 8000 and 16000: the selection runs 512-lane workgroups (8, 16 and 32
+    codes per lane).  Every head's kept set equals the oracle's selection on
+    the weights the batch exported, and each item's first head matches the
+    pure oracle at the stated bar."""
+    h_q, h_kv, d, W, walk = 32, 8, 128, 32, 3
+    cfg = _cfg(h_q, h_kv, d, W)
+    rng = np.random.default_rng(n_hi)
+    lens = rng.integers(n_hi // 4, n_hi + 1, size=64)
+    lens[0] = n_hi
+    items, bufs = [], []
+    for i, n in enumerate(lens.tolist()):
+        q, k = _synthetic(h_q, h_kv, d, W, torch.bfloat16, n, seed=7000 + i)
+        v = torch.randn(k.shape, device=DEV).bfloat16()
+        B = max(1, round(n / 5))
+        keep = torch.full((h_kv, B), -7, dtype=torch.int32, device=DEV)
+        ok = torch.empty(h_kv, B, d, dtype=torch.bfloat16, device=DEV)
+        ov = torch.empty_like(ok)
+        w = torch.full((h_kv, n), float("nan"), device=DEV)
+        bufs.append((q, k, v, keep, w, n, B))
+        items.append(dict(q=q, k=k, v=v, keep=keep, out_k=ok, out_v=ov, kv_head_stride=n * d,
+                          out_head_stride=B * d, n_tokens=n, budget=B, layer=i % 7, seq_id=i,
+                          out_w=w))
+    units = nx.make_units(items, device=DEV)
+    ws = _ws(cfg, n_hi, len(items), walk)
+    nx.nx_evict_batch(cfg, units, len(items), n_hi, walk, 21, workspace=ws, step=4,
+                      max_out_rows=round(n_hi / 5))
+    nx.nx_read_device_status(cfg, ws)
+    for i, (q, k, v, keep, w, n, B) in enumerate(bufs):
+        wh = w.cpu().numpy()
+        _, on_w = nexus.select_from_weights(wh, B, 21, layer=i % 7, step=4, seq_id=i)
+        kh = keep.cpu().numpy()
+        for h in range(h_kv):
+            np.testing.assert_array_equal(kh[h], on_w[h], err_msg=f"item {i} head {h}")
+        if i % 8 == 0:
+            qh, dt = gc.host(q)
+            kk, _ = gc.host(k)
+            vv, _ = gc.host(v)
+            ref = nexus.evict_step(qh, kk, vv, B, walk, 21, dtype=dt, layer=i % 7, step=4,
+                                   seq_id=i, heads=[0])
+            gc.assert_weights_close(wh[0], ref["w"][0], f"item {i}")
+            gc.assert_kept_matches_oracle(kh[0], ref["keep"][0], ref["keys"][0], min(B, n),
+                                          f"item {i}")
