@@ -88,7 +88,7 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->max_out_rows = max_tokens;
   g->n_t1 = (max_tokens + kMinTokPerBlock - 1) / kMinTokPerBlock;
   g->n_t2 = g->n_t1;
-  // Tokens per score workgroup: the widest power of two in [256, 2048] that
+  // Tokens per score workgroup: the widest power of two in [128, 2048] that
   // still gives >= 2048 workgroups per pass (8 per CU): fewer tile partials
   // and less per-workgroup setup without starving the chip.
   int32_t tpb = kMaxTokPerBlock;

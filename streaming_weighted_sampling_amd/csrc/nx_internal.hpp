@@ -37,7 +37,7 @@ constexpr int kMaxWalkDeep = 64;
 constexpr int kMaxCoef = kMaxWalkDeep;   // walk coefficient slots per head unit
 constexpr int kGramChunk = 2048;     // units per Gram workgroup of the deep walk
 constexpr int kMaxRows = 1024;       // G * W rows per head unit
-constexpr int kMinTokPerBlock = 256;   // smallest token range of a score workgroup
+constexpr int kMinTokPerBlock = 128;   // smallest token range of a score workgroup
 constexpr int kMaxTokPerBlock = 2048;  // largest (chosen per call, power of two)
 constexpr int kKeysPerBlock = 1024;  // tokens per reservoir_keys workgroup
 constexpr int kCompactRows = 64;     // kept rows per kv_compact workgroup
