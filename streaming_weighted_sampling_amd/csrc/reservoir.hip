@@ -1710,26 +1710,19 @@ hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
 
 hipError_t launch_sample_select(const Args& a, hipStream_t s) {
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
-  // Many head units of up to 16384 units: 512-lane workgroups with twice the
-  // codes per lane, so that two share a CU and hide each other's latency.
+  // Units of up to 16384 tokens: 512-lane workgroups (8, 16 or 32 codes per
+  // lane), two to a CU, so that a batch of many head units overlaps their
+  // latencies; up to 32768 the 1024-lane kernel holds 32 codes per lane; above
+  // that the codes stay in memory.
   constexpr int kHalf = kSelThreads / 2;
-  if (a.g.n_hu >= 512 && max_units <= kFusedPer * kHalf) {
-    if (max_units <= 8 * kHalf)
-      hipLaunchKernelGGL((sample_select_kernel<8, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
-    else if (max_units <= 16 * kHalf)
-      hipLaunchKernelGGL((sample_select_kernel<16, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
-    else
-      hipLaunchKernelGGL((sample_select_kernel<kFusedPer, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
-    return hipGetLastError();
-  }
-  if (max_units <= 4 * kSelThreads)
-    hipLaunchKernelGGL(sample_select_kernel<4>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
-  else if (max_units <= 8 * kSelThreads)
-    hipLaunchKernelGGL(sample_select_kernel<8>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
-  else if (max_units <= 16 * kSelThreads)
-    hipLaunchKernelGGL(sample_select_kernel<16>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+  if (max_units <= 8 * kHalf)
+    hipLaunchKernelGGL((sample_select_kernel<8, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
+  else if (max_units <= 16 * kHalf)
+    hipLaunchKernelGGL((sample_select_kernel<16, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
+  else if (max_units <= kFusedPer * kHalf)
+    hipLaunchKernelGGL((sample_select_kernel<kFusedPer, kHalf>), dim3(a.g.n_hu), dim3(kHalf), 0, s, a);
   else if (max_units <= kFusedMaxTokens)
-    hipLaunchKernelGGL(sample_select_kernel<kFusedPer>, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
+    hipLaunchKernelGGL((sample_select_kernel<kFusedPer>), dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   else
     hipLaunchKernelGGL(sample_select_wide_kernel, dim3(a.g.n_hu), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
