@@ -415,7 +415,7 @@ def headline(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, data, args.cpu_seconds, args.n_avg, args.block)
-    if args.n_avg == 1 and args.block == 1 and args.heads == "uniform":
+    if args.n_avg == 1 and args.block == 1 and args.heads == "uniform" and not args.no_steady:
         # Context, not the metric: the same model's streaming steady state (every
         # later event of the streaming workload), N = B + A -> B kept + A appended.
         del data
@@ -656,6 +656,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the headline part of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-steady", action="store_true",
+                    help="leave out the streaming steady-state context of the headline line "
+                         "(profiling runs of the headline event alone)")
     ap.add_argument("--steady", action="store_true",
                     help="time the streaming steady-state event (N = B + 256 -> B, 32 layers) "
                          "through StreamingCache instead of the N = 32768 event")
