@@ -97,6 +97,7 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
   g->deep = deep ? 1 : 0;
+  g->packed = packed_rows(g->walk, g->group, g->block, deep) ? 1 : 0;
   g->n_gc = (max_tokens + kGramChunk - 1) / kGramChunk;
   return NX_OK;
 }

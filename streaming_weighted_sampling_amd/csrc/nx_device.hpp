@@ -102,6 +102,24 @@ __device__ inline void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The second sweep's per-token outputs of head unit hu: a_j at a[j * ts] and
+// walk row P_t[j] at p[t * rs + j * ts] (planar rows, or 16-byte records
+// (a, P_1, P_2, P_3) when the geometry packs them).
+struct ScoreRows {
+  const float* a;
+  const float* p;
+  int ts;
+  size_t rs;
+};
+__device__ inline ScoreRows score_rows(const Args& a, int hu) {
+  const size_t nm = size_t(a.g.max_tokens);
+  if (a.g.packed) {
+    const float* rec = a.a + size_t(hu) * nm * 4;
+    return {rec, rec + 1, 4, 1};
+  }
+  return {a.a + size_t(hu) * nm, a.p + size_t(hu) * a.g.walk * nm, 1, nm};
+}
+
 // One KV head of one (sequence, layer) item, resolved on the device.
 struct HeadUnit {
   const char* q;       // first query row of the GQA group (query head h * G)

@@ -79,7 +79,15 @@ struct Geometry {
   int32_t head_alloc;    // NX_HEADS_UNIFORM / _GIVEN / _ALLOC
   int32_t deep;          // 1: deep walk (walk rows stored whole, Gram in its own pass)
   int32_t n_gc;          // Gram chunks per head unit (deep walk)
+  int32_t packed;        // 1: a_j and the walk rows as one 16-B record per token (packed_rows)
 };
+
+// Walks of exactly three rows at token granularity with G = 4 or 8 (the
+// second sweep's exact-depth kernels): the second sweep writes a_j, P_1[j],
+// P_2[j], P_3[j] as one 16-byte record per token instead of four planar rows.
+inline bool packed_rows(int walk, int group, int block, bool deep) {
+  return walk == 3 && (group == 4 || group == 8) && block <= 1 && !deep;
+}
 
 // Workspace carving (byte offsets from the workspace base, 256-B aligned).
 struct WsLayout {
@@ -95,8 +103,13 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.status = off; off = align256(off + 256);
   L.part1 = off;  off = align256(off + hu * g.n_t1 * g.rows_pad * 2 * sizeof(float));
   L.beta = off;   off = align256(off + hu * g.rows_pad * sizeof(float));
-  L.a = off;      off = align256(off + hu * nm * sizeof(float));
-  L.p = off;      off = align256(off + hu * size_t(g.walk) * nm * sizeof(float));   // none for H = 0
+  if (g.packed) {   // records [n_hu][max_tokens][4]
+    L.a = off;    off = align256(off + hu * nm * 4 * sizeof(float));
+    L.p = L.a;
+  } else {
+    L.a = off;    off = align256(off + hu * nm * sizeof(float));
+    L.p = off;    off = align256(off + hu * size_t(g.walk) * nm * sizeof(float));   // none for H = 0
+  }
   // Gram partials: per score tile [kMaxWalk][kMaxWalk]; deep walk: per Gram
   // chunk [H][H].
   const size_t gram_floats = g.deep ? size_t(g.n_gc) * g.walk * g.walk
@@ -105,7 +118,7 @@ inline WsLayout ws_layout(const Geometry& g) {
   L.coef = off;   off = align256(off + hu * kMaxCoef * sizeof(float));
   L.keys = off;   off = align256(off + hu * nm * sizeof(uint64_t));
   L.selp = off;   off = align256(off + hu * g.n_kc * 2 * sizeof(uint64_t));
-  // per-item histogram of the per-head allocation (left zeroed by every call)
+  // per-item histogram of the per-head allocation (cleared by each call that builds it)
   L.ahist = off;
   if (g.head_alloc == NX_HEADS_ALLOC) off = align256(off + (hu / g.h_kv) * kAllocBins * sizeof(uint32_t));
   // per head unit: its boundary-bin codes and (count above, candidate count)
@@ -136,8 +149,8 @@ struct Args {
   uint32_t* status;
   float* part1;    // [n_hu][n_t1][rows_pad][2]: (max, sum) in log2 units
   float* beta;     // [n_hu][rows_pad]
-  float* a;        // [n_hu][max_tokens]: direct score
-  float* p;        // [n_hu][walk][max_tokens]
+  float* a;        // [n_hu][max_tokens]: direct score (packed: [n_hu][max_tokens][4] records)
+  float* p;        // [n_hu][walk][max_tokens] (packed: unused)
   float* gram;     // [n_hu][n_t2][kMaxWalk * kMaxWalk]
   float* coef;     // [n_hu][kMaxWalk]: gamma_t / ||C||_1
   uint64_t* keys;  // [n_hu][max_tokens], order-preserving bits of the fp64 key

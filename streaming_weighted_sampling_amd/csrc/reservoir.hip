@@ -27,6 +27,7 @@
 // draws, or the top-B limit), the same radix select on the codes (held in
 // registers up to 32768 units, re-read from memory above), and exact fp64
 // keys only for the tokens within +-2^-9 of the boundary estimate.
+#include <algorithm>
 #include <type_traits>
 
 #include "nx_device.hpp"
@@ -190,12 +191,15 @@ __global__ __launch_bounds__(256) void walk_coef_deep_kernel(const Args a) {
 // c~_j = sum_t coef_t P_t[j] and r_j = j ramp, ramp = 1/(N-1).  Every fused
 // multiply-add is written out, so each kernel that forms a token's weight gets
 // the same bits (a weight export equals the weight the keys were drawn on).
+// kW >= 0: the walk depth, fixed at compile time (the same multiply-adds).
+template <int kW = -1>
 __device__ __attribute__((always_inline)) inline float combine_weight(
     const Args& a, const float* s_coef, float aj, const float (&pv)[kMaxWalk], int j, float ramp) {
+  const int walk = kW >= 0 ? kW : a.g.walk;
   float cj = 0.f;
 #pragma unroll
   for (int t = 0; t < kMaxWalk; ++t)
-    if (t < a.g.walk) cj = fmaf(s_coef[t], pv[t], cj);
+    if (t < walk) cj = fmaf(s_coef[t], pv[t], cj);
   const float r = float(j) * ramp;
   return fmaf(a.eps_tie, r, fmaf(a.lambda, cj, aj));
 }
@@ -274,8 +278,7 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
   __syncthreads();
 
-  const float* a_in = a.a + size_t(hu) * g.max_tokens;
-  const float* p_in = a.p + size_t(hu) * g.walk * g.max_tokens;
+  const ScoreRows sr = score_rows(a, hu);
   uint64_t* keys = a.keys + size_t(hu) * g.max_tokens;
   const size_t ext = size_t(u.h) * u.nu;   // row of head h in [h_kv, n] exports
   const float ramp = u.nu > 1 ? 1.f / float(u.nu - 1) : 0.f;
@@ -296,13 +299,13 @@ __global__ __launch_bounds__(kKeysThreads) void reservoir_keys_kernel(const Args
     if (a.w_in != nullptr) {
       w[i] = a.w_in[ext + jc];
     } else if (g.walk > kMaxWalk) {
-      w[i] = deep_weight(a, s_coef, a_in, p_in, ramp, jc);
+      w[i] = deep_weight(a, s_coef, sr.a, sr.p, ramp, jc);
     } else {
       // The same arithmetic as token_weight, loads first.
       float pv[kMaxWalk];
 #pragma unroll
-      for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < g.walk ? p_in[size_t(t) * g.max_tokens + jc] : 0.f;
-      w[i] = combine_weight(a, s_coef, a_in[jc], pv, jc, ramp);
+      for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < g.walk ? sr.p[t * sr.rs + size_t(jc) * sr.ts] : 0.f;
+      w[i] = combine_weight(a, s_coef, sr.a[size_t(jc) * sr.ts], pv, jc, ramp);
     }
   }
 #pragma unroll
@@ -624,23 +627,22 @@ struct SelShared {
 // (All loads are issued before the first use, so one memory round trip
 // serves the direct score and every walk row.)
 __device__ __attribute__((always_inline)) inline float token_weight(
-    const Args& a, const float* s_coef, const float* a_in, const float* p_in, float ramp, int j) {
-  if (a.g.walk > kMaxWalk) return deep_weight(a, s_coef, a_in, p_in, ramp, j);
+    const Args& a, const float* s_coef, const ScoreRows& sr, float ramp, int j) {
+  if (a.g.walk > kMaxWalk) return deep_weight(a, s_coef, sr.a, sr.p, ramp, j);
   float pv[kMaxWalk];
 #pragma unroll
-  for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < a.g.walk ? p_in[size_t(t) * a.g.max_tokens + j] : 0.f;
-  return combine_weight(a, s_coef, a_in[j], pv, j, ramp);
+  for (int t = 0; t < kMaxWalk; ++t) pv[t] = t < a.g.walk ? sr.p[t * sr.rs + size_t(j) * sr.ts] : 0.f;
+  return combine_weight(a, s_coef, sr.a[size_t(j) * sr.ts], pv, j, ramp);
 }
 
 // Weight of token j of this head unit (given weights, or a + lambda c~ + ramp).
 struct WeightSrc {
   const float* w_in;   // [h_kv, n] row of this head, or nullptr
-  const float* a_in;
-  const float* p_in;
+  ScoreRows sr;
   float ramp;
   __device__ __attribute__((always_inline)) float operator()(const Args& a, const float* s_coef,
                                                              int j) const {
-    return w_in != nullptr ? w_in[j] : token_weight(a, s_coef, a_in, p_in, ramp, j);
+    return w_in != nullptr ? w_in[j] : token_weight(a, s_coef, sr, ramp, j);
   }
 };
 
@@ -655,26 +657,25 @@ __device__ inline float f32_decode(uint32_t c) {
 
 // Estimate code of the key ln(u)/w: 0 for w <= 0 (key -inf), ~0 for a forced
 // slot (+inf), else the code of -s.  With u = m 2^-53 (m = k53 + 1) and
-// E = -ln u, x = (2^53 - m) 2^-53:
-//   x < 2^-7:    E = x (1 + x/2 + x^2/3 + x^3/4)        (relative error < 1e-7)
-//   otherwise:   E = -log2(u) ln 2, u rounded to fp32 (within 2^-23): since
-//                E >= 2^-7 here the rounding costs at most 2^-16 relative, and
-//                v_log_f32 is within one ulp of its output (measured on gfx950
-//                down to inputs 2^-24 below 1).
-// Then s = (eE - ew) + log2(mE / mw) from the exact binary exponents and
-// mantissas of E and w (subnormal w included).  |error of s| < 5e-5, twenty
-// times inside kBand.
+// x = 1 - u = (2^53 - m) 2^-53 (both exact in 53 bits), E = -ln u is taken in
+// the form E = x * ln(uf) / (uf - 1) with uf = u rounded to fp32 (Goldberg's
+// log1p identity: ln(w)/(w - 1) varies slowly, so the rounding of uf costs a
+// relative 2^-24 at most, for every u).  uf - 1 is exact for uf >= 1/2 and
+// within an ulp below; v_log_f32 is within one ulp of its output (measured on
+// gfx950 down to inputs 2^-24 below 1), so E carries a relative error of a few
+// 2^-24.  uf = 1 (x < 2^-25) gives E = x, whose neglected x^2/2 is below 2^-26
+// relative.  Then s = (eE - ew) + log2(mE / mw) from the exact binary
+// exponents and mantissas of E and w (subnormal w included).  |error of s| <
+// 5e-5, twenty times inside kBand.  One formula for every u keeps the
+// wavefront on one path.
 // E = -ln u of the uniform from words (x0, x1), as above; exactly 0 for u = 1.
 __device__ inline float neg_log_u(uint32_t x0, uint32_t x1) {
   const uint64_t m = (((uint64_t(x0) << 32) | uint64_t(x1)) >> 11) + 1;
   const uint64_t d = (1ull << 53) - m;
-  if (d == 0) return 0.f;
-  if (d < (1ull << 46)) {
-    const float x = float(uint32_t(d)) * 0x1p-53f + float(uint32_t(d >> 32)) * 0x1p-21f;
-    return x * (1.f + x * (0.5f + x * (0.333333343f + x * 0.25f)));
-  }
   const float uf = (float(uint32_t(m >> 21)) * 0x1p21f + float(uint32_t(m) & 0x1FFFFFu)) * 0x1p-53f;
-  return -__builtin_amdgcn_logf(uf) * kLn2f;
+  const float x = (float(uint32_t(d >> 21)) * 0x1p21f + float(uint32_t(d) & 0x1FFFFFu)) * 0x1p-53f;
+  const float r = -__builtin_amdgcn_logf(uf) * kLn2f * __builtin_amdgcn_rcpf(1.f - uf);
+  return (uf == 1.f || x == 0.f) ? x : x * r;   // u = 1: m = 2^53 does not fit uf's formula
 }
 
 // Code of -s, s = log2(X) - log2(w) for a key -X/w (X > 0; X = 0, key 0, is
@@ -756,6 +757,9 @@ __device__ inline bool uses_estimate(const Args& a, const HeadUnit& u) {
 // Estimate codes of kKeysPerBlock tokens of one head unit (many workgroups
 // per head unit, like reservoir_keys), stored as uint32 at the start of the
 // head unit's key array; also the non-finite check and the weight export.
+// kW >= 0: the call's walk depth at compile time (weights computed in rows of
+// a multiple of 4 floats).
+template <int kW>
 __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args a) {
   const Geometry& g = a.g;
   const int hu = blockIdx.y, chunk = blockIdx.x;
@@ -769,30 +773,49 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   __syncthreads();
   const int n = u.nu;
   const size_t ext = size_t(u.h) * n;
-  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
-                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, score_rows(a, hu),
+                     n > 1 ? 1.f / float(n - 1) : 0.f};
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   const bool estimate = uses_estimate(a, u);
   uint32_t* codes = reinterpret_cast<uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
   constexpr int kPer = kKeysPerBlock / kKeysThreads;
   static_assert(kPer == 4, "one 16-byte vector per array and thread");
-  // Computed weights in rows of a multiple of 4 floats: thread t takes tokens
-  // j0 + 4t .. +3 with one 16-byte load per array (and one 16-byte code
-  // store); otherwise tokens j0 + t + kKeysThreads i, one float at a time.
-  const bool vec = a.w_in == nullptr && g.walk <= kMaxWalk && (g.max_tokens & 3) == 0;
+  // Computed weights in planar rows of a multiple of 4 floats: thread t takes
+  // tokens j0 + 4t .. +3 with one 16-byte load per row (and one 16-byte code
+  // store); otherwise tokens j0 + t + kKeysThreads i: one float at a time, or
+  // for packed rows one 16-byte record (a, P_1, P_2, P_3) per token, so that
+  // each load instruction reads 1 KB in one piece.
+  const bool packed = kW == 3 && g.packed;
+  const bool vec = !packed && (kW >= 0 || (a.w_in == nullptr && g.walk <= kMaxWalk &&
+                                           (g.max_tokens & 3) == 0));
   auto tok = [&](int i) {
     return vec ? j0 + 4 * int(threadIdx.x) + i : j0 + int(threadIdx.x) + kKeysThreads * i;
   };
   float w[kPer];
-  if (vec) {
+  if (packed) {
+    const float4* rec = reinterpret_cast<const float4*>(ws.sr.a);
+    float4 r[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tok(i);
+      r[i] = rec[j < n ? j : j0];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int j = tok(i);
+      float pe[kMaxWalk] = {r[i].y, r[i].z, r[i].w};
+      w[i] = combine_weight<kW>(a, s_coef, r[i].x, pe, j < n ? j : j0, ws.ramp);
+    }
+  } else if (vec) {
     const int jv = j0 + 4 * int(threadIdx.x);
     const int jl = jv < n ? jv : j0;   // rows hold max_tokens >= n rounded up to 4 floats
-    const float4 av = *reinterpret_cast<const float4*>(ws.a_in + jl);
+    const float4 av = *reinterpret_cast<const float4*>(ws.sr.a + jl);
+    const int walk = kW >= 0 ? kW : g.walk;
     float4 pv[kMaxWalk];
 #pragma unroll
     for (int t = 0; t < kMaxWalk; ++t)
-      pv[t] = t < g.walk ? *reinterpret_cast<const float4*>(ws.p_in + size_t(t) * g.max_tokens + jl)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      pv[t] = t < walk ? *reinterpret_cast<const float4*>(ws.sr.p + t * ws.sr.rs + jl)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     const float ae[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -800,7 +823,7 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
 #pragma unroll
       for (int t = 0; t < kMaxWalk; ++t)
         pe[t] = e == 0 ? pv[t].x : e == 1 ? pv[t].y : e == 2 ? pv[t].z : pv[t].w;
-      w[e] = combine_weight(a, s_coef, ae[e], pe, jl + e, ws.ramp);
+      w[e] = combine_weight<kW>(a, s_coef, ae[e], pe, jl + e, ws.ramp);
     }
   } else {
 #pragma unroll
@@ -890,8 +913,8 @@ void sample_select_kernel(const Args a) {
   __syncthreads();
 
   const size_t ext = size_t(u.h) * u.nu;   // row of head h in [h_kv, n] exports
-  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
-                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, score_rows(a, hu),
+                     n > 1 ? 1.f / float(n - 1) : 0.f};
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   const bool estimate = uses_estimate(a, u);
   if (u.keep != nullptr && u.budget >= n && a.keys_out == nullptr) {
@@ -1125,8 +1148,8 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
   if (tid < kMaxCoef) sh.coef[tid] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + tid] : 0.f;
   __syncthreads();
   const size_t ext = size_t(u.h) * u.nu;
-  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, a.a + size_t(hu) * g.max_tokens,
-                     a.p + size_t(hu) * g.walk * g.max_tokens, n > 1 ? 1.f / float(n - 1) : 0.f};
+  const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, score_rows(a, hu),
+                     n > 1 ? 1.f / float(n - 1) : 0.f};
   const uint32_t k0 = uint32_t(a.seed), k1 = uint32_t(a.seed >> 32);
   if (u.keep != nullptr && u.budget >= n && a.keys_out == nullptr) {
     for (int j = tid; j < n; j += kSelThreads) u.keep[j] = j;
@@ -1304,8 +1327,7 @@ __global__ __launch_bounds__(kKeysThreads) void head_codes_kernel(const Args a) 
   __syncthreads();
   const int n = u.nu;
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + size_t(u.h) * n : nullptr,
-                     a.a + size_t(hu) * g.max_tokens, a.p + size_t(hu) * g.walk * g.max_tokens,
-                     n > 1 ? 1.f / float(n - 1) : 0.f};
+                     score_rows(a, hu), n > 1 ? 1.f / float(n - 1) : 0.f};
   uint32_t* codes = reinterpret_cast<uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
   constexpr int kPer = kKeysPerBlock / kKeysThreads;
 #pragma unroll
@@ -1507,16 +1529,12 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
   const uint32_t* base =
       reinterpret_cast<const uint32_t*>(a.keys + size_t(item) * H * g.max_tokens) + a.wcode_off;
   const size_t hstride = 2 * size_t(g.max_tokens);   // uint32 per head unit's key array
-  uint32_t* gh = a.ahist + size_t(item) * kAllocBins;
+  const uint32_t* gh = a.ahist + size_t(item) * kAllocBins;
   for (int h = tid; h < H; h += kSelThreads) {
     s_gt[h] = 0;
     s_eq[h] = 0;
   }
-  // The histogram into LDS; the global copy is cleared for the next call.
-  for (int b = tid; b < kAllocBins; b += kSelThreads) {
-    s_hist[b] = gh[b];
-    gh[b] = 0u;
-  }
+  for (int b = tid; b < kAllocBins; b += kSelThreads) s_hist[b] = gh[b];
   __syncthreads();
   bool all = true;   // every code of the threshold class is taken
   int need = 0;
@@ -1688,8 +1706,26 @@ __global__ __launch_bounds__(kSelThreads) void head_alloc_kernel(const Args a) {
   }
 }
 
+// Clears the per-item histograms of the allocation before a call builds them
+// (their place in the workspace moves with the call's shape, so a clear left
+// by an earlier call cannot be relied on).  A fill kernel, not a memset, so
+// that the call stays capturable into a graph.
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+hipError_t launch_clear_alloc_hist(const Args& a, hipStream_t s) {
+  const int64_t n = int64_t(a.g.n_hu / a.g.h_kv) * kAllocBins;
+  const int blocks = int(std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(clear_words_kernel, dim3(blocks), dim3(256), 0, s, a.ahist, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_head_budget(const Args& a, hipStream_t s) {
   if (a.g.head_alloc == NX_HEADS_ALLOC && !a.est_wcodes) {
+    const hipError_t cerr = launch_clear_alloc_hist(a, s);
+    if (cerr != hipSuccess) return cerr;
     hipLaunchKernelGGL(head_codes_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1704,7 +1740,21 @@ hipError_t launch_head_budget(const Args& a, hipStream_t s) {
 }
 
 hipError_t launch_estimate_keys(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(estimate_keys_kernel, dim3(a.g.n_kc, a.g.n_hu), dim3(kKeysThreads), 0, s, a);
+  if (a.est_wcodes) {   // this pass also builds the allocation histograms
+    const hipError_t cerr = launch_clear_alloc_hist(a, s);
+    if (cerr != hipSuccess) return cerr;
+  }
+  const dim3 grid(a.g.n_kc, a.g.n_hu), block(kKeysThreads);
+  const bool vec = a.w_in == nullptr && a.g.walk <= kMaxWalk && (a.g.max_tokens & 3) == 0;
+  switch (vec ? a.g.walk : -1) {
+    case 0: hipLaunchKernelGGL(estimate_keys_kernel<0>, grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL(estimate_keys_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(estimate_keys_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(estimate_keys_kernel<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(estimate_keys_kernel<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(estimate_keys_kernel<5>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(estimate_keys_kernel<-1>, grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

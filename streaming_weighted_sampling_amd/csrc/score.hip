@@ -409,7 +409,9 @@ constexpr int kWalkGlobal = 8;      // deep walks: every row tile stores its P_t
 //     G*H <= 32 each walk row covers whole 4-row groups of the MFMA output,
 //     so role 0 forms P_t in registers from in-lane group sums and one
 //     half-swap; other shapes leave the e values in LDS and role 0 sums them
-//     one sub-tile later.  Either way P_t goes to global memory and to LDS.
+//     one sub-tile later.  Either way P_t goes to global memory and to LDS
+//     (for H = 3 at token granularity only to LDS: role 1 then stores a_j
+//     and P_1..P_3 of each token as one 16-byte record).
 //     Roles 0 and 1 issue every global store of the pass and roles 2 and 3
 //     every K copy, so that no ring wait also waits for stores;
 //   * the Gram partials <P_t, P_t'> (diagonal |P_t|_1) accumulate one (or,
@@ -438,6 +440,9 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
                         : kWalk == kWalkFast8 || kWalk == kWalkFast4 ? 4
                         : kWalk == kWalkFast4Mid                   ? 6
                                                                    : kMaxWalk;   // deepest walk
+  // Exactly three walk rows at token granularity: a_j and P_1..P_3 leave as one
+  // 16-byte record per token (the rule of packed_rows: G = 4 or 8, H = 3, b = 1).
+  constexpr bool kPacked = kExactH == 3 && !kBlocks;
   constexpr int kHalfWaves = 2 * NW;
   constexpr int kPairsPerLane = (kMaxT * (kMaxT + 1) / 2 + kHalfWaves - 1) / kHalfWaves;
   auto s_pt = reinterpret_cast<float (*)[kMaxWalk][32]>(smem + GE::kSlotsProbs * GE::kTileBytes);
@@ -483,7 +488,8 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     gacc[k] = 0.f;
   }
 
-  const Buf a_out(a.a + size_t(hu) * g.max_tokens, uint32_t(g.max_tokens * 4));
+  const Buf a_out(a.a + size_t(hu) * g.max_tokens * (kPacked ? 4 : 1),
+                  uint32_t(g.max_tokens * (kPacked ? 16 : 4)));
   const Buf p_out(a.p + size_t(hu) * g.walk * g.max_tokens, uint32_t(g.walk * g.max_tokens * 4));
   const float wf = float(g.window);
 
@@ -501,7 +507,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     for (int t = 0; t < kMaxT; ++t) {
       if (t < walk) {
         if (blk == 1) {
-          if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
+          if (!kPacked && ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), pt[t]);
           s_pt[s & 1][t][nn] = ok ? pt[t] : 0.f;
         } else {
           const float v = group_sum(ok ? pt[t] : 0.f, blk);
@@ -566,7 +572,14 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   };
   auto a_put = [&](int s, float sum) {   // lanes of half 0
     const int tok = t0 + 32 * s + nn;
-    if (blk == 1) {
+    if constexpr (kPacked) {
+      // P_t of sub-tile s: left in LDS by role 0 before the barrier that
+      // ended sub-tile s (the Gram step reads the same slots).
+      if (tok < u.n)
+        a_out.st16(uint32_t(tok * 16),
+                   make_uint4(__float_as_uint(sum), __float_as_uint(s_pt[s & 1][0][nn]),
+                              __float_as_uint(s_pt[s & 1][1][nn]), __float_as_uint(s_pt[s & 1][2][nn])));
+    } else if (blk == 1) {
       if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
     } else {
       sum = group_sum(tok < u.n ? sum : 0.f, blk);

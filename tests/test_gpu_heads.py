@@ -61,7 +61,7 @@ def _layer(n):
     return wl, gen_layer(wl, n_tokens=n, device=DEV)
 
 
-def _run_batch(cfg, wl, lay, n, budget, cap, walk, hb_in=None, seed=3):
+def _run_batch(cfg, wl, lay, n, budget, cap, walk, hb_in=None, seed=3, ws=None):
     H, D = wl.h_kv, wl.head_dim
     rows = min(cap * cfg.block, n)
     keep = torch.full((H, cap), 12345, dtype=torch.int32, device=DEV)
@@ -77,7 +77,8 @@ def _run_batch(cfg, wl, lay, n, budget, cap, walk, hb_in=None, seed=3):
                                 budget=budget, head_cap=cap, head_budget=hb, layer=5,
                                 out_w=w_sel)],
                           device=DEV)
-    ws = nx.new_workspace(cfg, n, 1, walk, device=DEV)
+    if ws is None:
+        ws = nx.new_workspace(cfg, n, 1, walk, device=DEV)
     nx.nx_evict_batch(cfg, units, 1, n, walk, seed, workspace=ws, step=2, max_out_rows=rows)
     nx.nx_read_device_status(cfg, ws)
     return k, v, keep, out_k, out_v, hb.cpu().numpy(), w_sel.cpu().numpy()
@@ -308,6 +309,23 @@ def test_streaming_decode_with_allocated_budgets(inplace):
                 np.testing.assert_array_equal(vl[l, h, :kept + A], exp_v[:kept + A])
         drift = drift or len(set(post.ravel().tolist())) > 1
     assert drift, "the allocation never moved budget between heads"
+
+
+def test_allocated_budgets_on_a_reused_workspace():
+    """Two allocated-budget events of different sizes on one workspace: the
+    allocation histograms sit at another offset in the second call (over the
+    first call's keys and scores), so each call must clear them itself.  Both
+    calls' budgets equal the oracle's allocation on their exported weights."""
+    wl, lay = _layer(4096)
+    cfg = nx.NexusConfig(wl.h_q, wl.h_kv, wl.head_dim, wl.window, torch.bfloat16,
+                         head_alloc=nx.NX_HEADS_ALLOC, head_floor=40)
+    ws = nx.new_workspace(cfg, 4096, 1, wl.walk_iters, device=DEV)
+    for n in (4096, 1536):
+        B = n // 5
+        k, v, keep, ok, ov, hb, w = _run_batch(cfg, wl, lay, n, B, 2 * B, wl.walk_iters, ws=ws)
+        w_gpu = _check(cfg, wl, lay, k, v, keep, ok, ov, hb, n, wl.walk_iters, w)
+        np.testing.assert_array_equal(hb, nexus.ada_head_budgets(w_gpu, B, 40, cap=2 * B),
+                                      err_msg=f"n = {n}")
 
 
 def test_allocated_budgets_with_a_deep_walk():
