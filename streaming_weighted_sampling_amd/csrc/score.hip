@@ -393,6 +393,7 @@ constexpr int kWalkFast4Mid = 5;    // G = 4, 4 < H <= 6 (fewer Gram pairs per l
 constexpr int kWalkFast4H3 = 6;     // G = 4, H = 3 exactly (no per-row depth tests)
 constexpr int kWalkFast8H3 = 7;     // G = 8, H = 3 exactly
 constexpr int kWalkGlobal = 8;      // deep walks: every row tile stores its P_t rows (no Gram here)
+constexpr int kWalkFast4H5 = 9;     // G = 4, H = 5 exactly (15 Gram pairs, no per-row depth tests)
 
 // Pass 2 on one (head unit, tile) item.
 //
@@ -432,7 +433,9 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
   constexpr bool kHasWalk = kWalk != kWalkNone;
   constexpr bool kGlobal = kWalk == kWalkGlobal;
   constexpr bool kHasGram = kHasWalk && !kGlobal;   // Gram partials formed in this pass
-  constexpr int kExactH = kWalk == kWalkFast4H3 || kWalk == kWalkFast8H3 ? 3 : 0;
+  constexpr int kExactH = kWalk == kWalkFast4H3 || kWalk == kWalkFast8H3 ? 3
+                         : kWalk == kWalkFast4H5                        ? 5
+                                                                        : 0;
   constexpr bool kG8 = kWalk == kWalkFast8 || kWalk == kWalkFast8H3;   // walk rows span 8 output rows
   constexpr bool kFastWalk = kWalk == kWalkFast4 || kWalk == kWalkFast8 || kWalk == kWalkFast4Deep ||
                              kWalk == kWalkFast4Mid || kExactH > 0;
@@ -837,6 +840,7 @@ int walk_mode(const Geometry& g) {
   if (g.deep) return kWalkGlobal;
   if (g.walk == 3 && g.group == 4) return kWalkFast4H3;
   if (g.walk == 3 && g.group == 8) return kWalkFast8H3;
+  if (g.walk == 5 && g.group == 4) return kWalkFast4H5;
   if (g.walk <= 4 && g.group == 4) return kWalkFast4;
   if (g.walk <= 4 && g.group == 8) return kWalkFast8;
   if (g.walk <= 6 && g.group == 4) return kWalkFast4Mid;
@@ -871,6 +875,9 @@ void launch_probs(const Args& a, dim3 grid, hipStream_t s) {
       break;
     case kWalkFast4Mid:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4Mid, kBlocks>), grid, dim3(64 * NW), 0, s, a);
+      break;
+    case kWalkFast4H5:
+      hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkFast4H5, kBlocks>), grid, dim3(64 * NW), 0, s, a);
       break;
     case kWalkGlobal:
       hipLaunchKernelGGL((score_probs_kernel<T, D, MPW, NW, kWalkGlobal, kBlocks>), grid, dim3(64 * NW), 0, s, a);
