@@ -627,6 +627,10 @@ SCORE_CASES = [
     ("g16_w8_h4_64walkrows", 128, 8, 128, 8, torch.bfloat16, 2100, 4),
     ("mha_w32_h3", 8, 8, 128, 32, torch.bfloat16, 2600, 3),
     ("f32_d128_g4", 32, 8, 128, 32, torch.float32, 1500, 3),
+    # fp32 above 4 row tiles: eight wavefronts of two tiles each (the fp32
+    # D = 128 forms of these kernels hold part of their state in scratch)
+    ("f32_d128_g8_w32", 64, 8, 128, 32, torch.float32, 1300, 3),
+    ("f32_d64_g8_w64_h5", 64, 8, 64, 64, torch.float32, 900, 5),
     ("bf16_d64_g8_w64", 64, 8, 64, 64, torch.bfloat16, 1800, 3),
     ("bf16_d64", 16, 4, 64, 8, torch.bfloat16, 1500, 8),
     ("one_token", 4, 2, 128, 4, torch.bfloat16, 1, 2),
