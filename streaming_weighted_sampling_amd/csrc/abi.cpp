@@ -88,11 +88,16 @@ nx_status make_geometry(const nx_desc* d, int32_t max_tokens, int32_t n_items, i
   g->max_out_rows = max_tokens;
   g->n_t1 = (max_tokens + kMinTokPerBlock - 1) / kMinTokPerBlock;
   g->n_t2 = g->n_t1;
-  // Tokens per score workgroup: the widest power of two in [128, 2048] that
-  // still gives >= 2048 workgroups per pass (8 per CU): fewer tile partials
-  // and less per-workgroup setup without starving the chip.
-  int32_t tpb = kMaxTokPerBlock;
-  while (tpb > kMinTokPerBlock && n_hu * ((int64_t(max_tokens) + tpb - 1) / tpb) < 2048) tpb /= 2;
+  // Tokens per score workgroup: first the tile count per head unit, the
+  // fewest that give >= 2048 workgroups per pass (8 per CU) with tiles of at
+  // most 2048 tokens; then equal tiles, rounded up to whole 32-token
+  // sub-tiles and kept in [128, 2048].  Equal tiles keep the workgroups'
+  // rounds on the chip full (N = 6810 at 256 head units: 8 tiles of 864
+  // tokens, two full rounds, where halving powers of two gave 14 tiles of 512).
+  const int64_t t_min = std::max<int64_t>((2048 + n_hu - 1) / n_hu,
+                                          (int64_t(max_tokens) + kMaxTokPerBlock - 1) / kMaxTokPerBlock);
+  const int64_t tpb64 = ((int64_t(max_tokens) + t_min - 1) / t_min + 31) / 32 * 32;
+  const int32_t tpb = int32_t(std::min<int64_t>(std::max<int64_t>(tpb64, kMinTokPerBlock), kMaxTokPerBlock));
   g->tok_per_block = tpb;
   g->n_tmax = (max_tokens + tpb - 1) / tpb;
   g->n_kc = (max_tokens + kKeysPerBlock - 1) / kKeysPerBlock;
