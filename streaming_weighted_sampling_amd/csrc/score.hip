@@ -573,15 +573,24 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
     for (int r = 0; r < NW; ++r) la[r] = s_a[s & 1][r][nn];
   };
+  // Packed records: P_t of sub-tile s was left in LDS by role 0 before the
+  // barrier that ended sub-tile s (the Gram step reads the same slots).
+  auto p_load = [&](int s, float (&lp)[3]) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) lp[t] = s_pt[s & 1][t][nn];
+  };
+  auto a_put_rec = [&](int s, float sum, const float (&lp)[3]) {   // lanes of half 0
+    const int tok = t0 + 32 * s + nn;
+    if (tok < u.n)
+      a_out.st16(uint32_t(tok * 16), make_uint4(__float_as_uint(sum), __float_as_uint(lp[0]),
+                                                __float_as_uint(lp[1]), __float_as_uint(lp[2])));
+  };
   auto a_put = [&](int s, float sum) {   // lanes of half 0
     const int tok = t0 + 32 * s + nn;
     if constexpr (kPacked) {
-      // P_t of sub-tile s: left in LDS by role 0 before the barrier that
-      // ended sub-tile s (the Gram step reads the same slots).
-      if (tok < u.n)
-        a_out.st16(uint32_t(tok * 16),
-                   make_uint4(__float_as_uint(sum), __float_as_uint(s_pt[s & 1][0][nn]),
-                              __float_as_uint(s_pt[s & 1][1][nn]), __float_as_uint(s_pt[s & 1][2][nn])));
+      float lp[3];
+      p_load(s, lp);
+      a_put_rec(s, sum, lp);
     } else if (blk == 1) {
       if (tok < u.n) a_out.stf(uint32_t(tok * 4), sum);
     } else {
@@ -589,13 +598,14 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       if (lead && tok < u.n) a_out.stf(uint32_t((tok / blk) * 4), sum);
     }
   };
-  auto a_store = [&](int s, const float (&la)[NW]) {
+  auto a_store = [&](int s, const float (&la)[NW], const float (&lp)[3]) {
     if (hh != 0) return;
     float sum = la[0];
 #pragma unroll
     for (int r = 1; r < NW; ++r)
       if (r < row_roles) sum += la[r];
-    a_put(s, sum);
+    if constexpr (kPacked) a_put_rec(s, sum, lp);
+    else a_put(s, sum);
   };
   auto a_final = [&](int s) {
     if (role != 1) return;
@@ -613,9 +623,10 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       const float sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       if (hh == 0) a_put(s, sum);
     } else {
-      float la[NW];
+      float la[NW], lp[3] = {};
       a_load(s, la);
-      a_store(s, la);
+      if constexpr (kPacked) p_load(s, lp);
+      a_store(s, la, lp);
     }
   };
 
@@ -685,10 +696,13 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
     // eight a_j partials across the MFMA chains would spill.
     constexpr bool kSplitLag = kWalk != kWalkLds && NW == kWaves;
     const bool lag = st > 0;
-    float la[NW], gx[kPairsPerLane], gy[kPairsPerLane];
+    float la[NW], lp[3] = {}, gx[kPairsPerLane], gy[kPairsPerLane];
     if (lag) {
       if constexpr (kSplitLag) {
-        if (role == 1) a_load(st - 1, la);
+        if (role == 1) {
+          a_load(st - 1, la);
+          if constexpr (kPacked) p_load(st - 1, lp);
+        }
         if constexpr (kFastWalk) gram_load(st - 1, gx, gy);
       } else if constexpr (kWalk == kWalkLds) {
         a_final(st - 1);
@@ -707,7 +721,7 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
       const int mt = role + NW * i;
       auto consume_lag = [&] {
         if constexpr (kSplitLag) {
-          if (role == 1) a_store(st - 1, la);
+          if (role == 1) a_store(st - 1, la, lp);
           if constexpr (kFastWalk) gram_add(gx, gy);
         }
       };
