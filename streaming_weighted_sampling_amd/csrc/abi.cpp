@@ -231,15 +231,33 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profil
   const int max_units = (a.g.max_tokens + a.g.block - 1) / a.g.block;
   const bool fused = max_units <= kWideMaxTokens && !a.stop_after_weights &&
                      first <= kStageReservoirKeys && last >= kStageTopbSelect;
+  // Calls of at most 4096 estimate_keys workgroups form the walk coefficients
+  // inside estimate_keys (one launch fewer: on the single-layer shapes the
+  // walk_coef launch cost ~9 us on its own; on the 32-layer event the fold
+  // broke even).  Deep walks keep their Gram pass.
+  const bool coef_in_keys = fused && !a.g.deep && a.w_in == nullptr && first <= kStageWalkCoef &&
+                            int64_t(a.g.n_hu) * a.g.n_kc <= 4096;
+  // Calls of at most 2048 second-sweep workgroups (and at most 64 score tiles
+  // per head unit) merge the row statistics in each second-sweep workgroup
+  // instead of a score_combine launch.
+  const bool beta_in_probs = first <= kStageScoreCombine && last >= kStageScoreProbs &&
+                             int64_t(a.g.n_hu) * a.g.n_tmax <= 2048 && a.g.n_tmax <= 64;
+  Args sa = a;
+  sa.beta_in_probs = beta_in_probs ? 1 : 0;
   // The stages from the keys on read the per-head budgets of this call.
   Args live = a;
   live.heads_live = 1;
+  live.coef_in_keys = coef_in_keys ? 1 : 0;
   for (int st = first; st <= last && err == hipSuccess; ++st) {
     switch (st) {
       case kStageScoreStats: err = run_stage(st, s, [&] { return launch_score_stats(a, s); }); break;
-      case kStageScoreCombine: err = run_stage(st, s, [&] { return launch_score_combine(a, s); }); break;
-      case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(a, s); }); break;
-      case kStageWalkCoef: err = run_stage(st, s, [&] { return launch_walk_coef(a, s); }); break;
+      case kStageScoreCombine:
+        if (!beta_in_probs) err = run_stage(st, s, [&] { return launch_score_combine(a, s); });
+        break;
+      case kStageScoreProbs: err = run_stage(st, s, [&] { return launch_score_probs(sa, s); }); break;
+      case kStageWalkCoef:
+        if (!coef_in_keys) err = run_stage(st, s, [&] { return launch_walk_coef(a, s); });
+        break;
       case kStageReservoirKeys: {
         // Per-head budgets are settled before any stage that reads them.  On
         // the fused path with allocated budgets the estimate pass runs first
@@ -247,6 +265,7 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profil
         const bool heads = a.g.head_alloc != NX_HEADS_UNIFORM && !a.stop_after_weights;
         const bool est_first = heads && fused && a.g.head_alloc == NX_HEADS_ALLOC;
         Args pre = a;
+        pre.coef_in_keys = coef_in_keys ? 1 : 0;
         pre.est_wcodes = est_first ? 1 : 0;
         pre.wcode_off = est_first ? a.g.max_tokens : 0;
         if (est_first) {

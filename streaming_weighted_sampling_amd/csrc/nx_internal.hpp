@@ -165,6 +165,8 @@ struct Args {
   int32_t head_floor;   // NX_HEADS_ALLOC floor
   int32_t heads_live;   // 1: the items' head_budget arrays hold this call's budgets
   int32_t est_wcodes;   // 1: estimate_keys also writes the allocation's weight codes
+  int32_t coef_in_keys; // 1: estimate_keys forms the walk coefficients (no walk_coef launch)
+  int32_t beta_in_probs; // 1: score_probs merges the row statistics itself (no score_combine launch)
   int32_t wcode_off;    // uint32 offset of the weight codes in a head unit's key array
 };
 

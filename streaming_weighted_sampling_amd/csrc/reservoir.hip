@@ -44,12 +44,10 @@ static_assert(kFusedMaxTokens == kSelThreads * kFusedPer, "fused select covers 1
 // partials (lane-strided sums, then a butterfly), then the walk recurrence
 // of section 2.2 Eq. (4) in its rank-1 form: gamma_1 = 1,
 // gamma_t = 1 + sum_{t'<t} gamma_t' <P_t, P_t'>, ||C||_1 = sum_t gamma_t |P_t|_1.
-__global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
+// Lane 0 writes the coefficients gamma_t / ||C||_1 for t < kMaxWalk (zero past
+// the walk) to `out`.
+__device__ inline void walk_coef_unit(const Args& a, const HeadUnit& u, int hu, int lane, float* out) {
   const Geometry& g = a.g;
-  const int hu = blockIdx.x;
-  const HeadUnit u = head_unit(a, hu);
-  if (!u.valid) return;
-  const int lane = threadIdx.x;
   const int n_tiles = (u.n + g.tok_per_block - 1) / g.tok_per_block;
   const float* gp = a.gram + size_t(hu) * g.n_t2 * (kMaxWalk * kMaxWalk);
   float gm[kMaxWalk][kMaxWalk];
@@ -82,9 +80,15 @@ __global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
       if (t < g.walk) norm = fmaf(x, gm[t][t], norm);
     }
 #pragma unroll
-    for (int t = 0; t < kMaxWalk; ++t)
-      a.coef[size_t(hu) * kMaxCoef + t] = (t < g.walk) ? gam[t] / norm : 0.f;
+    for (int t = 0; t < kMaxWalk; ++t) out[t] = (t < g.walk) ? gam[t] / norm : 0.f;
   }
+}
+
+__global__ __launch_bounds__(64) void walk_coef_kernel(const Args a) {
+  const int hu = blockIdx.x;
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) return;
+  walk_coef_unit(a, u, hu, threadIdx.x, a.coef + size_t(hu) * kMaxCoef);
 }
 
 // ---- deep walks (H > kMaxWalk or G * H > kMaxWalkRows) --------------------
@@ -768,9 +772,17 @@ __global__ __launch_bounds__(kKeysThreads) void estimate_keys_kernel(const Args 
   const int j0 = chunk * kKeysPerBlock;
   if (j0 >= u.nu) return;
   __shared__ float s_coef[kMaxCoef];
-  if (threadIdx.x < kMaxCoef)
-    s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
-  __syncthreads();
+  if (a.coef_in_keys) {
+    // Small calls: the walk coefficients are formed here (no walk_coef
+    // launch), and chunk 0 leaves them for the select kernel.
+    if (threadIdx.x < 64) walk_coef_unit(a, u, hu, threadIdx.x, s_coef);
+    __syncthreads();
+    if (chunk == 0 && threadIdx.x < kMaxWalk) a.coef[size_t(hu) * kMaxCoef + threadIdx.x] = s_coef[threadIdx.x];
+  } else {
+    if (threadIdx.x < kMaxCoef)
+      s_coef[threadIdx.x] = a.w_in == nullptr ? a.coef[size_t(hu) * kMaxCoef + threadIdx.x] : 0.f;
+    __syncthreads();
+  }
   const int n = u.nu;
   const size_t ext = size_t(u.h) * n;
   const WeightSrc ws{a.w_in != nullptr ? a.w_in + ext : nullptr, score_rows(a, hu),

@@ -343,19 +343,16 @@ __device__ inline void stats_item(const Args& a, const HeadUnit& u, int hu, int 
 }
 
 // Merge the tile pairs of every window row of one head unit in tile order:
-// beta_r = max_r + log2(Z_r) + log2(G*W) (whole workgroup, one row per thread;
-// tile pairs are loaded 16 at a time so the loads overlap).
-__device__ inline void combine_unit(const Args& a, int hu) {
-  const HeadUnit u = head_unit(a, hu);
-  if (!u.valid) {
-    if (threadIdx.x == 0) raise_status(a, kStatusBadItem);
-    return;
-  }
+// beta_r = max_r + log2(Z_r) + log2(G*W) (one row per thread, nthreads threads
+// from tid; tile pairs are loaded 16 at a time so the loads overlap), into
+// out[rho] for rho < rows_pad.
+__device__ inline void combine_rows(const Args& a, const HeadUnit& u, int hu, float* out, int tid,
+                                    int nthreads) {
   const int n_tiles = (u.n + a.g.tok_per_block - 1) / a.g.tok_per_block;
   const float* part = a.part1 + size_t(hu) * a.g.n_t1 * a.g.rows_pad * 2;
   const float log2_gw = log2f(float(a.g.group * a.g.window));
   constexpr int kBatch = 16;
-  for (int rho = threadIdx.x; rho < a.g.rows_pad; rho += kThreads) {
+  for (int rho = tid; rho < a.g.rows_pad; rho += nthreads) {
     float beta = INFINITY;
     if (rho < a.g.rows) {
       float m = -INFINITY, zsum = 0.f;
@@ -378,8 +375,18 @@ __device__ inline void combine_unit(const Args& a, int hu) {
       }
       beta = m + log2f(zsum) + log2_gw;
     }
-    a.beta[size_t(hu) * a.g.rows_pad + rho] = beta;
+    out[rho] = beta;
   }
+}
+
+// The row merge of one head unit by a whole workgroup, into the workspace.
+__device__ inline void combine_unit(const Args& a, int hu) {
+  const HeadUnit u = head_unit(a, hu);
+  if (!u.valid) {
+    if (threadIdx.x == 0) raise_status(a, kStatusBadItem);
+    return;
+  }
+  combine_rows(a, u, hu, a.beta + size_t(hu) * a.g.rows_pad, threadIdx.x, kThreads);
 }
 
 // Walk modes of pass 2 (template parameter, chosen on the host).
@@ -470,14 +477,24 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 
   uint4 qf[MPW][GE::kChunks];
   load_q<T, D, MPW, NW>(a, u, role, nn, hh, qf);
+  // beta of this unit's rows: from the row merge, or (small calls, no merge
+  // launch) merged here into the LDS the ring fills only after the barrier.
+  const float* beta = a.beta + size_t(hu) * g.rows_pad;
+  if (a.beta_in_probs) {
+    float* s_beta = reinterpret_cast<float*>(smem);
+    combine_rows(a, u, hu, s_beta, threadIdx.x, 64 * NW);
+    __syncthreads();
+    beta = s_beta;
+  }
   float bt[MPW][16];
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
     const int mt = role + NW * i;
 #pragma unroll
     for (int v = 0; v < 16; ++v)
-      bt[i][v] = mt < n_mt ? a.beta[size_t(hu) * g.rows_pad + mt * 32 + out_row(v, hh)] : INFINITY;
+      bt[i][v] = mt < n_mt ? beta[mt * 32 + out_row(v, hh)] : INFINITY;
   }
+  if (a.beta_in_probs) __syncthreads();   // every wavefront has read the merge's LDS
   // This lane's Gram pairs (t, t'), 3 bits each, packed 6 bits per pair.
   uint32_t pairs = 0;
   float gacc[kPairsPerLane];
@@ -847,6 +864,7 @@ void score_probs_kernel(const Args a) {
   const int tile = blockIdx.x, hu = blockIdx.y;
   const HeadUnit u = head_unit(a, hu);
   if (u.valid) probs_item<T, D, MPW, NW, kWalk, kBlocks>(a, u, hu, tile, smem);
+  else if (a.beta_in_probs && tile == 0 && threadIdx.x == 0) raise_status(a, kStatusBadItem);
 }
 
 int walk_mode(const Geometry& g) {
