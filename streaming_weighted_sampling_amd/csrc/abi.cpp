@@ -237,11 +237,13 @@ nx_status enqueue(const Args& a, hipStream_t s, int first, int last, bool profil
   // broke even).  Deep walks keep their Gram pass.
   const bool coef_in_keys = fused && !a.g.deep && a.w_in == nullptr && first <= kStageWalkCoef &&
                             int64_t(a.g.n_hu) * a.g.n_kc <= 4096;
-  // Calls of at most 2048 second-sweep workgroups (and at most 64 score tiles
-  // per head unit) merge the row statistics in each second-sweep workgroup
-  // instead of a score_combine launch.
+  // Calls of at most 4096 second-sweep workgroups, each merging at most 4096
+  // (tile, row) pairs, merge the row statistics in every second-sweep
+  // workgroup instead of a score_combine launch (the 32-layer event: 16 x 128
+  // pairs per workgroup; the 70B-shaped share, 64 x 512, keeps the launch).
   const bool beta_in_probs = first <= kStageScoreCombine && last >= kStageScoreProbs &&
-                             int64_t(a.g.n_hu) * a.g.n_tmax <= 2048 && a.g.n_tmax <= 64;
+                             int64_t(a.g.n_hu) * a.g.n_tmax <= 4096 &&
+                             int64_t(a.g.n_tmax) * a.g.rows_pad <= 4096;
   Args sa = a;
   sa.beta_in_probs = beta_in_probs ? 1 : 0;
   // The stages from the keys on read the per-head budgets of this call.
