@@ -491,22 +491,42 @@ __device__ inline void sel_pick_bin(SelCore& sh, int shift, uint32_t dmask) {
 
 // MSD radix passes with 8-bit digits over the unresolved bits, highest first,
 // until the boundary bin holds exactly the missing count or every bit is
-// fixed; at most 64 bits, so at most 8 passes.  code_at(i) gives the code of
-// the i-th candidate slot of this thread (slot count `slots`, valid(i)).
+// fixed; at most 64 bits, so at most 8 passes.  Each pass clears the digit
+// histogram (sel_pass_begin), counts the candidates under the current prefix
+// (one atomic per code) and picks the boundary bin (sel_pass_end).
+__device__ inline void sel_pass_begin(SelCore& sh, int start, int* shift, uint32_t* dmask) {
+  *shift = start >= 7 ? start - 7 : 0;
+  *dmask = (1u << (start - *shift + 1)) - 1u;
+  for (int b = threadIdx.x; b < 256 * kHistCopies; b += blockDim.x) sh.hist[b] = 0;
+  __syncthreads();
+}
+__device__ inline void sel_pass_end(SelCore& sh, int shift, uint32_t dmask) {
+  __syncthreads();
+  if (threadIdx.x < 256) {   // fold bin threadIdx.x's copies into copy 0
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) t += sh.hist[threadIdx.x * kHistCopies + c];
+    sh.hist[threadIdx.x * kHistCopies] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) sel_pick_bin(sh, shift, dmask);
+  __syncthreads();
+}
+
+// The passes over slots: code_at(i) gives the code of the i-th candidate slot
+// of this thread (slot count `slots`, valid(i)).  kBatch slots at a time: for
+// codes read from memory (kBatch 8) their loads are all issued before the
+// first is used, one round trip per batch; codes in registers or LDS take
+// kBatch 1.
 template <int kBatch = 1, typename CodeAt, typename Valid>
 __device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Valid&& valid) {
   int start = sh.start;
   while (!sh.done && start >= 0) {
-    const int shift = start >= 7 ? start - 7 : 0;
-    const int width = start - shift + 1;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int b = threadIdx.x; b < 256 * kHistCopies; b += blockDim.x) sh.hist[b] = 0;
-    __syncthreads();
+    int shift;
+    uint32_t dmask;
+    sel_pass_begin(sh, start, &shift, &dmask);
     const uint64_t prefix = sh.prefix, mask = sh.mask;
     const uint32_t copy = threadIdx.x & (kHistCopies - 1);
-    // kBatch candidate slots at a time: for codes read from memory (kBatch
-    // 8) their loads are all issued before the first is used, one round
-    // trip per batch; codes in registers or LDS take kBatch 1.
     for (int i0 = 0; i0 < slots; i0 += kBatch) {
       uint64_t c[kBatch];
       bool ok[kBatch];
@@ -520,16 +540,27 @@ __device__ inline void sel_passes(SelCore& sh, int slots, CodeAt&& code_at, Vali
         if (ok[k] && (c[k] & mask) == prefix)
           atomicAdd(&sh.hist[((uint32_t(c[k] >> shift) & dmask) * kHistCopies) | copy], 1u);
     }
-    __syncthreads();
-    if (threadIdx.x < 256) {   // fold bin threadIdx.x's copies into copy 0
-      uint32_t t = 0;
-#pragma unroll
-      for (int c = 0; c < kHistCopies; ++c) t += sh.hist[threadIdx.x * kHistCopies + c];
-      sh.hist[threadIdx.x * kHistCopies] = t;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) sel_pick_bin(sh, shift, dmask);
-    __syncthreads();
+    sel_pass_end(sh, shift, dmask);
+    start = shift - 1;
+  }
+}
+
+// The same passes with visit(count) calling count(c) once for every candidate
+// code c of this thread (codes streamed from memory by the caller's loads).
+template <typename Visit>
+__device__ inline void sel_passes_visit(SelCore& sh, Visit&& visit) {
+  int start = sh.start;
+  while (!sh.done && start >= 0) {
+    int shift;
+    uint32_t dmask;
+    sel_pass_begin(sh, start, &shift, &dmask);
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    const uint32_t copy = threadIdx.x & (kHistCopies - 1);
+    visit([&](uint64_t c) {
+      if ((c & mask) == prefix)
+        atomicAdd(&sh.hist[((uint32_t(c >> shift) & dmask) * kHistCopies) | copy], 1u);
+    });
+    sel_pass_end(sh, shift, dmask);
     start = shift - 1;
   }
 }
@@ -1119,21 +1150,29 @@ void sample_select_kernel(const Args a) {
 // sample_select_kernel, with the 32-bit codes read from the head unit's key
 // array on every pass instead of held in registers.  The band argument does
 // not depend on n, so the kept set again equals the selection on exact keys.
-// f(j, code) for this thread's tokens j = tid + 1024 i < n, eight loads issued
-// before the first use.
+// f(j, code) for every token j < n of this thread: four consecutive codes per
+// 16-byte load (the key array is 16-byte aligned and holds at least
+// ceil(n / 4) * 4 codes), eight loads (32 codes per lane, 128 KB per
+// workgroup) in flight before the first use.
 template <typename F>
-__device__ __forceinline__ void for_codes(const uint32_t* codes, int n, int slots, F&& f) {
-  for (int i0 = 0; i0 < slots; i0 += 8) {
-    uint32_t c[8];
+__device__ __forceinline__ void for_codes(const uint32_t* codes, int n, F&& f) {
+  constexpr int kLoads = 8;
+  const uint4* c4 = reinterpret_cast<const uint4*>(codes);
+  const int n4 = (n + 3) >> 2;
+  for (int q0 = int(threadIdx.x); q0 < n4; q0 += kSelThreads * kLoads) {
+    uint4 c[kLoads];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = int(threadIdx.x) + kSelThreads * (i0 + k);
-      c[k] = j < n ? codes[j] : 0u;
+    for (int k = 0; k < kLoads; ++k) {
+      const int q = q0 + kSelThreads * k;
+      c[k] = q < n4 ? c4[q] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = int(threadIdx.x) + kSelThreads * (i0 + k);
-      if (j < n) f(j, c[k]);
+    for (int k = 0; k < kLoads; ++k) {
+      const int j = 4 * (q0 + kSelThreads * k);
+      if (j < n) f(j, c[k].x);
+      if (j + 1 < n) f(j + 1, c[k].y);
+      if (j + 2 < n) f(j + 2, c[k].z);
+      if (j + 3 < n) f(j + 3, c[k].w);
     }
   }
 }
@@ -1168,13 +1207,12 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
     return;
   }
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.keys + size_t(hu) * g.max_tokens);
-  const int slots = (n + kSelThreads - 1) / kSelThreads;
   bool fallback = !uses_estimate(a, u) || n > kWideMaxTokens;
   uint32_t hi = 0;
   int need2 = 0, m = 0;
   if (!fallback) {
     uint32_t v_or = 0, v_and = 0xFFFFFFFFu;
-    for_codes(codes, n, slots, [&](int, uint32_t c) { v_or |= c; v_and &= c; });
+    for_codes(codes, n, [&](int, uint32_t c) { v_or |= c; v_and &= c; });
 #pragma unroll
     for (int mm = 32; mm >= 1; mm >>= 1) {
       v_or |= uint32_t(__shfl_xor(int(v_or), mm, 64));
@@ -1191,8 +1229,9 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
       sh.cb = 0xFFFFFFFFu;
     }
     __syncthreads();
-    sel_passes<8>(core, slots, [&](int i) { return uint64_t(codes[tid + kSelThreads * i]) | 0xFFFFFFFF00000000ull; },
-               [&](int i) { return tid + kSelThreads * i < n; });
+    sel_passes_visit(core, [&](auto&& count) {
+      for_codes(codes, n, [&](int, uint32_t c) { count(uint64_t(c) | 0xFFFFFFFF00000000ull); });
+    });
     if (!core.done) {
       if (tid == 0) raise_status(a, kStatusBadItem);
       for (int j = tid; j < u.budget; j += kSelThreads) u.keep[j] = j;
@@ -1202,7 +1241,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
     {
       uint32_t mn = 0xFFFFFFFFu;
       const uint64_t prefix = core.prefix, mask = core.mask;
-      for_codes(codes, n, slots, [&](int, uint32_t c) {
+      for_codes(codes, n, [&](int, uint32_t c) {
         if (((uint64_t(c) | 0xFFFFFFFF00000000ull) & mask) == prefix) mn = min(mn, c);
       });
 #pragma unroll
@@ -1220,7 +1259,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
       hi = min(max(f32_code(v + kBand), 1u), 0xFFFFFFFEu);
     }
     int above = 0;
-    for_codes(codes, n, slots, [&](int j, uint32_t c) {
+    for_codes(codes, n, [&](int j, uint32_t c) {
       if (c > hi) {
         ++above;
       } else if (c >= lo) {
