@@ -420,6 +420,82 @@ __device__ inline void write_ascending(int n, int budget, int32_t* keep, int* ro
   }
 }
 
+// The same ascending write over codes in memory, four consecutive tokens per
+// lane: round r of a group covers kSelThreads * 4 tokens, lane tid the four at
+// 4 ((g0 + r) kSelThreads + tid), read with one 16-byte load (the code array
+// holds at least ceil(n / 4) * 4 codes); eight rounds (eight loads per lane
+// in flight) per group and one scan per group.  A lane's offset inside its
+// wavefront is the sum of the kept counts (0..4) of the lanes below it, taken
+// from three ballots over the counts' bits.  keep_at(j, code) decides token j;
+// round_cnt holds at least 8 * kSelWaves ints.
+template <typename KeepAt>
+__device__ inline void write_ascending4(const uint32_t* codes, int n, int budget, int32_t* keep,
+                                        int* round_cnt, int* group_total, KeepAt&& keep_at) {
+  constexpr int kR = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below_lane = (1ull << lane) - 1ull;
+  const uint4* c4 = reinterpret_cast<const uint4*>(codes);
+  const int n4 = (n + 3) >> 2;
+  int base = 0;
+  for (int g0 = 0; g0 * kSelThreads < n4; g0 += kR) {
+    uint4 c[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int q = (g0 + r) * kSelThreads + tid;
+      c[r] = q < n4 ? c4[q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t m[kR];   // keep mask of the lane's four tokens
+    int pre[kR];      // kept tokens of the lanes below, in this wavefront
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      const int j = 4 * ((g0 + r) * kSelThreads + tid);
+      m[r] = 0u;
+      if (j < n && keep_at(j, c[r].x)) m[r] |= 1u;
+      if (j + 1 < n && keep_at(j + 1, c[r].y)) m[r] |= 2u;
+      if (j + 2 < n && keep_at(j + 2, c[r].z)) m[r] |= 4u;
+      if (j + 3 < n && keep_at(j + 3, c[r].w)) m[r] |= 8u;
+      const uint32_t cnt = uint32_t(__popc(m[r]));
+      const uint64_t b0 = __ballot(cnt & 1u), b1 = __ballot(cnt & 2u), b2 = __ballot(cnt & 4u);
+      pre[r] = __popcll(b0 & below_lane) + 2 * __popcll(b1 & below_lane) + 4 * __popcll(b2 & below_lane);
+      if (lane == 0) round_cnt[r * kSelWaves + wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      constexpr int kPerLane = kR * kSelWaves / 64;
+      int loc[kPerLane], sum = 0;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) { loc[q] = sum; sum += round_cnt[lane * kPerLane + q]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      const int excl = incl - sum;
+#pragma unroll
+      for (int q = 0; q < kPerLane; ++q) round_cnt[lane * kPerLane + q] = excl + loc[q];
+      if (lane == 63) *group_total = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kR; ++r) {
+      if (m[r] != 0u) {
+        int pos = base + round_cnt[r * kSelWaves + wave] + pre[r];
+        const int j = 4 * ((g0 + r) * kSelThreads + tid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((m[r] >> e) & 1u) {
+            if (pos < budget) keep[pos] = j + e;
+            ++pos;
+          }
+        }
+      }
+    }
+    base += *group_total;
+    __syncthreads();   // round_cnt and group_total are rewritten by the next group
+  }
+}
+
 // Shared state of one radix selection.  After the passes: keys whose bits
 // under `mask` exceed `prefix` are kept; of the `eq` keys equal to it under
 // the mask, `need` are kept (all of them when eq == need, else the ones with
@@ -1325,10 +1401,9 @@ __global__ __launch_bounds__(kSelThreads) void sample_select_wide_kernel(const A
     if (rank < need2) atomicOr(&sh.chosen[it >> 5], 1u << (it & 31));
   }
   __syncthreads();
-  // Ascending write (groups of kFusedPer rounds, one scan per group).
-  write_ascending(n, u.budget, u.keep, core.round_cnt, &core.group_total, [&](int j) {
-    return codes[j] > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u);
-  });
+  // Ascending write (four tokens per lane, eight rounds per group).
+  write_ascending4(codes, n, u.budget, u.keep, core.round_cnt, &core.group_total,
+                   [&](int j, uint32_t c) { return c > hi || ((sh.chosen[j >> 5] >> (j & 31)) & 1u); });
 }
 
 }  // namespace
