@@ -131,9 +131,12 @@ Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
   std::memset(&a, 0, sizeof(a));
   a.g = g;
   // K streams of more than twice the 256 MB Infinity Cache bypass the caches
-  // (faster sweeps); smaller ones stay cached, where the compaction that
-  // follows finds part of the kept rows.
-  a.k_stream_nt = int64_t(g.n_hu) * g.max_tokens * g.head_dim * elem_size(g.dtype) > (int64_t(512) << 20);
+  // (faster sweeps); smaller ones stay cached, where the copy compaction that
+  // follows finds part of the kept rows.  In-place compaction reads only the
+  // moved rows, so there the sweeps bypass the caches above the cache's own
+  // size.
+  const int64_t nt_above = int64_t(g.inplace ? 256 : 512) << 20;
+  a.k_stream_nt = int64_t(g.n_hu) * g.max_tokens * g.head_dim * elem_size(g.dtype) > nt_above;
   a.lambda = d->lambda;
   a.eps_tie = d->eps_tie;
   a.c_log2 = float(1.4426950408889634 / std::sqrt(double(d->head_dim)));
