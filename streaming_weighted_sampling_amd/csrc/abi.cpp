@@ -131,12 +131,15 @@ Args base_args(const nx_desc* d, const Geometry& g, uint64_t seed) {
   std::memset(&a, 0, sizeof(a));
   a.g = g;
   // K streams of more than twice the 256 MB Infinity Cache bypass the caches
-  // (faster sweeps); smaller ones stay cached, where the copy compaction that
-  // follows finds part of the kept rows.  In-place compaction reads only the
-  // moved rows, so there the sweeps bypass the caches above the cache's own
-  // size.
-  const int64_t nt_above = int64_t(g.inplace ? 256 : 512) << 20;
-  a.k_stream_nt = int64_t(g.n_hu) * g.max_tokens * g.head_dim * elem_size(g.dtype) > nt_above;
+  // (faster sweeps); smaller ones stay cached in the second sweep, where the
+  // copy compaction that follows finds part of the kept rows.  In-place
+  // compaction reads only the moved rows, so there the second sweep bypasses
+  // the caches above the cache's own size, and the first sweep always does
+  // (the second re-reads K from its start, so whatever the first left cached
+  // is gone by then).
+  const int64_t k_bytes = int64_t(g.n_hu) * g.max_tokens * g.head_dim * elem_size(g.dtype);
+  a.k_stream_nt = k_bytes > (int64_t(g.inplace ? 256 : 512) << 20);
+  a.k_stream_nt1 = k_bytes > (int64_t(256) << 20);
   a.lambda = d->lambda;
   a.eps_tie = d->eps_tie;
   a.c_log2 = float(1.4426950408889634 / std::sqrt(double(d->head_dim)));

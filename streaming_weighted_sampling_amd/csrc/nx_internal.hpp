@@ -143,7 +143,8 @@ struct Args {
   int32_t n_sink, n_recent;
   uint32_t step;
   int32_t n_avg;   // 1, 2 .. NX_MAX_AVG draws, or NX_TOPK
-  int32_t k_stream_nt;   // 1: the score sweeps copy K with the non-temporal hint
+  int32_t k_stream_nt;   // 1: the second score sweep copies K with the non-temporal hint
+  int32_t k_stream_nt1;  // 1: the first score sweep does
   uint64_t seed;
   // workspace
   uint32_t* status;

@@ -237,7 +237,7 @@ __device__ inline void stats_sweep(const Args& a, const HeadUnit& u, int t0, int
   const float c = a.c_log2;
   // Every wavefront copies K, at least one 1-KB copy each per sub-tile.
   constexpr int kLoaders = NW < GE::kTileBytes / 1024 ? NW : GE::kTileBytes / 1024;
-  sweep_tiles<T, D, GE::kSlotsStats, kLoaders, NW>(u, t0, n_sub, ring, wave, a.k_stream_nt != 0,
+  sweep_tiles<T, D, GE::kSlotsStats, kLoaders, NW>(u, t0, n_sub, ring, wave, a.k_stream_nt1 != 0,
                                                    [&](int st, const char* cur) {
     uint4 kf[GE::kChunks];
     read_frag<T, D>(cur, nn, hh, kf);
