@@ -755,7 +755,27 @@ __device__ inline void probs_item(const Args& a, const HeadUnit& u, int hu, int 
 #pragma unroll
         for (int q = 0; q < 4; ++q) sq[q] = (e[4 * q] + e[4 * q + 1]) + (e[4 * q + 2] + e[4 * q + 3]);
         tp += (sq[0] + sq[1]) + (sq[2] + sq[3]);
-        if constexpr (kFastWalk) {
+        if constexpr (kFastWalk && !kG8 && !kBlocks && !kPacked) {
+          if (i == 0 && role == 0) {
+            // G = 4 with planar walk rows: walk row t is the 4-row group
+            // 8q + 4*half .. +3 with t = 2q + half, which this lane half
+            // already sums in sq[q]; each half writes and stores its own rows
+            // (no exchange between the halves, the stores split over both).
+            // With packed records role 0 only fills LDS, where the exchange
+            // below measured faster.
+            const int tok = t0 + 32 * st + nn;
+            const bool ok = tok < u.n;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int t = 2 * q + hh;
+              if (t < walk) {
+                const float v = wf * sq[q];
+                if (ok) p_out.stf(uint32_t((t * g.max_tokens + tok) * 4), v);
+                s_pt[st & 1][t][nn] = ok ? v : 0.f;
+              }
+            }
+          }
+        } else if constexpr (kFastWalk) {
           if (i == 0 && role == 0) {
             // Group sums S over rows 8q + 4*half .. +3; after the swap every
             // lane holds S for q' = 2q (half 0) and q' = 2q + 1 (half 1).
